@@ -1,0 +1,73 @@
+/*
+ * Plain CPU oracle of the block-FP8 mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path includes, links or
+ * calls this; only the tests, the smoke check and the bench's CPU-baseline
+ * leg do. It shares no code, header, table or constant with the HIP library.
+ *
+ * All pointers are host pointers. Arrays are row-major and dense.
+ * bf16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Variant switches of the oracle. */
+#define ORACLE_NO_ACT_QUANT  (1u << 0) /* skip both activation quantisations */
+#define ORACLE_LOGITS_FP32   (1u << 1) /* keep router logits in fp32 (no bf16 rounding) */
+
+typedef struct {
+    int32_t hidden;       /* H */
+    int32_t n_experts;    /* E */
+    int32_t top_k;        /* K */
+    int32_t inter;        /* I, routed expert intermediate */
+    int32_t shared_inter; /* Is, 0 = no shared expert */
+    uint32_t flags;       /* ORACLE_* */
+} oracle_cfg;
+
+typedef struct {
+    const uint16_t *router_w;    /* bf16 [E,H] */
+    const float *router_bias;    /* fp32 [E] or NULL */
+    const uint8_t *w_gate;       /* e4m3 [E][I,H] */
+    const float *s_gate;         /* fp32 [E][I/128,H/128] */
+    const uint8_t *w_up;         /* e4m3 [E][I,H] */
+    const float *s_up;           /* fp32 [E][I/128,H/128] */
+    const uint8_t *w_down;       /* e4m3 [E][H,I] */
+    const float *s_down;         /* fp32 [E][H/128,I/128] */
+    const uint16_t *sh_gate;     /* bf16 [Is,H] */
+    const uint16_t *sh_up;       /* bf16 [Is,H] */
+    const uint16_t *sh_down;     /* bf16 [H,Is] */
+    const uint16_t *sh_gate_w;   /* bf16 [H] */
+} oracle_weights;
+
+float oracle_e4m3_decode(uint8_t code);
+uint8_t oracle_e4m3_encode(float r);
+void oracle_e4m3_encode_n(const float *r, int64_t n, uint8_t *out);
+uint16_t oracle_bf16_round(float f);
+void oracle_bf16_round_n(const float *f, int64_t n, uint16_t *out);
+
+void oracle_quant_groups(const float *v, int64_t n_groups, uint8_t *q, float *s);
+void oracle_quant_act(const uint16_t *x, int64_t T, int64_t C, uint8_t *q, float *s);
+
+void oracle_route(const oracle_cfg *cfg, const uint16_t *x, int64_t T,
+                  const uint16_t *router_w, const float *router_bias,
+                  int32_t *ids, float *weights, float *logits);
+
+/* Whole layer. y: bf16 [T,H]; acc (optional): the fp32 value before the
+ * final bf16 rounding; ids/weights (optional): the routing it used. */
+void oracle_forward(const oracle_cfg *cfg, const oracle_weights *w,
+                    const uint16_t *x, int64_t T, uint16_t *y, float *acc,
+                    int32_t *ids, float *weights);
+
+/* Threads the OpenMP runtime will use (for the baseline record). */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
