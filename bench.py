@@ -1,0 +1,194 @@
+"""Benchmark of the block-FP8 MoE layer on one MI355X.
+
+A step is one pass of the whole layer (router, activation quantisation,
+routed FP8 experts, SwiGLU, shared expert, gate, combine) on one bf16 row of
+the decode layer (H 2048, 256 experts top-8, I = Is = 512). Steps rotate over
+16 independently generated layers and rows, so the 256 MB Infinity Cache
+cannot hold the working set (one layer touches 32.5 MB). The K timed steps
+are captured once in a HIP graph (the way a frame step runs) and replayed.
+
+The JSON line's `value` is the decode layer's algorithmic HBM bytes per step
+divided by the time per step, in TB/s; `us_per_layer` is that time. The same
+run also times 1024-row chunks (uniform and skewed routing) and reports FP8
+TFLOP/s, and times the CPU oracle on a bounded sample for context.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import block_fp8_mixture_router_amd as moe  # noqa: E402
+from block_fp8_mixture_router_amd import inputs  # noqa: E402
+
+METRIC = "decode µs/layer + HBM TB/s; 1024-row chunk FP8 TFLOP/s (% of peak)"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0  # dense MFMA, no sparsity
+
+
+def decode_bytes(shape, rows=1, experts_touched=None) -> int:
+    """Algorithmic HBM bytes of one layer pass: every touched expert's codes
+    and scales once, shared expert, router, gate vector, x and y."""
+    k = shape.top_k * rows if experts_touched is None else experts_touched
+    routed = k * shape.expert_bytes()
+    shared = 3 * shape.hidden * shape.shared_inter * 2
+    router = shape.n_experts * shape.hidden * 2
+    return routed + shared + router + shape.hidden * 2 + rows * shape.hidden * 2 * 2
+
+
+def fp8_flops(shape, rows) -> int:
+    return 2 * rows * shape.top_k * 3 * shape.hidden * shape.inter
+
+
+def graph_time(step_fn, n_steps, warmup, stream):
+    """Capture n_steps calls in one graph; returns seconds for one replay."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step_fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n_steps):
+            step_fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3, g
+
+
+def cpu_baseline(shape, host_layer, target_s=10.0):
+    import oracle
+    x = inputs.make_x(shape, 256, seed=99)
+    rows, took = 8, 0.0
+    oracle.forward(shape, host_layer, x[:1])  # warm
+    while True:
+        t0 = time.perf_counter()
+        oracle.forward(shape, host_layer, x[:rows])
+        took = time.perf_counter() - t0
+        if took >= target_s / 3 or rows >= 256:
+            break
+        rows = min(256, rows * 4)
+    per_row = took / rows
+    return {
+        "value": decode_bytes(shape) / per_row / 1e12,
+        "unit": "TB/s",
+        "us_per_layer": per_row * 1e6,
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} rows of the decode layer in one oracle call "
+                  f"({took:.1f} s); per-row time taken as the layer time",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1600)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--chunk-steps", type=int, default=16)
+    ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is benchmarked at its single-GPU shape)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if not moe.supported(0):
+        raise SystemExit("cuda:0 is not a gfx950 GPU")
+    shape = inputs.DECODE
+    L = args.layers
+    print(f"[bench] generating {L} decode layers", file=sys.stderr, flush=True)
+    layers = [inputs.make_layer(shape, seed=0, layer=l, device="cuda") for l in range(L)]
+    wstructs = [moe.weights_struct(lw) for lw in layers]
+    xs = inputs.make_x(shape, L, seed=0, device="cuda")
+    ys = torch.empty_like(xs)
+    cfg = moe.config(shape)
+    ws = moe.alloc_workspace(cfg, 1024)
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        j = i % L
+        moe.forward(cfg, layers[j], xs[j:j + 1], y=ys[j:j + 1], workspace=ws,
+                    wstruct=wstructs[j], stream=stream)
+
+    print(f"[bench] decode: {args.steps} steps", file=sys.stderr, flush=True)
+    secs, _ = graph_time(step, args.steps, args.warmup, stream)
+    us = secs / args.steps * 1e6
+    nbytes = decode_bytes(shape)
+    tbs = nbytes / (us * 1e-6) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(tbs, 4), "unit": "TB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": secs / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "decode_1row", "hidden": shape.hidden,
+                   "experts": shape.n_experts, "top_k": shape.top_k, "inter": shape.inter,
+                   "shared_inter": shape.shared_inter, "rows": 1, "layers_rotated": L},
+        "us_per_layer": round(us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "whole decode layer (graph of its launches)",
+                     "bytes_per_launch": nbytes},
+    }
+    if not args.no_chunk:
+        chunk = {}
+        xc = inputs.make_x(shape, 1024, seed=1, device="cuda")
+        yc = torch.empty_like(xc)
+        nrot = min(4, L)
+        for name, skew in (("chunk1024_uniform", False), ("chunk1024_skewed", True)):
+            bias = inputs.skew_bias(shape.n_experts).cuda() if skew else None
+            ls = []
+            for l in range(nrot):
+                lw = layers[l]
+                if skew:
+                    import dataclasses
+                    lw = dataclasses.replace(lw, router_bias=bias)
+                ls.append((lw, moe.weights_struct(lw)))
+            ids, _, _ = moe.route(cfg, xc, ls[0][0].router_w, bias,
+                                  logits=torch.empty(1024, shape.n_experts, device="cuda"))
+            touched = int(torch.unique(ids).numel())
+
+            def cstep(i, ls=ls):
+                lw, wsr = ls[i % nrot]
+                moe.forward(cfg, lw, xc, y=yc, workspace=ws, wstruct=wsr, stream=stream)
+
+            print(f"[bench] {name}: {args.chunk_steps} steps", file=sys.stderr, flush=True)
+            csecs, _ = graph_time(cstep, args.chunk_steps, 2, stream)
+            cus = csecs / args.chunk_steps * 1e6
+            fl = fp8_flops(shape, 1024)
+            cb = decode_bytes(shape, rows=1024, experts_touched=touched)
+            tflops = fl / (cus * 1e-6) / 1e12
+            attain = min(FP8_PEAK_TFLOPS, fl / cb * HBM_PEAK_GBS / 1e3)
+            chunk[name] = {"us_per_chunk": round(cus, 2), "fp8_tflops": round(tflops, 1),
+                           "pct_fp8_peak": round(100 * tflops / FP8_PEAK_TFLOPS, 2),
+                           "roofline_attainable_tflops": round(attain, 1),
+                           "pct_of_attainable": round(100 * tflops / attain, 1),
+                           "hbm_tbs_algorithmic": round(cb / (cus * 1e-6) / 1e12, 3),
+                           "experts_touched": touched, "algorithmic_bytes": cb}
+        rec["chunk"] = chunk
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+"""Python binding of libmoe, the gfx950 block-FP8 MoE layer (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch tensors on the current device; the stream is torch's current
+stream. If the library is missing or the device is not gfx950 the calls raise
+(there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
+          -4: "MOE_E_WORKSPACE", -5: "MOE_E_UNSUPPORTED", -6: "MOE_E_LAUNCH"}
+LOGITS_FP32 = 1 << 1
+FORCE_GEMV = 1 << 8
+FORCE_GROUPED = 1 << 9
+
+EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
+           "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "router_bias", "w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down",
+        "sh_gate", "sh_up", "sh_down", "sh_gate_w")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (loads the HIP runtime torch uses)
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() or "
+                "python block_fp8_mixture_router_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.moe_supported.argtypes = [ctypes.c_int]
+        L.moe_supported.restype = ctypes.c_int
+        L.moe_workspace_bytes.argtypes = [vp, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_quant_act.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_quant_act.restype = ctypes.c_int
+        L.moe_forward.argtypes = [vp, vp, vp, i32, vp, vp, sz, vp]
+        L.moe_forward.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def config(shape, flags: int = 0, shared: bool = True) -> Config:
+    return Config(shape.hidden, shape.n_experts, shape.top_k, shape.inter,
+                  shape.shared_inter if shared else 0, flags)
+
+
+def supported(device: int = 0) -> bool:
+    return bool(lib().moe_supported(device))
+
+
+def workspace_bytes(cfg: Config, max_rows: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(cfg), max_rows))
+
+
+def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
+    import torch
+    n = workspace_bytes(cfg, max_rows)
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def quant_act(x, q=None, scales=None, stream=None):
+    """x bf16 [T, C] -> (q uint8 [T, C] e4m3 codes, scales fp32 [T, C/128])."""
+    import torch
+    T, C = x.shape
+    if q is None:
+        q = torch.empty((T, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T, C // 128), dtype=torch.float32, device=x.device)
+    _check("moe_quant_act", lib().moe_quant_act(_ptr(x), T, C, _ptr(q), _ptr(scales),
+                                                _stream(stream)))
+    return q, scales
+
+
+def route(cfg: Config, x, router_w, router_bias=None, ids=None, weights=None, logits=None,
+          workspace=None, stream=None):
+    """-> (ids int32 [T,K], weights fp32 [T,K], logits fp32 [T,E] or None)."""
+    import torch
+    T = x.shape[0]
+    if ids is None:
+        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, cfg.top_k), dtype=torch.float32, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check("moe_route", lib().moe_route(
+        ctypes.byref(cfg), _ptr(x), T, _ptr(router_w), _ptr(router_bias), _ptr(ids),
+        _ptr(weights), _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)))
+    return ids, weights, logits
+
+
+def weights_struct(lw) -> Weights:
+    """Weights struct from an object with the tensor attributes of
+    inputs.LayerWeights (all on the device)."""
+    return Weights(**{k: _ptr(getattr(lw, k)) for k, _ in Weights._fields_})
+
+
+def forward(cfg: Config, lw, x, y=None, workspace=None, stream=None, wstruct=None):
+    """Whole layer: y bf16 [T, H]."""
+    import torch
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, max(T, 1), x.device)
+    ws = wstruct if wstruct is not None else weights_struct(lw)
+    _check("moe_forward", lib().moe_forward(
+        ctypes.byref(cfg), ctypes.byref(ws), _ptr(x), T, _ptr(y), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return y

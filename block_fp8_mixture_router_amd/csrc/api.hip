@@ -1,0 +1,248 @@
+// C ABI of libmoe: validation, workspace layout and dispatch.
+//
+// Conventions follow the host code the pages describe: shapes the kernels
+// cannot honour are refused at the door with a named code, before anything
+// is enqueued; buffers are caller-owned and the library allocates nothing
+// (PR #925 "drama: load the checkpoint with direct I/O in file order and
+// build the codec on its own thread", commit summaries on refusal at open
+// and on the allocation cap; PR #939 "drama3: Fish Audio Drama 3 text to
+// speech on one CUDA GPU", "What it adds": config.zig refuses other shapes).
+#include <atomic>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<int> g_dev_state[MAX_DEVICES];  // 0 unknown, 1 gfx950, 2 other
+
+int device_is_gfx950(int dev) {
+    if (dev < 0 || dev >= MAX_DEVICES) return 0;
+    int s = g_dev_state[dev].load(std::memory_order_acquire);
+    if (s == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return 0;
+        s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_state[dev].store(s, std::memory_order_release);
+    }
+    return s == 1;
+}
+
+bool current_device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    return device_is_gfx950(dev) != 0;
+}
+
+bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_cfg(const moe_config *c) {
+    if (!c) return MOE_E_NULL;
+    const uint32_t known = MOE_LOGITS_FP32 | MOE_FORCE_GEMV | MOE_FORCE_GROUPED;
+    if (c->flags & ~known) return MOE_E_UNSUPPORTED;
+    if ((c->flags & MOE_FORCE_GEMV) && (c->flags & MOE_FORCE_GROUPED)) return MOE_E_UNSUPPORTED;
+    if (c->hidden < 128 || c->hidden > 8192 || c->hidden % 128) return MOE_E_SHAPE;
+    if (c->inter < 128 || c->inter > 4096 || c->inter % 128) return MOE_E_SHAPE;
+    if (c->shared_inter < 0 || c->shared_inter > 4096 || c->shared_inter % 128) return MOE_E_SHAPE;
+    if (c->n_experts < 1 || c->n_experts > 1024) return MOE_E_SHAPE;
+    if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return MOE_E_SHAPE;
+    return MOE_OK;
+}
+
+constexpr int MAX_ROWS = 65536;
+
+size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t logits, ids, wts, gamma, h, hs, qx, sx, offsets, perm, tiles, n_tiles, qh, sh, stage;
+    size_t total;
+    int max_tiles;
+};
+
+Layout layout_of(const moe_config *c, int T) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += a256(bytes);
+        return o;
+    };
+    const size_t t = (size_t)T, E = c->n_experts, K = c->top_k, H = c->hidden, I = c->inter,
+                 Is = c->shared_inter;
+    L.max_tiles = grouped_max_tiles(T, (int)K, (int)E);
+    L.logits = take(t * E * 4);
+    L.ids = take(t * K * 4);
+    L.wts = take(t * K * 4);
+    L.gamma = take(t * 4);
+    L.h = take(t * K * I * 4);
+    L.hs = take(t * Is * 2);
+    L.qx = take(t * H);
+    L.sx = take(t * (H / 128) * 4);
+    L.offsets = take((E + 1) * 4);
+    L.perm = take(t * K * 4);
+    L.tiles = take((size_t)L.max_tiles * 16);
+    L.n_tiles = take(4);
+    L.qh = take(t * K * I);
+    L.sh = take(t * K * (I / 128) * 4);
+    L.stage = take(t * K * H * 2);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<unsigned char *>(ws) + off);
+}
+
+#define MOE_TRY(expr)                                  \
+    do {                                               \
+        if ((expr) != hipSuccess) return MOE_E_LAUNCH; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moe_supported(int device) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return 0;
+    return device_is_gfx950(device);
+}
+
+size_t moe_workspace_bytes(const moe_config *cfg, int32_t max_rows) {
+    if (check_cfg(cfg) != MOE_OK || max_rows < 0 || max_rows > MAX_ROWS) return 0;
+    return layout_of(cfg, max_rows < 1 ? 1 : max_rows).total;
+}
+
+moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float *scales,
+                         void *stream) {
+    if (T < 0 || T > MAX_ROWS || C < 128 || C > 65536 || C % 128) return MOE_E_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !q || !scales) return MOE_E_NULL;
+    if (!al16(x) || !al16(q) || (reinterpret_cast<uintptr_t>(scales) & 3u)) return MOE_E_ALIGN;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    MOE_TRY(launch_quant_act(static_cast<const uint16_t *>(x), (int64_t)T * (C / 128), q, scales,
+                             static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void *router_w,
+                     const float *router_bias, int32_t *ids, float *weights, float *logits,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status s = check_cfg(cfg);
+    if (s != MOE_OK) return s;
+    if (T < 0 || T > MAX_ROWS) return MOE_E_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !router_w || !ids || !weights) return MOE_E_NULL;
+    if (!logits && !workspace) return MOE_E_NULL;
+    if (!al16(x) || !al16(router_w) || !al16(ids) || !al16(weights) ||
+        (logits && !al16(logits)) || (router_bias && !al16(router_bias)))
+        return MOE_E_ALIGN;
+    if (!logits) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
+        if (workspace_bytes < layout_of(cfg, T).total) return MOE_E_WORKSPACE;
+    }
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *lg = logits ? logits : at<float>(workspace, layout_of(cfg, T).logits);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(router_w), router_bias,
+                                cfg->hidden, cfg->n_experts, cfg->flags, lg, st));
+    MOE_TRY(launch_route_topk(lg, T, cfg->n_experts, cfg->top_k, ids, weights, nullptr, nullptr,
+                              cfg->hidden, nullptr, st));
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int32_t T,
+                       void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status s = check_cfg(cfg);
+    if (s != MOE_OK) return s;
+    if (T < 0 || T > MAX_ROWS) return MOE_E_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!w || !x || !y || !workspace) return MOE_E_NULL;
+    if (!w->router_w || !w->w_gate || !w->s_gate || !w->w_up || !w->s_up || !w->w_down ||
+        !w->s_down)
+        return MOE_E_NULL;
+    const bool shared = cfg->shared_inter > 0;
+    if (shared && (!w->sh_gate || !w->sh_up || !w->sh_down || !w->sh_gate_w)) return MOE_E_NULL;
+    const void *ptrs[] = {x, y, w->router_w, w->w_gate, w->s_gate, w->w_up, w->s_up,
+                          w->w_down, w->s_down};
+    for (const void *p : ptrs)
+        if (!al16(p)) return MOE_E_ALIGN;
+    if (w->router_bias && !al16(w->router_bias)) return MOE_E_ALIGN;
+    if (shared && (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down) ||
+                   !al16(w->sh_gate_w)))
+        return MOE_E_ALIGN;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
+    const Layout L = layout_of(cfg, T);
+    if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
+    if (x == y) return MOE_E_UNSUPPORTED;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int H = cfg->hidden, E = cfg->n_experts, K = cfg->top_k;
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    float *lg = at<float>(workspace, L.logits);
+    int32_t *ids = at<int32_t>(workspace, L.ids);
+    float *wts = at<float>(workspace, L.wts);
+    float *gamma = at<float>(workspace, L.gamma);
+    MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(w->router_w),
+                                w->router_bias, H, E, cfg->flags, lg, st));
+    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
+                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
+                              gamma, st));
+
+    const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
+                      (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4);
+    if (gemv) {
+        DecodeArgs a{};
+        a.T = T; a.H = H; a.E = E; a.K = K; a.I = cfg->inter; a.Is = cfg->shared_inter;
+        a.x = xb; a.ids = ids; a.wts = wts; a.gamma = gamma;
+        a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+        a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+        a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
+        a.sh_up = static_cast<const uint16_t *>(w->sh_up);
+        a.sh_down = static_cast<const uint16_t *>(w->sh_down);
+        a.h = at<float>(workspace, L.h);
+        a.hs = at<uint16_t>(workspace, L.hs);
+        a.y = static_cast<uint16_t *>(y);
+        MOE_TRY(launch_decode_gateup(a, st));
+        MOE_TRY(launch_decode_down(a, st));
+        return MOE_OK;
+    }
+    GroupedArgs g{};
+    g.T = T; g.H = H; g.E = E; g.K = K; g.I = cfg->inter; g.Is = cfg->shared_inter;
+    g.x = xb;
+    g.qx = at<uint8_t>(workspace, L.qx);
+    g.sx = at<float>(workspace, L.sx);
+    g.ids = ids; g.wts = wts; g.gamma = gamma;
+    g.w_gate = w->w_gate; g.w_up = w->w_up; g.w_down = w->w_down;
+    g.s_gate = w->s_gate; g.s_up = w->s_up; g.s_down = w->s_down;
+    g.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
+    g.sh_up = static_cast<const uint16_t *>(w->sh_up);
+    g.sh_down = static_cast<const uint16_t *>(w->sh_down);
+    g.offsets = at<int32_t>(workspace, L.offsets);
+    g.perm = at<int32_t>(workspace, L.perm);
+    g.tiles = at<int32_t>(workspace, L.tiles);
+    g.n_tiles = at<int32_t>(workspace, L.n_tiles);
+    g.max_tiles = L.max_tiles;
+    g.qh = at<uint8_t>(workspace, L.qh);
+    g.sh = at<float>(workspace, L.sh);
+    g.hs = at<uint16_t>(workspace, L.hs);
+    g.stage = at<uint16_t>(workspace, L.stage);
+    g.y = static_cast<uint16_t *>(y);
+    MOE_TRY(launch_quant_act(xb, (int64_t)T * (H / 128), const_cast<uint8_t *>(g.qx),
+                             const_cast<float *>(g.sx), st));
+    MOE_TRY(launch_group_sort(g, st));
+    MOE_TRY(launch_grouped_gateup(g, st));
+    MOE_TRY(launch_shared_gateup(g, st));
+    MOE_TRY(launch_grouped_down(g, st));
+    MOE_TRY(launch_shared_down_combine(g, st));
+    return MOE_OK;
+}
+
+}  // extern "C"

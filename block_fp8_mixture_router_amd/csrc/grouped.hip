@@ -1,0 +1,604 @@
+// Expert-grouped path for prompt chunks: rows sorted by expert, block-FP8
+// GEMMs on gfx950 FP8 matrix cores, bf16 shared expert on bf16 matrix cores,
+// and a combine that reads every slot's output with 16-byte loads.
+//
+// The pages run the FP8 experts "on FP8 rows with per-row scales", write the
+// SwiGLU's routed rows as FP8 and the shared rows as bf16, and combine with
+// 8 contiguous outputs per thread from 16-byte loads in a fixed order
+// (PR #939 "drama3: Fish Audio Drama 3 text to speech on one CUDA GPU",
+// "What it adds"; PR #925 "drama: load the checkpoint with direct I/O in file
+// order and build the codec on its own thread", commit summaries of the
+// SwiGLU launch and of drama_moe_combine).
+//
+// MI355X design:
+//  - v_mfma_scale_f32_16x16x128_f8f6f4 consumes K = 128 per instruction,
+//    exactly one 128x128 weight block and one activation group, so each MFMA
+//    starts from zero and the lane folds (activation scale x weight scale) into
+//    its fp32 accumulator: the block scaling costs four FMAs per MFMA.
+//  - A work tile is up to 64 sorted (row, slot) pairs of one expert times 128
+//    output columns; activations are staged through LDS (shared by the four
+//    waves), weights stream straight from HBM into registers (each weight
+//    byte is used by one wave only), double-buffered one K step ahead.
+//  - The gate/up epilogue applies SwiGLU and re-quantises each pair's 128
+//    columns (one group) to e4m3 before anything leaves the CU.
+//  - No floating-point atomics anywhere: every sum has a fixed order, so
+//    results are bitwise deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int GR = GROUP_ROWS;   // 64 rows per tile
+constexpr int APAD = 16;         // LDS row padding (bytes) against bank conflicts
+
+int grouped_max_tiles(int T, int K, int E) {
+    const int64_t P = (int64_t)T * K;
+    const int64_t used = P < E ? P : E;
+    return (int)((P + GR - 1) / GR + used + 1);
+}
+
+// ------------------------------------------------------------- group sort
+// One workgroup of 1024 threads. Stable counting sort of the T*K (row,slot)
+// pairs by expert: wave w owns a contiguous segment of pairs; pass A counts
+// per (wave, expert); pass B walks the segment in order, 64 pairs at a time,
+// and ranks equal experts within the step with ballots over the key bits.
+
+__global__ __launch_bounds__(1024) void group_sort_kernel(const int32_t *__restrict__ ids,
+                                                          int P, int E,
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ perm,
+                                                          int32_t *__restrict__ tiles,
+                                                          int32_t *__restrict__ n_tiles) {
+    __shared__ int wbase[16][1024];
+    __shared__ int offs[1024];
+    __shared__ int scan_c[1024];
+    __shared__ int scan_t[1024];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int e = tid; e < 1024; e += 1024)
+        for (int w = 0; w < 16; ++w) wbase[w][e] = 0;
+    __syncthreads();
+    const int seg = (P + 15) / 16;
+    const int p_begin = wave * seg;
+    const int p_end = min(P, p_begin + seg);
+    for (int p = p_begin + lane; p < p_end; p += 64) atomicAdd(&wbase[wave][ids[p]], 1);
+    __syncthreads();
+    int total = 0;
+    if (tid < E) {
+        for (int w = 0; w < 16; ++w) {
+            const int c = wbase[w][tid];
+            wbase[w][tid] = total;
+            total += c;
+        }
+    }
+    const int ntile = (total + GR - 1) / GR;
+    scan_c[tid] = total;
+    scan_t[tid] = ntile;
+    __syncthreads();
+    // inclusive Hillis-Steele scans over the 1024 experts
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int c = tid >= o ? scan_c[tid - o] : 0;
+        const int t = tid >= o ? scan_t[tid - o] : 0;
+        __syncthreads();
+        scan_c[tid] += c;
+        scan_t[tid] += t;
+        __syncthreads();
+    }
+    if (tid < E) {
+        const int off = scan_c[tid] - total;
+        const int tb = scan_t[tid] - ntile;
+        offs[tid] = off;
+        offsets[tid] = off;
+        for (int i = 0; i < ntile; ++i) {
+            int32_t *tl = tiles + 4 * (tb + i);
+            tl[0] = tid;
+            tl[1] = off + i * GR;
+            tl[2] = min(GR, total - i * GR);
+            tl[3] = 0;
+        }
+        if (tid == E - 1) {
+            offsets[E] = scan_c[tid];
+            *n_tiles = scan_t[tid];
+        }
+    }
+    __syncthreads();
+    int kbits = 0;
+    while ((1 << kbits) < E) ++kbits;
+    for (int p0 = p_begin; p0 < p_end; p0 += 64) {
+        const int p = p0 + lane;
+        const bool valid = p < p_end;
+        const int e = valid ? ids[p] : 0;
+        uint64_t mask = __ballot(valid);
+        for (int b = 0; b < kbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(valid && bit);
+            mask &= bit ? bal : ~bal;
+        }
+        const uint64_t below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
+        const int rank = __popcll(below);
+        const int n = __popcll(mask);
+        int base = 0;
+        if (valid) base = wbase[wave][e];
+        if (valid) perm[offs[e] + base + rank] = p;
+        if (valid && rank == 0) wbase[wave][e] = base + n;
+    }
+}
+
+hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(group_sort_kernel, dim3(1), dim3(1024), 0, st, a.ids, a.T * a.K, a.E,
+                       a.offsets, a.perm, a.tiles, a.n_tiles);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- FP8 MFMA helpers
+
+__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// 16x16 output, K = 128 e4m3 per operand; E8M0 scales 127 = x1.
+__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// ----------------------------------------------------------- gate / up
+// grid.x = max_tiles * (I / 128). Wave w owns output columns
+// [nb*128 + 32w, +32): two 16-column MFMA tiles for gate and two for up.
+
+__global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[GR][GROUP + APAD];
+    __shared__ float sxs[GR][64];
+    __shared__ int toks[GR];
+    __shared__ float amax_part[4][GR];
+    const int nbs = a.I / GROUP;
+    const int tile = blockIdx.x / nbs, nb = blockIdx.x % nbs;
+    if (tile >= *a.n_tiles) return;
+    const int e = a.tiles[4 * tile], r0 = a.tiles[4 * tile + 1], nr = a.tiles[4 * tile + 2];
+    const int H = a.H, I = a.I, KB = H / GROUP;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    if (tid < GR) toks[tid] = tid < nr ? a.perm[r0 + tid] / a.K : -1;
+    __syncthreads();
+    for (int idx = tid; idx < GR * KB; idx += 256) {
+        const int row = idx / KB, b = idx % KB;
+        const int t = toks[row];
+        sxs[row][b] = t >= 0 ? a.sx[(int64_t)t * KB + b] : 0.0f;
+    }
+    // activation staging: thread -> (row, 32-byte slice)
+    const int arow = tid >> 2, acol = (tid & 3) * 32;
+    const int atok = toks[arow];
+    const uint8_t *aptr = a.qx + (int64_t)(atok >= 0 ? atok : 0) * H + acol;
+    // weights: lane (l16, kq) -> column n, bytes [32kq, 32kq + 32) of each K block
+    const uint8_t *wgp[2], *wup[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int n = nb * GROUP + 32 * wave + 16 * ct + l16;
+        wgp[ct] = a.w_gate + ((int64_t)e * I + n) * H + 32 * kq;
+        wup[ct] = a.w_up + ((int64_t)e * I + n) * H + 32 * kq;
+    }
+    const float *sgr = a.s_gate + ((int64_t)e * nbs + nb) * KB;
+    const float *sur = a.s_up + ((int64_t)e * nbs + nb) * KB;
+    const int nrt = (nr + 15) / 16;
+
+    v4f accg[4][2], accu[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) accg[rt][ct] = accu[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    uint4 bg[2][2], bu[2][2], av[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        bg[ct][0] = ld16(wgp[ct]);
+        bg[ct][1] = ld16(wgp[ct] + 16);
+        bu[ct][0] = ld16(wup[ct]);
+        bu[ct][1] = ld16(wup[ct] + 16);
+    }
+    av[0] = atok >= 0 ? ld16(aptr) : make_uint4(0, 0, 0, 0);
+    av[1] = atok >= 0 ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
+
+    for (int kb = 0; kb < KB; ++kb) {
+        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
+        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
+        __syncthreads();
+        v8i cg[2], cu[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            cg[ct] = as_v8i(bg[ct][0], bg[ct][1]);
+            cu[ct] = as_v8i(bu[ct][0], bu[ct][1]);
+        }
+        if (kb + 1 < KB) {
+            const int off = (kb + 1) * GROUP;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bg[ct][0] = ld16(wgp[ct] + off);
+                bg[ct][1] = ld16(wgp[ct] + off + 16);
+                bu[ct][0] = ld16(wup[ct] + off);
+                bu[ct][1] = ld16(wup[ct] + off + 16);
+            }
+            if (atok >= 0) {
+                av[0] = ld16(aptr + off);
+                av[1] = ld16(aptr + off + 16);
+            }
+        }
+        const float sgk = sgr[kb], suk = sur[kb];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt < nrt) {
+                const uint8_t *ar = &As[rt * 16 + l16][32 * kq];
+                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                      *reinterpret_cast<const uint4 *>(ar + 16));
+                float sxr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sxr[i] = sxs[rt * 16 + 4 * kq + i][kb];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const v4f pg = mfma_fp8_k128(af, cg[ct]);
+                    const v4f pu = mfma_fp8_k128(af, cu[ct]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        accg[rt][ct][i] = fmaf(sxr[i] * sgk, pg[i], accg[rt][ct][i]);
+                        accu[rt][ct][i] = fmaf(sxr[i] * suk, pu[i], accu[rt][ct][i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: h = silu(g) * u, per-row amax over the 128 columns, e4m3
+    float hv[4][2][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        float m4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hv[rt][ct][i] = silu(accg[rt][ct][i]) * accu[rt][ct][i];
+                m4[i] = fmaxf(m4[i], fabsf(hv[rt][ct][i]));
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float m = wave_max<16>(m4[i]);
+            if (l16 == 0) amax_part[wave][rt * 16 + 4 * kq + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t(*Cs)[GROUP + APAD] = As;  // reuse the staging buffer for codes
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rt * 16 + 4 * kq + i;
+            const float am = fmaxf(fmaxf(amax_part[0][row], amax_part[1][row]),
+                                   fmaxf(amax_part[2][row], amax_part[3][row]));
+            const float sc = group_scale(am);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const uint32_t code = e4m3x4(hv[rt][ct][i] / sc, 0.f, 0.f, 0.f) & 0xFFu;
+                Cs[row][32 * wave + 16 * ct + l16] = (uint8_t)code;
+            }
+            if (wave == 0 && l16 == 0 && row < nr)
+                a.sh[(int64_t)(r0 + row) * nbs + nb] = sc;
+        }
+    __syncthreads();
+    for (int idx = tid; idx < GR * 8; idx += 256) {
+        const int row = idx >> 3, c = idx & 7;
+        if (row < nr)
+            st16(a.qh + (int64_t)(r0 + row) * I + nb * GROUP + c * 16,
+                 *reinterpret_cast<const uint4 *>(&Cs[row][c * 16]));
+    }
+}
+
+hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(a.max_tiles * (a.I / GROUP)));
+    hipLaunchKernelGGL(grouped_gateup_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- down
+// grid.x = max_tiles * (H / 128). Outputs e_j in bf16, written to the
+// (row, slot) pair's own row of the stage buffer.
+
+__global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[GR][GROUP + APAD];
+    __shared__ float shs[GR][32];
+    __shared__ int pairs[GR];
+    __shared__ __align__(16) uint16_t Ys[GR][GROUP + 8];
+    const int mbs = a.H / GROUP;
+    const int tile = blockIdx.x / mbs, mb = blockIdx.x % mbs;
+    if (tile >= *a.n_tiles) return;
+    const int e = a.tiles[4 * tile], r0 = a.tiles[4 * tile + 1], nr = a.tiles[4 * tile + 2];
+    const int H = a.H, I = a.I, KB = I / GROUP;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    if (tid < GR) pairs[tid] = tid < nr ? a.perm[r0 + tid] : -1;
+    for (int idx = tid; idx < GR * KB; idx += 256) {
+        const int row = idx / KB, b = idx % KB;
+        shs[row][b] = row < nr ? a.sh[(int64_t)(r0 + row) * KB + b] : 0.0f;
+    }
+    const int arow = tid >> 2, acol = (tid & 3) * 32;
+    const bool arv = arow < nr;
+    const uint8_t *aptr = a.qh + (int64_t)(r0 + (arv ? arow : 0)) * I + acol;
+    const uint8_t *wdp[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int m = mb * GROUP + 32 * wave + 16 * ct + l16;
+        wdp[ct] = a.w_down + ((int64_t)e * H + m) * I + 32 * kq;
+    }
+    const float *sdr = a.s_down + ((int64_t)e * mbs + mb) * KB;
+    const int nrt = (nr + 15) / 16;
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+    uint4 bd[2][2], av[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        bd[ct][0] = ld16(wdp[ct]);
+        bd[ct][1] = ld16(wdp[ct] + 16);
+    }
+    av[0] = arv ? ld16(aptr) : make_uint4(0, 0, 0, 0);
+    av[1] = arv ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
+    __syncthreads();  // shs and pairs ready
+
+    for (int kb = 0; kb < KB; ++kb) {
+        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
+        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
+        __syncthreads();
+        v8i cd[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) cd[ct] = as_v8i(bd[ct][0], bd[ct][1]);
+        if (kb + 1 < KB) {
+            const int off = (kb + 1) * GROUP;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bd[ct][0] = ld16(wdp[ct] + off);
+                bd[ct][1] = ld16(wdp[ct] + off + 16);
+            }
+            if (arv) {
+                av[0] = ld16(aptr + off);
+                av[1] = ld16(aptr + off + 16);
+            }
+        }
+        const float sdk = sdr[kb];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt < nrt) {
+                const uint8_t *ar = &As[rt * 16 + l16][32 * kq];
+                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                      *reinterpret_cast<const uint4 *>(ar + 16));
+                float shr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) shr[i] = shs[rt * 16 + 4 * kq + i][kb];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const v4f p = mfma_fp8_k128(af, cd[ct]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[rt][ct][i] = fmaf(shr[i] * sdk, p[i], acc[rt][ct][i]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Ys[rt * 16 + 4 * kq + i][32 * wave + 16 * ct + l16] =
+                    (uint16_t)f32_to_bf16(acc[rt][ct][i]);
+    __syncthreads();
+    for (int idx = tid; idx < GR * 16; idx += 256) {
+        const int row = idx >> 4, c = idx & 15;
+        if (row < nr)
+            st16(a.stage + (int64_t)pairs[row] * H + mb * GROUP + c * 8,
+                 *reinterpret_cast<const uint4 *>(&Ys[row][c * 8]));
+    }
+}
+
+hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(a.max_tiles * (a.H / GROUP)));
+    hipLaunchKernelGGL(grouped_down_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- bf16 MFMA helpers
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+__device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------- shared gate / up
+// Tile: 32 rows x 64 columns of Is; grid (ceil(T/32), Is/64). Wave w owns
+// 16 columns of gate and up. Each lane reads 64 contiguous bytes of its
+// weight row per 128 columns of H and splits them over four MFMAs; the LDS
+// activation fragments follow the same column split.
+
+constexpr int SR = 32;  // rows per shared-expert tile
+
+__global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[SR][GROUP * 2 + APAD];
+    const int H = a.H, Is = a.Is;
+    const int t0 = blockIdx.x * SR, nb = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int arow = tid >> 3, acol = (tid & 7) * 32;  // bytes
+    const bool arv = t0 + arow < a.T;
+    const uint8_t *aptr =
+        reinterpret_cast<const uint8_t *>(a.x + (int64_t)(arv ? t0 + arow : 0) * H) + acol;
+    const int n = nb * 64 + 16 * wave + l16;
+    const uint8_t *gp = reinterpret_cast<const uint8_t *>(a.sh_gate + (int64_t)n * H) + 64 * kq;
+    const uint8_t *up = reinterpret_cast<const uint8_t *>(a.sh_up + (int64_t)n * H) + 64 * kq;
+    v4f accg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    v4f accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    uint4 bg[4], bu[4], av[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bg[i] = ld16(gp + 16 * i);
+        bu[i] = ld16(up + 16 * i);
+    }
+    av[0] = arv ? ld16(aptr) : make_uint4(0, 0, 0, 0);
+    av[1] = arv ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
+    const int KB = H / GROUP;
+    for (int kb = 0; kb < KB; ++kb) {
+        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
+        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
+        __syncthreads();
+        uint4 cg[4], cu[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cg[i] = bg[i];
+            cu[i] = bu[i];
+        }
+        if (kb + 1 < KB) {
+            const int off = (kb + 1) * GROUP * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bg[i] = ld16(gp + off + 16 * i);
+                bu[i] = ld16(up + off + 16 * i);
+            }
+            if (arv) {
+                av[0] = ld16(aptr + off);
+                av[1] = ld16(aptr + off + 16);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const uint8_t *ar = &As[rt * 16 + l16][64 * kq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+                accg[rt] = mfma_bf16_k32(af, as_v8bf(cg[i]), accg[rt]);
+                accu[rt] = mfma_bf16_k32(af, as_v8bf(cu[i]), accu[rt]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + rt * 16 + 4 * kq + i;
+            if (t < a.T)
+                a.hs[(int64_t)t * Is + n] = (uint16_t)f32_to_bf16(silu(accg[rt][i]) * accu[rt][i]);
+        }
+}
+
+hipError_t launch_shared_gateup(const GroupedArgs &a, hipStream_t st) {
+    if (a.Is == 0) return hipSuccess;
+    hipLaunchKernelGGL(shared_gateup_kernel, dim3((a.T + SR - 1) / SR, a.Is / 64), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------- shared down + combine
+// Tile: 32 rows x 128 columns of H; grid (ceil(T/32), H/128). The shared
+// expert's down product s lands in LDS; then each thread produces 8
+// contiguous outputs y = bf16(sum_j w_j e_j + gamma s) from 16-byte loads of
+// the staged e_j, summing the slots in order.
+
+__global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[SR][GROUP * 2 + APAD];
+    __shared__ __align__(16) float Ss[SR][GROUP + 4];
+    const int H = a.H, Is = a.Is, K = a.K;
+    const int t0 = blockIdx.x * SR, mb = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    if (Is > 0) {
+        const int arow = tid >> 3, acol = (tid & 7) * 32;
+        const bool arv = t0 + arow < a.T;
+        const uint8_t *aptr =
+            reinterpret_cast<const uint8_t *>(a.hs + (int64_t)(arv ? t0 + arow : 0) * Is) + acol;
+        const uint8_t *wp[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int m = mb * GROUP + 32 * wave + 16 * ct + l16;
+            wp[ct] = reinterpret_cast<const uint8_t *>(a.sh_down + (int64_t)m * Is) + 64 * kq;
+        }
+        v4f acc[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+        const int KB = Is / GROUP;
+        for (int kb = 0; kb < KB; ++kb) {
+            const int off = kb * GROUP * 2;
+            const uint4 a0 = arv ? ld16(aptr + off) : make_uint4(0, 0, 0, 0);
+            const uint4 a1 = arv ? ld16(aptr + off + 16) : make_uint4(0, 0, 0, 0);
+            uint4 b[2][4];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b[ct][i] = ld16(wp[ct] + off + 16 * i);
+            *reinterpret_cast<uint4 *>(&As[arow][acol]) = a0;
+            *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = a1;
+            __syncthreads();
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const uint8_t *ar = &As[rt * 16 + l16][64 * kq];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[ct][i]), acc[rt][ct]);
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Ss[rt * 16 + 4 * kq + i][32 * wave + 16 * ct + l16] = acc[rt][ct][i];
+        __syncthreads();
+    }
+    for (int idx = tid; idx < SR * 16; idx += 256) {
+        const int row = idx >> 4, c = idx & 15;
+        const int t = t0 + row;
+        if (t >= a.T) continue;
+        float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < K; ++j) {
+            const float w = a.wts[(int64_t)t * K + j];
+            const uint4 v = ld16(a.stage + ((int64_t)t * K + j) * H + mb * GROUP + c * 8);
+            const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc8[2 * i] = fmaf(w, bf16_lo(vs[i]), acc8[2 * i]);
+                acc8[2 * i + 1] = fmaf(w, bf16_hi(vs[i]), acc8[2 * i + 1]);
+            }
+        }
+        if (Is > 0) {
+            const float g = a.gamma[t];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc8[i] = fmaf(g, Ss[row][c * 8 + i], acc8[i]);
+        }
+        uint4 out;
+        out.x = f32_to_bf16(acc8[0]) | (f32_to_bf16(acc8[1]) << 16);
+        out.y = f32_to_bf16(acc8[2]) | (f32_to_bf16(acc8[3]) << 16);
+        out.z = f32_to_bf16(acc8[4]) | (f32_to_bf16(acc8[5]) << 16);
+        out.w = f32_to_bf16(acc8[6]) | (f32_to_bf16(acc8[7]) << 16);
+        st16(a.y + (int64_t)t * H + mb * GROUP + c * 8, out);
+    }
+}
+
+hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(shared_down_combine_kernel, dim3((a.T + SR - 1) / SR, a.H / GROUP),
+                       dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

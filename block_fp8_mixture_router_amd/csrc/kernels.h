@@ -1,0 +1,74 @@
+// Internal launchers of libmoe's gfx950 kernels. Every launcher enqueues on
+// `st` and returns the launch status; shapes were validated by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// flags understood by the router kernels (same bit as the public flag)
+constexpr uint32_t K_LOGITS_FP32 = 1u << 1;
+
+// ---- quant.hip
+hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, float *s,
+                            hipStream_t st);
+
+// ---- route.hip
+hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_w,
+                               const float *bias, int H, int E, uint32_t flags, float *logits,
+                               hipStream_t st);
+// top-K + softmax per row; when gate_w != NULL also gamma[t] = sigmoid(gate_w . x[t])
+hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids,
+                             float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
+                             float *gamma, hipStream_t st);
+
+// ---- decode.hip (row-at-a-time path)
+struct DecodeArgs {
+    int T, H, E, K, I, Is;
+    const uint16_t *x;
+    const int32_t *ids;
+    const float *wts;
+    const float *gamma;
+    const uint8_t *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+    const uint16_t *sh_gate, *sh_up, *sh_down;
+    float *h;         // [T, K, I] fp32 SwiGLU output of the routed experts
+    uint16_t *hs;     // [T, Is] bf16 SwiGLU output of the shared expert
+    uint16_t *y;      // [T, H] bf16
+};
+hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t st);
+
+// ---- grouped.hip (expert-grouped MFMA path)
+struct GroupedArgs {
+    int T, H, E, K, I, Is;
+    const uint16_t *x;
+    const uint8_t *qx;   // [T, H] e4m3
+    const float *sx;     // [T, H/128]
+    const int32_t *ids;  // [T, K]
+    const float *wts;    // [T, K]
+    const float *gamma;  // [T]
+    const uint8_t *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+    const uint16_t *sh_gate, *sh_up, *sh_down;
+    int32_t *offsets;    // [E + 1] start of each expert in the sorted pair list
+    int32_t *perm;       // [T*K] sorted position -> pair id (t*K + j)
+    int32_t *tiles;      // [max_tiles * 4] (expert, first sorted row, rows, 0)
+    int32_t *n_tiles;    // [1]
+    int max_tiles;
+    uint8_t *qh;         // [T*K, I] e4m3, sorted order
+    float *sh;           // [T*K, I/128]
+    uint16_t *hs;        // [T, Is] bf16
+    uint16_t *stage;     // [T*K, H] bf16 expert outputs e_j, pair order
+    uint16_t *y;         // [T, H]
+};
+constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
+int grouped_max_tiles(int T, int K, int E);
+hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st);
+hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st);
+hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st);
+hipError_t launch_shared_gateup(const GroupedArgs &a, hipStream_t st);
+hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,199 @@
+// Router: logits, top-K selection and renormalised softmax.
+//
+// The pages' router decides on bf16 logits and runs its softmax in fp32
+// (PR #939 "drama3: Fish Audio Drama 3 text to speech on one CUDA GPU",
+// "Fidelity against the PyTorch oracle" and "How it fits the engine" >
+// Precision). bf16 logits tie often, so any change of summation order would
+// move picks; each logit here is the exact sum of the exact bf16 x bf16
+// products, accumulated in fp64 and rounded once to fp32, then to bf16.
+//
+// Two logit kernels:
+//  - few rows (decode): one wave per (row, expert), 16-byte loads, fp64 FMA,
+//    a wave reduction; the 1 MiB router matrix streams once per row.
+//  - many rows (prompt chunks): fp64 MFMA 16x16x4 tiles, 16 rows x 16 experts
+//    per wave; each lane streams 32 contiguous bytes of its row and of its
+//    expert per 64 columns and the MFMA sums over the lanes' column slices.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__device__ __forceinline__ float finish_logit(double acc, const float *bias, int e,
+                                              uint32_t flags) {
+    float l = (float)acc;  // the single rounding of the exact sum to fp32
+    if (!(flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
+    if (bias) l = l + bias[e];
+    return l;
+}
+
+__global__ __launch_bounds__(256) void route_logits_vec(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ rw,
+                                                        const float *__restrict__ bias, int H,
+                                                        int E, uint32_t flags,
+                                                        float *__restrict__ logits) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.y;
+    if (e >= E) return;
+    const uint16_t *xr = x + (int64_t)t * H;
+    const uint16_t *wr = rw + (int64_t)e * H;
+    double acc = 0.0;
+    for (int c = lane; c < H / 8; c += WAVE) {
+        const uint4 a = ld16(xr + c * 8), b = ld16(wr + c * 8);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fma((double)bf16_lo(av[i]), (double)bf16_lo(bv[i]), acc);
+            acc = fma((double)bf16_hi(av[i]), (double)bf16_hi(bv[i]), acc);
+        }
+    }
+    acc = wave_sum_f64<64>(acc);
+    if (lane == 0) logits[(int64_t)t * E + e] = finish_logit(acc, bias, e, flags);
+}
+
+// grid: x = ceil(E / 64) (four waves of 16 experts), y = ceil(T / 16)
+__global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restrict__ x, int T,
+                                                         const uint16_t *__restrict__ rw,
+                                                         const float *__restrict__ bias, int H,
+                                                         int E, uint32_t flags,
+                                                         float *__restrict__ logits) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e0 = (blockIdx.x * 4 + wave) * 16;
+    if (e0 >= E) return;
+    const int t0 = blockIdx.y * 16;
+    const int r = lane & 15, q = lane >> 4;
+    const bool tv = t0 + r < T, ev = e0 + r < E;
+    // lane (r, q) supplies row r / expert r, columns [k + 16q, k + 16q + 16)
+    const uint16_t *xr = x + (int64_t)(tv ? t0 + r : 0) * H + q * 16;
+    const uint16_t *wr = rw + (int64_t)(ev ? e0 + r : 0) * H + q * 16;
+    v4d acc = {0.0, 0.0, 0.0, 0.0};
+    for (int k = 0; k < H; k += 64) {
+        uint4 xa = ld16(xr + k), xb = ld16(xr + k + 8);
+        uint4 wa = ld16(wr + k), wb = ld16(wr + k + 8);
+        if (!tv) xa = xb = make_uint4(0, 0, 0, 0);
+        if (!ev) wa = wb = make_uint4(0, 0, 0, 0);
+        const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        const uint32_t ws[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xs[i]),
+                                                       (double)bf16_lo(ws[i]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xs[i]),
+                                                       (double)bf16_hi(ws[i]), acc, 0, 0, 0);
+        }
+    }
+    // accumulator layout: lane (r, q) holds rows 4q..4q+3 of column r
+    if (!ev) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * q + i;
+        if (t < T) logits[(int64_t)t * E + e0 + r] = finish_logit(acc[i], bias, e0 + r, flags);
+    }
+}
+
+hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_w,
+                               const float *bias, int H, int E, uint32_t flags, float *logits,
+                               hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (T <= 16) {
+        hipLaunchKernelGGL(route_logits_vec, dim3((E + 3) / 4, T), dim3(256), 0, st, x,
+                           router_w, bias, H, E, flags, logits);
+    } else {
+        hipLaunchKernelGGL(route_logits_mfma, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0,
+                           st, x, T, router_w, bias, H, E, flags, logits);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ top-K
+
+// Order-preserving key: larger logit first, then the lower expert index.
+// +0 and -0 compare equal, as floats do.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+    uint32_t o = (uint32_t)(k >> 32);
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One wave per row: K rounds of a wave-wide max over keys, then the softmax
+// over the K selected logits in slot order.
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float *__restrict__ logits, int T, int E, int K, int32_t *__restrict__ ids,
+    float *__restrict__ wts, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ gate_w, int H, float *__restrict__ gamma) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const float *lr = logits + (int64_t)t * E;
+    uint64_t key[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = lane + WAVE * i;
+        key[i] = e < E ? topk_key(lr[e], e) : 0ull;  // valid keys are never 0
+    }
+    int my_id = 0;
+    float my_v = 0.0f, v0 = 0.0f;
+    for (int j = 0; j < K; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint64_t other = shfl_xor_u64(best, o);
+            best = other > best ? other : best;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (key[i] == best) key[i] = 0;
+        const float v = key_value(best);
+        if (j == 0) v0 = v;
+        if (lane == j) {
+            my_id = (int)(0xFFFFFFFFu - (uint32_t)best);
+            my_v = v;
+        }
+    }
+    const float ex = lane < K ? expf(my_v - v0) : 0.0f;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) sum += __shfl(ex, j);
+    if (lane < K) {
+        ids[(int64_t)t * K + lane] = my_id;
+        wts[(int64_t)t * K + lane] = ex / sum;
+    }
+    if (gate_w) {
+        const uint16_t *xr = x + (int64_t)t * H;
+        float z = 0.0f;
+        for (int c = lane; c < H / 8; c += WAVE) {
+            const uint4 a = ld16(xr + c * 8), b = ld16(gate_w + c * 8);
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z += bf16_lo(av[i]) * bf16_lo(bv[i]);
+                z += bf16_hi(av[i]) * bf16_hi(bv[i]);
+            }
+        }
+        z = wave_sum<64>(z);
+        if (lane == 0) gamma[t] = 1.0f / (1.0f + expf(-z));
+    }
+}
+
+hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids,
+                             float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
+                             float *gamma, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K,
+                       ids, weights, x, gate_w, H, gamma);
+    return hipGetLastError();
+}
+
+}  // namespace moe

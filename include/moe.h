@@ -1,0 +1,154 @@
+/*
+ * libmoe: a block-FP8 mixture-of-experts layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the backbone MoE of the "Drama 3" speech model described on
+ * the pages: 256 routed experts with top-8 routing, block-FP8 (e4m3, one fp32
+ * scale per 128x128 block) expert weights, and a gated shared expert (PR #925
+ * "drama: load the checkpoint with direct I/O in file order and build the
+ * codec on its own thread", commit summary of the Drama 3 backbone).
+ * Activations are bf16 and the FP8 experts quantise their input rows to e4m3
+ * per row and per 128 columns with scale amax / 448 (PR #939 "drama3: Fish
+ * Audio Drama 3 text to speech on one CUDA GPU", "How it fits the engine" >
+ * Precision).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named as device pointers are device memory owned by the caller,
+ *    16-byte aligned; the workspace is 256-byte aligned. Config structs are
+ *    host memory, read during the call only.
+ *  - Matrices are row-major and dense; weight matrices are [out, in].
+ *  - bf16 tensors are passed as void* (16-bit storage).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it; no call synchronises, copies to the host or
+ *    allocates memory.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    refused call returns a negative moe_status and enqueues nothing.
+ *    MOE_E_LAUNCH reports a failed kernel launch. Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give the same bytes on every
+ *    call. Calls keep no state between them and may run on several streams
+ *    at once when their workspaces and outputs are distinct.
+ *
+ * Supported shapes: hidden H and expert intermediate I are multiples of 128
+ * with 128 <= H <= 8192 and 128 <= I <= 4096; the shared intermediate Is is a
+ * multiple of 128 up to 4096, or 0 for no shared expert; 1 <= E <= 1024;
+ * 1 <= K <= min(E, 16); 0 <= T <= 65536 rows (T = 0 does nothing and
+ * returns MOE_OK).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_NULL = -1,        /* a required pointer is NULL */
+    MOE_E_SHAPE = -2,       /* a size is outside the supported shapes above */
+    MOE_E_ALIGN = -3,       /* a pointer is not aligned as required */
+    MOE_E_WORKSPACE = -4,   /* workspace smaller than moe_workspace_bytes() */
+    MOE_E_UNSUPPORTED = -5, /* the current device is not gfx950, or bad flags */
+    MOE_E_LAUNCH = -6       /* a kernel launch failed */
+} moe_status;
+
+/* moe_config.flags */
+#define MOE_LOGITS_FP32   (1u << 1) /* decide on fp32 router logits (no bf16 rounding) */
+#define MOE_FORCE_GEMV    (1u << 8) /* run the row-at-a-time decode path at any T */
+#define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
+
+typedef struct {
+    int32_t hidden;       /* H */
+    int32_t n_experts;    /* E */
+    int32_t top_k;        /* K */
+    int32_t inter;        /* I: routed expert intermediate */
+    int32_t shared_inter; /* Is: shared expert intermediate, 0 = none */
+    uint32_t flags;       /* MOE_* flags above */
+} moe_config;
+
+/* Layer weights, all device pointers, caller-owned, read-only.
+ * FP8 matrices hold OCP e4m3 codes; w ~= code * scale of its 128x128 block. */
+typedef struct {
+    const void *router_w;     /* bf16 [E, H] */
+    const float *router_bias; /* fp32 [E], added to the logits; or NULL */
+    const uint8_t *w_gate;    /* e4m3 [E][I, H] */
+    const float *s_gate;      /* fp32 [E][I/128, H/128] */
+    const uint8_t *w_up;      /* e4m3 [E][I, H] */
+    const float *s_up;        /* fp32 [E][I/128, H/128] */
+    const uint8_t *w_down;    /* e4m3 [E][H, I] */
+    const float *s_down;      /* fp32 [E][H/128, I/128] */
+    const void *sh_gate;      /* bf16 [Is, H]; unused when Is = 0 */
+    const void *sh_up;        /* bf16 [Is, H] */
+    const void *sh_down;      /* bf16 [H, Is] */
+    const void *sh_gate_w;    /* bf16 [H]: shared-expert gate vector */
+} moe_weights;
+
+/* 1 if `device` is a gfx950 GPU this library was built for; 0 otherwise and
+ * on any runtime failure (never an error). */
+int moe_supported(int device);
+
+/* Bytes of device workspace moe_forward and moe_route need for up to
+ * `max_rows` rows of this config; 0 if the config is refused. */
+size_t moe_workspace_bytes(const moe_config *cfg, int32_t max_rows);
+
+/*
+ * Router (PR #939, "What it adds": the router in the backbone fatbin;
+ * "Fidelity against the PyTorch oracle": decisions on bf16 logits; softmax in
+ * fp32 per "How it fits the engine" > Precision).
+ *   logit[t,e] = bf16(fp32(sum_h x[t,h] * router_w[e,h])) (+ router_bias[e]),
+ *                the sum taken exactly (fp64 accumulation of exact products)
+ *                and rounded once; MOE_LOGITS_FP32 skips the bf16 rounding;
+ *   ids[t,:]   = the K experts with the largest logits, in order of logit
+ *                descending, lower expert index first on equal logits;
+ *   weights[t,j] = exp(logit_j - logit_0) / sum_i exp(logit_i - logit_0)
+ *                over the K selected (softmax renormalised over the top K).
+ * x: bf16 [T, H]; ids: int32 [T, K]; weights: fp32 [T, K];
+ * logits: fp32 [T, E] (bf16 values held in fp32, bias included) or NULL, in
+ * which case `workspace` (>= moe_workspace_bytes(cfg, T)) holds them.
+ */
+moe_status moe_route(const moe_config *cfg, const void *x, int32_t T,
+                     const void *router_w, const float *router_bias,
+                     int32_t *ids, float *weights, float *logits,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dynamic 1x128 activation quantisation (PR #925, backbone commit summary;
+ * PR #939, "How it fits the engine" > Precision). For each row t and each
+ * group g of 128 columns:
+ *   s[t,g]   = fp32(max(amax, 1e-10) / 448), amax = max |x| over the group;
+ *   q[t,c]   = e4m3 code nearest fp32(x[t,c] / s[t,g]) after saturation to
+ *              +-448, ties to even; a negative value that rounds to 0 gives
+ *              0x80.
+ * x: bf16 [T, C] with C a multiple of 128 (128 <= C <= 65536);
+ * q: uint8 [T, C]; scales: fp32 [T, C/128].
+ */
+moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float *scales,
+                         void *stream);
+
+/*
+ * The whole layer, without the residual (PR #925 commit summaries: the
+ * router, the FP8 experts on FP8 rows with per-row scales, one SwiGLU launch
+ * writing routed rows as FP8 and shared rows as bf16, and the combine that
+ * keeps every sum in a fixed order). For each row t with routing (ids, w):
+ *   (qx, sx)  = the 1x128 quantisation of x[t] (as moe_quant_act);
+ *   g_j, u_j  = block-FP8 products of expert ids[t,j]'s gate and up matrices
+ *               with (qx, sx), fp32 accumulation;
+ *   h_j       = silu(g_j) * u_j, re-quantised 1x128 to e4m3;
+ *   e_j       = block-FP8 product of the expert's down matrix with h_j;
+ *   s         = Wsd . bf16(silu(Wsg x) * (Wsu x))   (bf16 shared expert);
+ *   gamma     = sigmoid(sh_gate_w . x);
+ *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
+ * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
+ * workspace: >= moe_workspace_bytes(cfg, T) bytes, contents need not be
+ * initialised and are overwritten.
+ */
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
+                       int32_t T, void *y, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

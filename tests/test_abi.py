@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and refuses bad arguments with its named codes before touching the
+device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_fp8_mixture_router_amd as moe
+from block_fp8_mixture_router_amd import inputs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|int|size_t)\s+(moe_\w+)\s*\(", src,
+                                 re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _cfg(**kw):
+    c = moe.config(inputs.DECODE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 100), ("hidden", 0), ("hidden", 16384), ("inter", 64), ("inter", 8192),
+    ("shared_inter", 100), ("shared_inter", -128), ("n_experts", 0), ("n_experts", 2048),
+    ("top_k", 0), ("top_k", 17), ("flags", 1 << 20),
+])
+def test_workspace_refuses_bad_config(field, value):
+    assert moe.workspace_bytes(_cfg(**{field: value}), 1) == 0
+
+
+def test_workspace_grows_with_rows():
+    c = _cfg()
+    a, b = moe.workspace_bytes(c, 1), moe.workspace_bytes(c, 1024)
+    assert 0 < a < b
+    assert b % 256 == 0
+    assert moe.workspace_bytes(c, -1) == 0 and moe.workspace_bytes(c, 65537) == 0
+
+
+def _fwd(cfg, w, x, T, y, ws, nbytes):
+    return moe.lib().moe_forward(ctypes.byref(cfg) if cfg is not None else None,
+                                 ctypes.byref(w) if w is not None else None, x, T, y, ws,
+                                 nbytes, None)
+
+
+def _fake_weights(base=0x10000000):
+    w = moe.Weights()
+    for i, (name, _) in enumerate(moe.Weights._fields_):
+        setattr(w, name, base + 0x100000 * (i + 1))
+    w.router_bias = None
+    return w
+
+
+def test_forward_refusals_before_any_device_call():
+    c = _cfg()
+    w = _fake_weights()
+    n = moe.workspace_bytes(c, 4)
+    X, Y, WS = 0x20000000, 0x30000000, 0x40000000
+    assert _fwd(None, w, X, 4, Y, WS, n) == -1
+    assert _fwd(c, None, X, 4, Y, WS, n) == -1
+    assert _fwd(c, w, None, 4, Y, WS, n) == -1
+    assert _fwd(c, w, X, 4, Y, None, n) == -1
+    assert _fwd(c, w, X, -1, Y, WS, n) == -2
+    assert _fwd(c, w, X, 70000, Y, WS, n) == -2
+    assert _fwd(c, w, X, 0, Y, WS, n) == 0          # T = 0 is a no-op
+    assert _fwd(c, w, X + 2, 4, Y, WS, n) == -3      # misaligned x
+    assert _fwd(c, w, X, 4, Y, WS + 16, n) == -3     # workspace not 256-aligned
+    assert _fwd(c, w, X, 4, Y, WS, n - 1) == -4
+    bad = _cfg(flags=moe.FORCE_GEMV | moe.FORCE_GROUPED)
+    assert _fwd(bad, w, X, 4, Y, WS, n) == -5
+    w2 = _fake_weights()
+    w2.w_down = None
+    assert _fwd(c, w2, X, 4, Y, WS, n) == -1
+    # all arguments valid: without a gfx950 device the call is refused, not run
+    assert _fwd(c, w, X, 4, Y, WS, n) == -5
+
+
+def test_quant_and_route_refusals():
+    L = moe.lib()
+    X, Q, S = 0x20000000, 0x30000000, 0x40000000
+    assert L.moe_quant_act(X, 4, 100, Q, S, None) == -2
+    assert L.moe_quant_act(X, 4, 0, Q, S, None) == -2
+    assert L.moe_quant_act(X, -1, 128, Q, S, None) == -2
+    assert L.moe_quant_act(X, 0, 128, Q, S, None) == 0
+    assert L.moe_quant_act(None, 4, 128, Q, S, None) == -1
+    assert L.moe_quant_act(X + 8, 4, 128, Q, S, None) == -3
+    assert L.moe_quant_act(X, 4, 128, Q, S, None) == -5
+    c = _cfg()
+    cb = ctypes.byref(c)
+    assert L.moe_route(cb, X, 4, Q, None, S, S + 4096, None, None, 0, None) == -1
+    assert L.moe_route(cb, X, 4, Q, None, S, S + 4096, S + 8192, None, 0, None) == -5
+    WS = 0x50000000
+    assert L.moe_route(cb, X, 4, Q, None, S, S + 4096, None, WS, 16, None) == -4
+
+
+def test_supported_is_false_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert moe.supported(0) is False
+    assert moe.supported(-1) is False

@@ -1,0 +1,159 @@
+"""GPU parity of moe_forward against the oracle, on both paths, plus the
+layer's invariants on the GPU (determinism, poisoned scratch, row order,
+identical experts, closed shared gate)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_router_amd as moe
+import oracle
+from block_fp8_mixture_router_amd import inputs
+from tests import exact
+from tests.gpu_common import OUT_TOL, bits, layer, need_gpu, rel_rows, run_forward, say, x_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _check(shape, host, x_host, y_dev, rows=None, tol=OUT_TOL, flags=0, shared=True):
+    xs = x_host if rows is None else x_host[rows]
+    yb = bits(y_dev.cpu())
+    if rows is not None:
+        yb = yb[rows]
+    _, acc, _, _ = oracle.forward(shape, host, xs, flags=flags, shared=shared)
+    rel, worst = rel_rows(yb, acc)
+    say(f"  relL2 {rel:.2e}  worst row {worst:.2e}")
+    assert np.all(np.isfinite(exact.bits_to_f32(yb)))
+    assert rel <= tol, (rel, worst)
+    return rel, worst
+
+
+CASES = [
+    # (shape, T, flags, skewed)
+    ("TINY", 1, 0, False),
+    ("TINY", 3, 0, False),
+    ("TINY", 5, 0, False),
+    ("TINY", 70, 0, False),
+    ("TINY", 1, moe.FORCE_GROUPED, False),
+    ("TINY", 9, moe.FORCE_GEMV, False),
+    ("DECODE", 1, 0, False),
+    ("DECODE", 2, 0, False),
+    ("DECODE", 4, 0, False),
+    ("DECODE", 1, moe.FORCE_GROUPED, False),
+    ("DECODE", 7, moe.FORCE_GEMV, False),
+    ("DECODE", 37, 0, False),
+]
+
+
+@pytest.mark.parametrize("shape_name,T,flags,skewed", CASES)
+def test_forward_matches_oracle(shape_name, T, flags, skewed):
+    say(f"forward {shape_name} T={T} flags={flags} skewed={skewed}")
+    shape, dev, host = layer(shape_name, 0, skewed)
+    x, xh = x_rows(shape, T, seed=100 + T)
+    y = run_forward(shape, dev, x, flags)
+    _check(shape, host, xh, y)
+
+
+@pytest.mark.parametrize("skewed", [False, True])
+@pytest.mark.parametrize("T", [1023, 1024])
+def test_forward_chunk_sampled_rows(T, skewed):
+    """Full chunk sizes in the launch configuration the bench times; the
+    oracle checks a sample of rows (rows are independent)."""
+    say(f"forward chunk T={T} skewed={skewed}")
+    shape, dev, host = layer("DECODE", 0, skewed)
+    x, xh = x_rows(shape, T, seed=T + skewed)
+    y = run_forward(shape, dev, x)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                     np.random.default_rng(T).choice(T, 48, replace=False)]))
+    _check(shape, host, xh, y, rows=rows)
+
+
+def test_forward_deterministic_and_poison_proof():
+    shape, dev, host = layer("DECODE", 0, False)
+    for T, flags in ((1, 0), (300, 0), (3, moe.FORCE_GROUPED)):
+        say(f"determinism T={T} flags={flags}")
+        x, _ = x_rows(shape, T, seed=5)
+        y1 = run_forward(shape, dev, x, flags)
+        y2 = run_forward(shape, dev, x, flags, poison=True)
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_grouped_rows_independent_of_order():
+    shape, dev, host = layer("DECODE", 0, False)
+    x, _ = x_rows(shape, 200, seed=6)
+    y = run_forward(shape, dev, x)
+    p = torch.randperm(200, generator=torch.Generator().manual_seed(0)).cuda()
+    yp = run_forward(shape, dev, x[p].contiguous())
+    assert torch.equal(y[p].view(torch.int16), yp.view(torch.int16))
+    # a row alone through the grouped path gives the same bytes as in the chunk
+    y1 = run_forward(shape, dev, x[17:18].contiguous(), moe.FORCE_GROUPED)
+    assert torch.equal(y[17:18].view(torch.int16), y1.view(torch.int16))
+
+
+def test_all_rows_on_the_same_experts():
+    """A bias that sends every row to experts 0..7: 16 full tiles per expert."""
+    shape, dev, host = layer("DECODE", 0, False)
+    bias = torch.zeros(shape.n_experts)
+    bias[:8] = 64.0
+    dev_b = dataclasses.replace(dev, router_bias=bias.cuda())
+    host_b = dataclasses.replace(host, router_bias=bias)
+    x, xh = x_rows(shape, 1024, seed=7)
+    y = run_forward(shape, dev_b, x)
+    rows = np.arange(0, 1024, 16)
+    _check(shape, host_b, xh, y, rows=rows)
+
+
+def test_single_expert_layer():
+    shape = dataclasses.replace(inputs.TINY, n_experts=1, top_k=1)
+    dev = inputs.make_layer(shape, seed=3, device="cuda")
+    host = dev.to("cpu")
+    for T in (1, 40):
+        x, xh = x_rows(shape, T, seed=3)
+        y = run_forward(shape, dev, x)
+        _check(shape, host, xh, y)
+
+
+def test_identical_experts_on_gpu():
+    shape, _, _ = layer("TINY", 0, False)
+    dev = inputs.make_layer(shape, seed=4, device="cuda")
+    for name in ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down"):
+        t = getattr(dev, name)
+        t[:] = t[5:6].clone()
+    host = dev.to("cpu")
+    one = dataclasses.replace(shape, n_experts=1, top_k=1)
+    dev1 = dataclasses.replace(dev, shape=one, router_w=dev.router_w[5:6].contiguous())
+    for name in ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down"):
+        setattr(dev1, name, getattr(dev, name)[5:6].contiguous())
+    for T in (2, 50):
+        x, xh = x_rows(shape, T, seed=4)
+        y = run_forward(shape, dev, x)
+        y1 = run_forward(one, dev1, x)
+        d = exact.rel_l2(y.float().cpu().numpy(), y1.float().cpu().numpy())
+        say(f"  identical experts T={T}: relL2 vs single expert {d:.2e}")
+        assert d <= 1e-2
+        _check(shape, host, xh, y)
+
+
+def test_closed_shared_gate_removes_shared_branch():
+    shape, dev, host = layer("TINY", 0, False)
+    x, xh = x_rows(shape, 1, seed=9)
+    gw = (-0.125 * torch.sign(x[0].float())).to(torch.bfloat16)
+    dev_g = dataclasses.replace(dev, sh_gate_w=gw)
+    for flags in (0, moe.FORCE_GROUPED):
+        y = run_forward(shape, dev_g, x, flags)
+        y0 = run_forward(shape, dev, x, flags, shared=False)
+        assert torch.equal(y.float(), y0.float())
+
+
+def test_no_shared_expert_matches_oracle():
+    shape, dev, host = layer("DECODE", 0, False)
+    for T in (1, 64):
+        x, xh = x_rows(shape, T, seed=10)
+        y = run_forward(shape, dev, x, shared=False)
+        _check(shape, host, xh, y, shared=False)
