@@ -139,8 +139,10 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
     if (T == 0) return MOE_OK;
     if (!x || !router_w || !ids || !weights) return MOE_E_NULL;
     if (!logits && !workspace) return MOE_E_NULL;
-    if (!al16(x) || !al16(router_w) || !al16(ids) || !al16(weights) ||
-        (logits && !al16(logits)) || (router_bias && !al16(router_bias)))
+    if (!al16(x) || !al16(router_w) || (reinterpret_cast<uintptr_t>(ids) & 3u) ||
+        (reinterpret_cast<uintptr_t>(weights) & 3u) ||
+        (logits && (reinterpret_cast<uintptr_t>(logits) & 3u)) ||
+        (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u)))
         return MOE_E_ALIGN;
     if (!logits) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
@@ -169,11 +171,12 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
         return MOE_E_NULL;
     const bool shared = cfg->shared_inter > 0;
     if (shared && (!w->sh_gate || !w->sh_up || !w->sh_down || !w->sh_gate_w)) return MOE_E_NULL;
-    const void *ptrs[] = {x, y, w->router_w, w->w_gate, w->s_gate, w->w_up, w->s_up,
-                          w->w_down, w->s_down};
+    const void *ptrs[] = {x, y, w->router_w, w->w_gate, w->w_up, w->w_down};
     for (const void *p : ptrs)
         if (!al16(p)) return MOE_E_ALIGN;
-    if (w->router_bias && !al16(w->router_bias)) return MOE_E_ALIGN;
+    const void *scalars[] = {w->s_gate, w->s_up, w->s_down, w->router_bias};
+    for (const void *p : scalars)
+        if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
     if (shared && (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down) ||
                    !al16(w->sh_gate_w)))
         return MOE_E_ALIGN;

@@ -82,11 +82,11 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restr
                                                        (double)bf16_hi(ws[i]), acc, 0, 0, 0);
         }
     }
-    // accumulator layout: lane (r, q) holds rows 4q..4q+3 of column r
+    // fp64 accumulator layout: element i of lane (r, q) is row q + 4i of column r
     if (!ev) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * q + i;
+        const int t = t0 + q + 4 * i;
         if (t < T) logits[(int64_t)t * E + e0 + r] = finish_logit(acc[i], bias, e0 + r, flags);
     }
 }

@@ -12,9 +12,11 @@
  * Precision).
  *
  * Conventions shared by every call:
- *  - Pointers named as device pointers are device memory owned by the caller,
- *    16-byte aligned; the workspace is 256-byte aligned. Config structs are
- *    host memory, read during the call only.
+ *  - Pointers named as device pointers are device memory owned by the caller.
+ *    bf16 and e4m3 tensors are 16-byte aligned; fp32 scale, bias, weight and
+ *    logit arrays and int32 id arrays are 4-byte aligned; the workspace is
+ *    256-byte aligned. Config structs are host memory, read during the call
+ *    only.
  *  - Matrices are row-major and dense; weight matrices are [out, in].
  *  - bf16 tensors are passed as void* (16-bit storage).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
