@@ -32,6 +32,22 @@ int device_is_gfx950(int dev) {
     return s == 1;
 }
 
+std::atomic<int> g_dev_cus[MAX_DEVICES];
+
+// compute units of the current device (the decode kernel's grid)
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 0;
+    int n = g_dev_cus[dev].load(std::memory_order_acquire);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        if (n > 1024) n = 1024;
+        g_dev_cus[dev].store(n, std::memory_order_release);
+    }
+    return n;
+}
+
 bool current_device_ok() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return false;
@@ -58,7 +74,8 @@ constexpr int MAX_ROWS = 65536;
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t logits, ids, wts, gamma, h, hs, qx, sx, offsets, perm, tiles, n_tiles, qh, sh, stage;
+    size_t sync, logits, ids, wts, gamma, h, hs, qx, sx, offsets, perm, tiles, n_tiles, qh, sh,
+        stage;
     size_t total;
     int max_tiles;
 };
@@ -74,11 +91,12 @@ Layout layout_of(const moe_config *c, int T) {
     const size_t t = (size_t)T, E = c->n_experts, K = c->top_k, H = c->hidden, I = c->inter,
                  Is = c->shared_inter;
     L.max_tiles = grouped_max_tiles(T, (int)K, (int)E);
+    L.sync = take((size_t)SYNC_WORDS * 4);
     L.logits = take(t * E * 4);
     L.ids = take(t * K * 4);
     L.wts = take(t * K * 4);
     L.gamma = take(t * 4);
-    L.h = take(t * K * I * 4);
+    L.h = take((t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS) * K * I * 4);
     L.hs = take(t * Is * 2);
     L.qx = take(t * H);
     L.sx = take(t * (H / 128) * 4);
@@ -193,30 +211,39 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     int32_t *ids = at<int32_t>(workspace, L.ids);
     float *wts = at<float>(workspace, L.wts);
     float *gamma = at<float>(workspace, L.gamma);
-    MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(w->router_w),
-                                w->router_bias, H, E, cfg->flags, lg, st));
-    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
-                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
-                              gamma, st));
-
+    const bool fits = decode_fits(T, H, K, cfg->inter);
+    if ((cfg->flags & MOE_FORCE_GEMV) && !fits) return MOE_E_UNSUPPORTED;
     const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
-                      (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4);
+                      (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4 && fits);
     if (gemv) {
-        DecodeArgs a{};
+        FusedArgs a{};
         a.T = T; a.H = H; a.E = E; a.K = K; a.I = cfg->inter; a.Is = cfg->shared_inter;
-        a.x = xb; a.ids = ids; a.wts = wts; a.gamma = gamma;
+        a.flags = cfg->flags;
+        a.x = xb;
+        a.router_w = static_cast<const uint16_t *>(w->router_w);
+        a.bias = w->router_bias;
         a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
         a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
         a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
         a.sh_up = static_cast<const uint16_t *>(w->sh_up);
         a.sh_down = static_cast<const uint16_t *>(w->sh_down);
-        a.h = at<float>(workspace, L.h);
+        a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
+        a.logits = lg;
+        a.gamma = gamma;
         a.hs = at<uint16_t>(workspace, L.hs);
+        a.h = at<float>(workspace, L.h);
+        a.sync = at<uint32_t>(workspace, L.sync);
         a.y = static_cast<uint16_t *>(y);
-        MOE_TRY(launch_decode_gateup(a, st));
-        MOE_TRY(launch_decode_down(a, st));
+        a.nwg = device_cus();
+        if (a.nwg <= 0) return MOE_E_UNSUPPORTED;
+        MOE_TRY(launch_decode_fused(a, st));
         return MOE_OK;
     }
+    MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(w->router_w),
+                                w->router_bias, H, E, cfg->flags, lg, st));
+    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
+                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
+                              gamma, st));
     GroupedArgs g{};
     g.T = T; g.H = H; g.E = E; g.K = K; g.I = cfg->inter; g.Is = cfg->shared_inter;
     g.x = xb;

@@ -63,6 +63,93 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float &a, float &b, fl
 __device__ __forceinline__ float group_scale(float amax) { return fmaxf(amax, 1e-10f) / 448.0f; }
 
 // ------------------------------------------------------- wave reductions
+// DPP lane moves inside rows of 16 lanes, then v_readlane across the four
+// rows: no LDS round trips on the dependency chain. Every lane of the wave
+// must be active.
+
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm(1,0,3,2)
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm(2,3,0,1)
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = dpp_i<CTRL>((int)(uint32_t)u), hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// all-lanes sum / max / min over the 64-lane wave (fixed order: deterministic)
+__device__ __forceinline__ float wave_allsum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    v += dpp_f<DPP_MIRROR>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ double wave_allsum_d(double v) {
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HALF_MIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+                 fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_allmin_i(int v) {
+    v = min(v, dpp_i<DPP_XOR1>(v));
+    v = min(v, dpp_i<DPP_XOR2>(v));
+    v = min(v, dpp_i<DPP_HALF_MIRROR>(v));
+    v = min(v, dpp_i<DPP_MIRROR>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// max over aligned groups of 8 lanes (result in every lane of the group)
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    return fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+}
+// max / sum over aligned groups of 16 lanes
+__device__ __forceinline__ float group16_max(float v) {
+    v = group8_max(v);
+    return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float group16_sum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    return v + dpp_f<DPP_MIRROR>(v);
+}
+// sum over aligned groups of 32 lanes
+__device__ __forceinline__ float group32_sum(float v) {
+    v = group16_sum(v);
+    return v + __shfl_xor(v, 16);
+}
+
 
 template <int WIDTH>
 __device__ __forceinline__ float wave_max(float v) {

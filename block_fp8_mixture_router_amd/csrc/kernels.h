@@ -23,22 +23,27 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *
                              float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
                              float *gamma, hipStream_t st);
 
-// ---- decode.hip (row-at-a-time path)
-struct DecodeArgs {
+// ---- decode.hip (row-at-a-time path: one persistent kernel per call)
+struct FusedArgs {
     int T, H, E, K, I, Is;
-    const uint16_t *x;
-    const int32_t *ids;
-    const float *wts;
-    const float *gamma;
+    uint32_t flags;
+    const uint16_t *x, *router_w;
+    const float *bias;
     const uint8_t *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
-    const uint16_t *sh_gate, *sh_up, *sh_down;
-    float *h;         // [T, K, I] fp32 SwiGLU output of the routed experts
-    uint16_t *hs;     // [T, Is] bf16 SwiGLU output of the shared expert
-    uint16_t *y;      // [T, H] bf16
+    const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
+    float *logits;    // [T, E]
+    float *gamma;     // [T]
+    uint16_t *hs;     // [T, Is] bf16 shared-expert SwiGLU output
+    float *h;         // [T*K, I] routed SwiGLU output (fp32)
+    uint32_t *sync;   // [0] generation, [32] error, [64 + b*nwg + w] handoff flags
+    uint16_t *y;      // [T, H]
+    int nwg;          // workgroups = compute units (all co-resident)
 };
-hipError_t launch_decode_gateup(const DecodeArgs &a, hipStream_t st);
-hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t st);
+constexpr int DECODE_MAX_ROWS = 16;
+constexpr int SYNC_WORDS = 64 + 2 * 1024;
+bool decode_fits(int T, int H, int K, int I);
+hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
 
 // ---- grouped.hip (expert-grouped MFMA path)
 struct GroupedArgs {

@@ -15,6 +15,7 @@
 //    expert per 64 columns and the MFMA sums over the lanes' column slices.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void route_logits_vec(const uint16_t *__restri
             acc = fma((double)bf16_hi(av[i]), (double)bf16_hi(bv[i]), acc);
         }
     }
-    acc = wave_sum_f64<64>(acc);
+    acc = wave_allsum_d(acc);
     if (lane == 0) logits[(int64_t)t * E + e] = finish_logit(acc, bias, e, flags);
 }
 
@@ -107,69 +108,16 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
 
 // ------------------------------------------------------------------ top-K
 
-// Order-preserving key: larger logit first, then the lower expert index.
-// +0 and -0 compare equal, as floats do.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
-    uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(uint64_t k) {
-    uint32_t o = (uint32_t)(k >> 32);
-    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// One wave per row: K rounds of a wave-wide max over keys, then the softmax
-// over the K selected logits in slot order.
+// One wave per row: the shared top-K routine, then (forward only) the
+// shared-expert gate gamma[t] = sigmoid(gate_w . x[t]).
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float *__restrict__ logits, int T, int E, int K, int32_t *__restrict__ ids,
     float *__restrict__ wts, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ gate_w, int H, float *__restrict__ gamma) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (t >= T) return;
-    const float *lr = logits + (int64_t)t * E;
-    uint64_t key[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + WAVE * i;
-        key[i] = e < E ? topk_key(lr[e], e) : 0ull;  // valid keys are never 0
-    }
-    int my_id = 0;
-    float my_v = 0.0f, v0 = 0.0f;
-    for (int j = 0; j < K; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint64_t other = shfl_xor_u64(best, o);
-            best = other > best ? other : best;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (key[i] == best) key[i] = 0;
-        const float v = key_value(best);
-        if (j == 0) v0 = v;
-        if (lane == j) {
-            my_id = (int)(0xFFFFFFFFu - (uint32_t)best);
-            my_v = v;
-        }
-    }
-    const float ex = lane < K ? expf(my_v - v0) : 0.0f;
-    float sum = 0.0f;
-    for (int j = 0; j < K; ++j) sum += __shfl(ex, j);
-    if (lane < K) {
-        ids[(int64_t)t * K + lane] = my_id;
-        wts[(int64_t)t * K + lane] = ex / sum;
-    }
+    if (t >= T) return;  // whole waves leave together
+    topk_row(logits + (int64_t)t * E, E, K, lane, ids + (int64_t)t * K, wts + (int64_t)t * K);
     if (gate_w) {
         const uint16_t *xr = x + (int64_t)t * H;
         float z = 0.0f;
@@ -178,11 +126,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
             const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                z += bf16_lo(av[i]) * bf16_lo(bv[i]);
-                z += bf16_hi(av[i]) * bf16_hi(bv[i]);
+                z = fmaf(bf16_lo(av[i]), bf16_lo(bv[i]), z);
+                z = fmaf(bf16_hi(av[i]), bf16_hi(bv[i]), z);
             }
         }
-        z = wave_sum<64>(z);
+        z = wave_allsum(z);
         if (lane == 0) gamma[t] = 1.0f / (1.0f + expf(-z));
     }
 }

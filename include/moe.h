@@ -58,7 +58,8 @@ typedef enum {
 
 /* moe_config.flags */
 #define MOE_LOGITS_FP32   (1u << 1) /* decide on fp32 router logits (no bf16 rounding) */
-#define MOE_FORCE_GEMV    (1u << 8) /* run the row-at-a-time decode path at any T */
+#define MOE_FORCE_GEMV    (1u << 8) /* run the row-at-a-time decode path (T <= 16; refused
+                                       with MOE_E_UNSUPPORTED where its LDS plan does not fit) */
 #define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
 
 typedef struct {
@@ -143,8 +144,10 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
  *   gamma     = sigmoid(sh_gate_w . x);
  *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
  * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
- * workspace: >= moe_workspace_bytes(cfg, T) bytes, contents need not be
- * initialised and are overwritten.
+ * workspace: >= moe_workspace_bytes(cfg, T) bytes; its contents need not be
+ * initialised. The decode path (T <= 4 by default) keeps a generation word
+ * and handoff flags in it between calls, so two calls that overlap in time
+ * must not share a workspace; calls ordered on one stream may.
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,
