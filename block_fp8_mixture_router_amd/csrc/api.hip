@@ -92,12 +92,17 @@ Layout layout_of(const moe_config *c, int T) {
                  Is = c->shared_inter;
     L.max_tiles = grouped_max_tiles(T, (int)K, (int)E);
     L.sync = take((size_t)SYNC_WORDS * 4);
-    L.logits = take(t * E * 4);
+    // decode keeps DECODE_REPLICAS copies of logits, gamma, hs and h; the
+    // grouped path uses copy 0. Every size is non-decreasing in T, so a
+    // workspace sized for max_rows serves every T <= max_rows.
+    const size_t R = DECODE_REPLICAS, td = t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS;
+    const size_t tr = t > R * td ? t : R * td;
+    L.logits = take(tr * E * 4);
     L.ids = take(t * K * 4);
     L.wts = take(t * K * 4);
-    L.gamma = take(t * 4);
-    L.h = take((t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS) * K * I * 4);
-    L.hs = take(t * Is * 2);
+    L.gamma = take(tr * 4);
+    L.h = take(R * td * K * I * 4);
+    L.hs = take(tr * Is * 2);
     L.qx = take(t * H);
     L.sx = take(t * (H / 128) * 4);
     L.offsets = take((E + 1) * 4);
@@ -173,7 +178,8 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
     MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(router_w), router_bias,
                                 cfg->hidden, cfg->n_experts, cfg->flags, lg, st));
     MOE_TRY(launch_route_topk(lg, T, cfg->n_experts, cfg->top_k, ids, weights, nullptr, nullptr,
-                              cfg->hidden, nullptr, st));
+                              cfg->hidden, nullptr,
+                              !router_bias && !(cfg->flags & MOE_LOGITS_FP32), st));
     return MOE_OK;
 }
 
@@ -243,7 +249,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                                 w->router_bias, H, E, cfg->flags, lg, st));
     MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
                               shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
-                              gamma, st));
+                              gamma, !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32), st));
     GroupedArgs g{};
     g.T = T; g.H = H; g.E = E; g.K = K; g.I = cfg->inter; g.Is = cfg->shared_inter;
     g.x = xb;

@@ -10,11 +10,14 @@
 // three dependent steps, so it runs as ONE launch of one workgroup per
 // compute unit, with two grid-wide handoffs instead of kernel boundaries:
 //
-//  A. router logits (exact fp64 sums), shared-expert gate/up rows and the
-//     shared gate; every workgroup also quantises x (1x128) into LDS;
+//  A. router logits (exact fp64 sums), shared-expert gate/up rows
+//     (hs = bf16(silu(gs) * us)) and the shared gate; every load that does not
+//     depend on the routing, the phase-C shared down rows included, is issued
+//     here; every workgroup also quantises x (1x128) into LDS;
 //     -- handoff 1: logits, hs and gamma visible --
-//  B. every workgroup selects the top-K itself (wave argmax, DPP lane moves)
-//     and streams its share of the routed gate/up rows: h = silu(g) * u;
+//  B. every workgroup selects the top-K itself (wave argmax, DPP lane moves),
+//     issues the loads of its phase-C routed down rows, and streams its share
+//     of the routed gate/up rows: h = silu(g) * u;
 //     -- handoff 2: h visible --
 //  C. every workgroup re-quantises h (1x128) into LDS and owns whole output
 //     rows m: all K down rows plus the shared down row, then writes
@@ -24,13 +27,21 @@
 // different compute units. Each lane streams 16 contiguous weight bytes per
 // load; a wave covers 1 KiB of a weight row per load.
 //
-// Handoffs: each workgroup publishes a per-call flag value (generation + 1)
-// in its own slot and waits until all slots carry it. The generation word
-// lives in the workspace and advances by 2 per call, so neither an
-// uninitialised workspace nor flags left by an earlier call (or an earlier
-// replay of a captured graph) can satisfy a wait. The wait is bounded: if it
-// ever spins out (workgroups not co-resident) an error word is set and the
-// kernel still finishes.
+// Handoffs: every value that crosses workgroups (logits, hs, gamma, h, the
+// flags) is written and read with device-coherent (sc1) loads and stores,
+// which bypass the per-XCD L2 for that access only; a device-scope fence
+// would instead write back or invalidate a whole L2, and a thousand of them
+// per handoff cost tens of microseconds. A producer drains its own stores
+// (s_waitcnt) before its workgroup's arrival flag is stored. Every such value
+// is stored in DECODE_REPLICAS copies and each workgroup reads copy
+// blockIdx % DECODE_REPLICAS, so no cache line is read by more than 1/8 of
+// the workgroups (one copy per XCD when workgroups are dealt round-robin).
+// Flag values are the call's generation + 1; the
+// generation word lives in the workspace and advances by 2 per call, so
+// neither an uninitialised workspace nor flags left by an earlier call (or an
+// earlier replay of a captured graph) can satisfy a wait. Waits are bounded:
+// a spin-out (workgroups not co-resident) sets an error word and the kernel
+// still finishes.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -38,8 +49,7 @@
 namespace moe {
 
 constexpr int GU_ROWS = 4;       // routed gate/up rows per wave item
-constexpr int SH_ROWS = 2;       // shared gate/up rows per wave item
-constexpr int MAX_K = 16;
+constexpr int REPL = DECODE_REPLICAS;  // copies of every cross-workgroup value
 constexpr uint32_t SPIN_LIMIT = 1u << 17;  // ~0.2 s of polling, then give up
 
 // Dot product of 16 decoded e4m3 activation values with 16 e4m3 weights.
@@ -67,135 +77,177 @@ __device__ __forceinline__ void decode16(uint4 q, float (&f)[16]) {
 
 // ------------------------------------------------------------ handoffs
 
-__device__ __forceinline__ uint32_t ld_acquire_relaxed(const uint32_t *p) {
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
+// sync words: [0] generation, [32] error, [SYNC_FLAGS + (b * REPL + r) * nwg + w]
+// replica r of workgroup w's arrival flag at handoff b. Each workgroup writes
+// its flag into every replica and polls replica blockIdx % REPL.
 __device__ __forceinline__ void handoff(const FusedArgs &a, int b, uint32_t target) {
-    // every wave releases its own stores at device scope before the flag
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-coherent stores are done
     __syncthreads();
-    uint32_t *flags = a.sync + 64 + b * a.nwg;
-    if (threadIdx.x == 0)
-        __hip_atomic_store(flags + blockIdx.x, target, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t *flags = a.sync + SYNC_FLAGS + b * REPL * a.nwg;
+    if (threadIdx.x < REPL) st_dev(flags + threadIdx.x * a.nwg + blockIdx.x, target);
     if (threadIdx.x < WAVE) {
+        const uint32_t *mine = flags + (blockIdx.x % REPL) * a.nwg;
         for (uint32_t spin = 0;; ++spin) {
             bool ok = true;
-            for (int i = threadIdx.x; i < a.nwg; i += WAVE) ok &= ld_acquire_relaxed(flags + i) == target;
+            for (int i = threadIdx.x; i < a.nwg; i += WAVE) ok &= ld_dev(mine + i) == target;
             if (__all(ok)) break;
             if (spin >= SPIN_LIMIT) {
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(a.sync + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) st_dev(a.sync + 32, 1u);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
     }
     __syncthreads();
-    // every wave acquires the other workgroups' results
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // ------------------------------------------------------------- phase A
 
+// NB = 16-byte chunks of a bf16 H-row per lane (H / 512, rounded up). All of
+// an item's loads are issued before any arithmetic.
+
 // logit of (row t, expert e): exact fp64 sum of bf16 products, one rounding
+template <int NB>
 __device__ void router_item(const FusedArgs &a, int t, int e, int lane) {
     const uint16_t *xr = a.x + (int64_t)t * a.H;
     const uint16_t *wr = a.router_w + (int64_t)e * a.H;
-    double acc = 0.0;
-    for (int c = lane; c < a.H / 8; c += WAVE) {
-        const uint4 xv = ld16(xr + c * 8), wv = ld16(wr + c * 8);
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+    const int nc8 = a.H / 8;
+    uint4 xv[NB], wv[NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fma((double)bf16_lo(xs[i]), (double)bf16_lo(ws[i]), acc);
-            acc = fma((double)bf16_hi(xs[i]), (double)bf16_hi(ws[i]), acc);
+    for (int i = 0; i < NB; ++i) {
+        const int c = lane + WAVE * i;
+        xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        wv[i] = c < nc8 ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    double acc0 = 0.0, acc1 = 0.0;  // two independent chains
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const uint32_t xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
+            acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
         }
     }
-    acc = wave_allsum_d(acc);
-    if (lane == 0) {
+    const double acc = wave_allsum_d(acc0 + acc1);
+    if (lane < REPL) {
         float l = (float)acc;
         if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
         if (a.bias) l = l + a.bias[e];
-        a.logits[(int64_t)t * a.E + e] = l;
+        st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e, l);
     }
 }
 
-// shared-expert rows n0..n0+SH_ROWS-1 of row t: hs = bf16(silu(g) * u)
-__device__ void shared_item(const FusedArgs &a, int t, int n0, int lane) {
+__device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
+    const uint32_t as[4] = {a.x, a.y, a.z, a.w}, bs[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc = fmaf(bf16_lo(as[k]), bf16_lo(bs[k]), acc);
+        acc = fmaf(bf16_hi(as[k]), bf16_hi(bs[k]), acc);
+    }
+    return acc;
+}
+
+// one shared-expert row n of row t: hs = bf16(silu(g) * u); loads first
+template <int NB>
+struct SharedRegs {
+    uint4 x[NB], g[NB], u[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void shared_load(const FusedArgs &a, int t, int n, int lane,
+                                            SharedRegs<NB> &r) {
     const uint16_t *xr = a.x + (int64_t)t * a.H;
-    float g[SH_ROWS] = {}, u[SH_ROWS] = {};
-    for (int c = lane; c < a.H / 8; c += WAVE) {
-        const uint4 xv = ld16(xr + c * 8);
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        uint4 gv[SH_ROWS], uv[SH_ROWS];
+    const int nc8 = a.H / 8;
 #pragma unroll
-        for (int r = 0; r < SH_ROWS; ++r) {
-            gv[r] = ld16(a.sh_gate + (int64_t)(n0 + r) * a.H + c * 8);
-            uv[r] = ld16(a.sh_up + (int64_t)(n0 + r) * a.H + c * 8);
-        }
-#pragma unroll
-        for (int r = 0; r < SH_ROWS; ++r) {
-            const uint32_t gs[4] = {gv[r].x, gv[r].y, gv[r].z, gv[r].w};
-            const uint32_t us[4] = {uv[r].x, uv[r].y, uv[r].z, uv[r].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                g[r] = fmaf(bf16_lo(xs[i]), bf16_lo(gs[i]), g[r]);
-                g[r] = fmaf(bf16_hi(xs[i]), bf16_hi(gs[i]), g[r]);
-                u[r] = fmaf(bf16_lo(xs[i]), bf16_lo(us[i]), u[r]);
-                u[r] = fmaf(bf16_hi(xs[i]), bf16_hi(us[i]), u[r]);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < SH_ROWS; ++r) {
-        const float gs = wave_allsum(g[r]), us = wave_allsum(u[r]);
-        if (lane == r) a.hs[(int64_t)t * a.Is + n0 + r] = (uint16_t)f32_to_bf16(silu(gs) * us);
+    for (int i = 0; i < NB; ++i) {
+        const int c = lane + WAVE * i;
+        const bool ok = c < nc8;
+        r.x[i] = ok ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        r.g[i] = ok ? ld16(a.sh_gate + (int64_t)n * a.H + c * 8) : make_uint4(0, 0, 0, 0);
+        r.u[i] = ok ? ld16(a.sh_up + (int64_t)n * a.H + c * 8) : make_uint4(0, 0, 0, 0);
     }
 }
 
+template <int NB>
+__device__ __forceinline__ void shared_compute(const FusedArgs &a, int t, int n, int lane,
+                                               const SharedRegs<NB> &r) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        g = dot8_bf16_regs(r.x[i], r.g[i], g);
+        u = dot8_bf16_regs(r.x[i], r.u[i], u);
+    }
+    g = wave_allsum(g);
+    u = wave_allsum(u);
+    if (lane < REPL)
+        st_dev(a.hs + (int64_t)(lane * a.T + t) * a.Is + n, (uint16_t)f32_to_bf16(silu(g) * u));
+}
+
+template <int NB>
 __device__ void gamma_item(const FusedArgs &a, int t, int lane) {
     const uint16_t *xr = a.x + (int64_t)t * a.H;
-    float z = 0.0f;
-    for (int c = lane; c < a.H / 8; c += WAVE) {
-        const uint4 xv = ld16(xr + c * 8), wv = ld16(a.sh_gate_w + c * 8);
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+    const int nc8 = a.H / 8;
+    uint4 xv[NB], wv[NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z = fmaf(bf16_lo(xs[i]), bf16_lo(ws[i]), z);
-            z = fmaf(bf16_hi(xs[i]), bf16_hi(ws[i]), z);
-        }
+    for (int i = 0; i < NB; ++i) {
+        const int c = lane + WAVE * i;
+        xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        wv[i] = c < nc8 ? ld16(a.sh_gate_w + c * 8) : make_uint4(0, 0, 0, 0);
     }
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) z = dot8_bf16_regs(xv[i], wv[i], z);
     z = wave_allsum(z);
-    if (lane == 0) a.gamma[t] = 1.0f / (1.0f + expf(-z));
+    if (lane < REPL) st_dev(a.gamma + lane * a.T + t, 1.0f / (1.0f + expf(-z)));
 }
 
 // ------------------------------------------------------------- phase B
 
-// routed rows n0..n0+GU_ROWS-1 of pair p: h = silu(g) * u (fp32)
+// routed rows n0..n0+GU_ROWS-1 of pair p: h = silu(g) * u (fp32); loads first
 template <int NC>
-__device__ void gateup_item(const FusedArgs &a, int p, int n0, int e, const uint8_t *qx,
-                            const float *sx, int lane) {
-    const int H = a.H, I = a.I, nchunk = H / 16, KB = H / GROUP;
+struct GateUpRegs {
+    uint4 g[NC][GU_ROWS], u[NC][GU_ROWS];
+};
+
+template <int NC>
+__device__ __forceinline__ void gateup_load(const FusedArgs &a, int n0, int e, int lane,
+                                            GateUpRegs<NC> &r) {
+    const int H = a.H, I = a.I, nchunk = H / 16;
     const uint8_t *wg = a.w_gate + ((int64_t)e * I + n0) * H;
     const uint8_t *wu = a.w_up + ((int64_t)e * I + n0) * H;
-    const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
-    const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
-    uint4 wgv[NC][GU_ROWS], wuv[NC][GU_ROWS];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + WAVE * i;
 #pragma unroll
-        for (int r = 0; r < GU_ROWS; ++r) {
+        for (int q = 0; q < GU_ROWS; ++q) {
             if (c < nchunk) {
-                wgv[i][r] = ld16(wg + (int64_t)r * H + c * 16);
-                wuv[i][r] = ld16(wu + (int64_t)r * H + c * 16);
+                r.g[i][q] = ld16(wg + (int64_t)q * H + c * 16);
+                r.u[i][q] = ld16(wu + (int64_t)q * H + c * 16);
             } else {
-                wgv[i][r] = wuv[i][r] = make_uint4(0, 0, 0, 0);
+                r.g[i][q] = r.u[i][q] = make_uint4(0, 0, 0, 0);
             }
         }
     }
+}
+
+template <int NC>
+__device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0, int e,
+                                               const uint8_t *qx, const float *sx, int lane,
+                                               const GateUpRegs<NC> &r) {
+    const int H = a.H, I = a.I, nchunk = H / 16, KB = H / GROUP;
+    const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+    const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
     float accg[GU_ROWS] = {}, accu[GU_ROWS] = {};
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -206,19 +258,20 @@ __device__ void gateup_item(const FusedArgs &a, int p, int n0, int e, const uint
             const int b = c / 8;
             const float s = sx[b];
 #pragma unroll
-            for (int r = 0; r < GU_ROWS; ++r) {
-                accg[r] = fmaf(s * sg[b], dot16_fp8(xq, wgv[i][r]), accg[r]);
-                accu[r] = fmaf(s * su[b], dot16_fp8(xq, wuv[i][r]), accu[r]);
+            for (int q = 0; q < GU_ROWS; ++q) {
+                accg[q] = fmaf(s * sg[b], dot16_fp8(xq, r.g[i][q]), accg[q]);
+                accu[q] = fmaf(s * su[b], dot16_fp8(xq, r.u[i][q]), accu[q]);
             }
         }
     }
     float hv = 0.0f;
 #pragma unroll
-    for (int r = 0; r < GU_ROWS; ++r) {
-        const float g = wave_allsum(accg[r]), u = wave_allsum(accu[r]);
-        if (lane == r) hv = silu(g) * u;
+    for (int q = 0; q < GU_ROWS; ++q) {
+        const float g = wave_allsum(accg[q]), u = wave_allsum(accu[q]);
+        if (lane % GU_ROWS == q) hv = silu(g) * u;
     }
-    if (lane < GU_ROWS) a.h[(int64_t)p * I + n0 + lane] = hv;
+    if (lane < GU_ROWS * REPL)
+        st_dev(a.h + ((int64_t)(lane / GU_ROWS) * a.T * a.K + p) * I + n0 + lane % GU_ROWS, hv);
 }
 
 // ------------------------------------------------------------- phase C
@@ -234,39 +287,113 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 // Output rows of row t: RPP = 64 / LPR rows per wave item, LPR lanes per
-// row, CPL 16-byte chunks per lane of one I-long down row.
-template <int CPL, int LPR>
-__device__ void down_item(const FusedArgs &a, int t, int m, int sub, const uint8_t *qh,
-                          const float *shs, const int32_t *ids, const float *wts) {
-    const int H = a.H, I = a.I, K = a.K, Is = a.Is, IB = I / GROUP;
-    uint4 wv[MAX_K][CPL];
+// row, CPL 16-byte chunks per lane of one I-long down row. The weight loads
+// are split from the arithmetic so a wave can issue its first item's down
+// rows before the routed gate/up work and the second handoff.
+constexpr int SD_CH = 4;  // shared down-row chunks per lane held in registers
+
+template <int KMAX, int CPL>
+struct DownRegs {
+    uint4 w[KMAX][CPL];  // routed down rows (known after routing)
+    uint4 s[SD_CH];      // shared down row (known at kernel start)
+};
+
+template <int KMAX, int CPL, int LPR>
+__device__ __forceinline__ void down_load_shared(const FusedArgs &a, int m, int sub,
+                                                 DownRegs<KMAX, CPL> &r) {
+    const uint16_t *srow = a.sh_down + (int64_t)m * a.Is;
 #pragma unroll
-    for (int j = 0; j < MAX_K; ++j)
+    for (int i = 0; i < SD_CH; ++i) {
+        const int c = sub + LPR * i;
+        r.s[i] = c < a.Is / 8 ? ld16(srow + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int KMAX, int CPL, int LPR>
+__device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int m, int sub,
+                                                 const int32_t *ids, DownRegs<KMAX, CPL> &r) {
+    const int H = a.H, I = a.I, K = a.K;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
         if (j < K) {
             const uint8_t *row = a.w_down + ((int64_t)ids[t * K + j] * H + m) * I;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = sub + LPR * i;
-                wv[j][i] = c < I / 16 ? ld16(row + c * 16) : make_uint4(0, 0, 0, 0);
+                r.w[j][i] = c < I / 16 ? ld16(row + c * 16) : make_uint4(0, 0, 0, 0);
             }
         }
-    float sacc = 0.0f;
-    if (Is > 0) {
-        const uint16_t *srow = a.sh_down + (int64_t)m * Is;
-        const uint16_t *hsr = a.hs + (int64_t)t * Is;
-        for (int c = sub; c < Is / 8; c += LPR) {
-            const uint4 w8 = ld16(srow + c * 8), h8 = ld16(hsr + c * 8);
-            const uint32_t ws[4] = {w8.x, w8.y, w8.z, w8.w}, hs[4] = {h8.x, h8.y, h8.z, h8.w};
+}
+
+// hs chunks and gamma of row t for one shared down row, from this
+// workgroup's replica (written by other workgroups: device-coherent loads)
+struct HsRegs {
+    uint64_t h[SD_CH][2];
+    float gamma;
+};
+
+template <int LPR>
+__device__ __forceinline__ void hs_load(const FusedArgs &a, int t, int sub, HsRegs &r) {
+    const int rp = blockIdx.x % REPL;
+    const uint64_t *hsr =
+        reinterpret_cast<const uint64_t *>(a.hs + (int64_t)(rp * a.T + t) * a.Is);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sacc = fmaf(bf16_lo(hs[i]), bf16_lo(ws[i]), sacc);
-                sacc = fmaf(bf16_hi(hs[i]), bf16_hi(ws[i]), sacc);
-            }
-        }
+    for (int i = 0; i < SD_CH; ++i) {
+        const int c = sub + LPR * i;
+        r.h[i][0] = c < a.Is / 8 ? ld_dev(hsr + 2 * c) : 0ull;
+        r.h[i][1] = c < a.Is / 8 ? ld_dev(hsr + 2 * c + 1) : 0ull;
     }
+    r.gamma = ld_dev(a.gamma + rp * a.T + t);
+}
+
+__device__ __forceinline__ float dot8_bf16_pair(uint4 w8, uint64_t h01, uint64_t h23) {
+    const uint32_t hs[4] = {(uint32_t)h01, (uint32_t)(h01 >> 32), (uint32_t)h23,
+                            (uint32_t)(h23 >> 32)};
+    const uint32_t ws[4] = {w8.x, w8.y, w8.z, w8.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_lo(hs[i]), bf16_lo(ws[i]), acc);
+        acc = fmaf(bf16_hi(hs[i]), bf16_hi(ws[i]), acc);
+    }
+    return acc;
+}
+
+// gamma * (shared down row m . hs[t]), reduced over the row's LPR lanes
+template <int KMAX, int CPL, int LPR>
+__device__ float shared_down(const FusedArgs &a, int t, int m, int sub,
+                             const DownRegs<KMAX, CPL> &r, const HsRegs &hr) {
+    const int Is = a.Is;
+    if (Is == 0) return 0.0f;
+    float sacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SD_CH; ++i) {
+        const int c = sub + LPR * i;
+        if (c < Is / 8) sacc += dot8_bf16_pair(r.s[i], hr.h[i][0], hr.h[i][1]);
+    }
+    if (Is / 8 > LPR * SD_CH) {  // rows longer than the register copy
+        const int rp = blockIdx.x % REPL;
+        const uint64_t *hsr =
+            reinterpret_cast<const uint64_t *>(a.hs + (int64_t)(rp * a.T + t) * Is);
+        const uint16_t *srow = a.sh_down + (int64_t)m * Is;
+        for (int c = sub + LPR * SD_CH; c < Is / 8; c += LPR)
+            sacc += dot8_bf16_pair(ld16(srow + c * 8), ld_dev(hsr + 2 * c), ld_dev(hsr + 2 * c + 1));
+    }
+    return hr.gamma * seg_sum<LPR>(sacc);
+}
+
+// routed down rows and the combine: y = bf16(sum_j w_j e_j + gs), gs from
+// shared_down
+template <int KMAX, int CPL, int LPR>
+__device__ void down_compute(const FusedArgs &a, int t, int m, int sub, const uint8_t *qh,
+                             const float *shs, const int32_t *ids, const float *wts,
+                             const DownRegs<KMAX, CPL> &r, float gs) {
+    const int H = a.H, I = a.I, K = a.K, IB = I / GROUP;
+    // each lane sums its slots' partial products (weight applied per slot,
+    // slots in order), then one reduction over the row's lanes
     float yacc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MAX_K; ++j)
+    for (int j = 0; j < KMAX; ++j)
         if (j < K) {
             const int p = t * K + j;
             const float *sd = a.s_down + ((int64_t)ids[p] * (H / GROUP) + m / GROUP) * IB;
@@ -278,12 +405,12 @@ __device__ void down_item(const FusedArgs &a, int t, int m, int sub, const uint8
                     float hq[16];
                     decode16(*reinterpret_cast<const uint4 *>(qh + (int64_t)p * I + c * 16), hq);
                     const int b = c / 8;
-                    acc = fmaf(shs[p * IB + b] * sd[b], dot16_fp8(hq, wv[j][i]), acc);
+                    acc = fmaf(shs[p * IB + b] * sd[b], dot16_fp8(hq, r.w[j][i]), acc);
                 }
             }
-            yacc = fmaf(wts[p], seg_sum<LPR>(acc), yacc);
+            yacc = fmaf(wts[p], acc, yacc);
         }
-    if (Is > 0) yacc = fmaf(a.gamma[t], seg_sum<LPR>(sacc), yacc);
+    yacc = seg_sum<LPR>(yacc) + gs;
     if (sub == 0) a.y[(int64_t)t * H + m] = (uint16_t)f32_to_bf16(yacc);
 }
 
@@ -322,11 +449,15 @@ __device__ void quant_to_lds(const void *src, int n_groups, uint8_t *q, float *s
             f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
             f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
         } else {
-            const float *p = static_cast<const float *>(src) + (int64_t)g * GROUP + sub * 8;
-            const float4 v0 = *reinterpret_cast<const float4 *>(p);
-            const float4 v1 = *reinterpret_cast<const float4 *>(p + 4);
-            f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
-            f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+            // h was written by other workgroups: device-coherent loads
+            const uint64_t *p = reinterpret_cast<const uint64_t *>(
+                static_cast<const float *>(src) + (int64_t)g * GROUP + sub * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t v = ld_dev(p + i);
+                f[2 * i] = __uint_as_float((uint32_t)v);
+                f[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+            }
         }
         float amax = 0.0f;
 #pragma unroll
@@ -341,7 +472,7 @@ __device__ void quant_to_lds(const void *src, int n_groups, uint8_t *q, float *s
     }
 }
 
-template <int NC, int CPL, int LPR>
+template <int NC, int KMAX, int CPL, int LPR>
 __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a.T, H = a.H, K = a.K, I = a.I, P = T * K;
@@ -356,90 +487,140 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nw = a.nwg * 4;
+    constexpr int NB = 2 * NC;  // bf16 H-row chunks per lane
     const int gw = wave * a.nwg + blockIdx.x;  // workgroup-major wave index
-    if (threadIdx.x == 0) s_target = ld_acquire_relaxed(a.sync) + 1u;
-    quant_to_lds<true>(a.x, T * (H / GROUP), qx, sx);
+    if (threadIdx.x == 0) s_target = ld_dev(a.sync) + 1u;
 
-    // A: router logits, shared gate/up, gate
-    const int n_router = T * a.E;
-    const int n_shared = a.Is > 0 ? T * (a.Is / SH_ROWS) : 0;
-    const int n_gamma = a.Is > 0 ? T : 0;
-    for (int it = gw; it < n_router + n_shared + n_gamma; it += nw) {
+    constexpr int RPP = WAVE / LPR;
+    const int sub = lane % LPR, rsel = lane / LPR;
+    const int items = T * (H / RPP);  // phase-C output row blocks
+    const int t_first = gw / (H / RPP), m_first = (gw % (H / RPP)) * RPP + rsel;
+    DownRegs<KMAX, CPL> dr;
+
+    // A: router logits, shared-expert gate/up rows and the shared gate. Every
+    // load that does not depend on the routing is issued here, including
+    // this wave's first shared down row (kept in registers until phase C).
+    if (gw < items && a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m_first, sub, dr);
+    const int n_router = T * a.E, n_shrows = T * a.Is, n_gamma = a.Is > 0 ? T : 0;
+    for (int it = gw; it < n_router + n_shrows + n_gamma; it += nw) {
         if (it < n_router) {
-            router_item(a, it / a.E, it % a.E, lane);
-        } else if (it < n_router + n_shared) {
-            const int s = it - n_router, per = a.Is / SH_ROWS;
-            shared_item(a, s / per, (s % per) * SH_ROWS, lane);
+            router_item<NB>(a, it / a.E, it % a.E, lane);
+        } else if (it < n_router + n_shrows) {
+            const int sidx = it - n_router;
+            SharedRegs<NB> sr;
+            shared_load<NB>(a, sidx / a.Is, sidx % a.Is, lane, sr);
+            shared_compute<NB>(a, sidx / a.Is, sidx % a.Is, lane, sr);
         } else {
-            gamma_item(a, it - n_router - n_shared, lane);
+            gamma_item<NB>(a, it - n_router - n_shrows, lane);
         }
     }
+    quant_to_lds<true>(a.x, T * (H / GROUP), qx, sx);  // needed from phase B on
     __syncthreads();
     const uint32_t target = s_target;
     handoff(a, 0, target);
     // every workgroup has read the generation word: advance it for the next call
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        __hip_atomic_store(a.sync, target + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev(a.sync, target + 1u);
 
-    // B: top-K per row (one wave per row), then routed gate/up
-    for (int t = wave; t < T; t += 4) topk_row(a.logits + (int64_t)t * a.E, a.E, K, lane,
-                                               ids + t * K, wts + t * K);
+    // B: top-K per row (one wave per row); issue this wave's first block of
+    // routed down rows; then the routed gate/up rows
+    for (int t = wave; t < T; t += 4)
+        topk_row<true>(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * a.E, a.E, K, lane,
+                       ids + t * K, wts + t * K, !a.bias && !(a.flags & K_LOGITS_FP32));
     __syncthreads();
+    HsRegs hr;
+    if (gw < items) {
+        down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
+        if (a.Is > 0) hs_load<LPR>(a, t_first, sub, hr);
+    }
     const int per_pair = I / GU_ROWS;
     for (int it = gw; it < P * per_pair; it += nw) {
         const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
-        gateup_item<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane);
+        GateUpRegs<NC> gr;
+        gateup_load<NC>(a, n0, ids[p], lane, gr);
+        gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr);
     }
+    // the first item's shared-expert term needs only phase-A results
+    float gs_first = 0.0f;
+    if (gw < items) gs_first = shared_down<KMAX, CPL, LPR>(a, t_first, m_first, sub, dr, hr);
     handoff(a, 1, target);
 
     // C: re-quantise h, then whole output rows with the combine
-    quant_to_lds<false>(a.h, P * (I / GROUP), qh, shs);
+    quant_to_lds<false>(a.h + (int64_t)(blockIdx.x % REPL) * P * I, P * (I / GROUP), qh, shs);
     __syncthreads();
-    constexpr int RPP = WAVE / LPR;
-    const int sub = lane % LPR, rsel = lane / LPR;
-    const int items = T * (H / RPP);
     for (int it = gw; it < items; it += nw) {
         const int t = it / (H / RPP);
         const int m = (it % (H / RPP)) * RPP + rsel;
-        down_item<CPL, LPR>(a, t, m, sub, qh, shs, ids, wts);
+        float gsv = gs_first;
+        if (it != gw) {
+            if (a.Is > 0) {
+                down_load_shared<KMAX, CPL, LPR>(a, m, sub, dr);
+                hs_load<LPR>(a, t, sub, hr);
+            }
+            down_load_routed<KMAX, CPL, LPR>(a, t, m, sub, ids, dr);
+            gsv = shared_down<KMAX, CPL, LPR>(a, t, m, sub, dr, hr);
+        }
+        down_compute<KMAX, CPL, LPR>(a, t, m, sub, qh, shs, ids, wts, dr, gsv);
     }
+}
+
+template <int NC, int KMAX>
+static hipError_t launch_k(const FusedArgs &a, size_t lds, hipStream_t st) {
+    const dim3 grid(a.nwg), block(256);
+    const int chunks = a.I / 16;
+    if (chunks <= 8)
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 1, 8>), grid, block, lds, st, a);
+    else if (chunks <= 16)
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 1, 16>), grid, block, lds, st, a);
+    else if (chunks <= 32)
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 1, 32>), grid, block, lds, st, a);
+    else if (chunks <= 64)
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 1, 64>), grid, block, lds, st, a);
+    else if (chunks <= 128)
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 2, 64>), grid, block, lds, st, a);
+    else
+        hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, 4, 64>), grid, block, lds, st, a);
+    return hipGetLastError();
 }
 
 template <int NC>
 static hipError_t launch_nc(const FusedArgs &a, size_t lds, hipStream_t st) {
-    const dim3 grid(a.nwg), block(256);
-    const int chunks = a.I / 16;
-    if (chunks <= 8)
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 1, 8>), grid, block, lds, st, a);
-    else if (chunks <= 16)
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 1, 16>), grid, block, lds, st, a);
-    else if (chunks <= 32)
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 1, 32>), grid, block, lds, st, a);
-    else if (chunks <= 64)
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 1, 64>), grid, block, lds, st, a);
-    else if (chunks <= 128)
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 2, 64>), grid, block, lds, st, a);
-    else
-        hipLaunchKernelGGL((decode_fused_kernel<NC, 4, 64>), grid, block, lds, st, a);
-    return hipGetLastError();
+    if (a.K <= 4) return launch_k<NC, 4>(a, lds, st);
+    if (a.K <= 8) return launch_k<NC, 8>(a, lds, st);
+    return launch_k<NC, 16>(a, lds, st);
 }
 
-template <int NC, int CPL, int LPR>
-static hipError_t set_lds_limit() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_fused_kernel<NC, CPL, LPR>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+template <int NC, int KMAX, int CPL, int LPR>
+static void set_lds_limit() {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&decode_fused_kernel<NC, KMAX, CPL, LPR>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
+template <int NC, int KMAX>
+static void set_lds_limits_k() {
+    set_lds_limit<NC, KMAX, 1, 8>();
+    set_lds_limit<NC, KMAX, 1, 16>();
+    set_lds_limit<NC, KMAX, 1, 32>();
+    set_lds_limit<NC, KMAX, 1, 64>();
+    set_lds_limit<NC, KMAX, 2, 64>();
+    set_lds_limit<NC, KMAX, 4, 64>();
+}
+
+template <int NC>
+static void set_lds_limits() {
+    set_lds_limits_k<NC, 4>();
+    set_lds_limits_k<NC, 8>();
+    set_lds_limits_k<NC, 16>();
 }
 
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {
     const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I).total;
     if (lds > 64 * 1024) {
         static const bool once = [] {
-#define MOE_SET(NC)                                                                       \
-    (void)set_lds_limit<NC, 1, 8>(); (void)set_lds_limit<NC, 1, 16>();                       \
-    (void)set_lds_limit<NC, 1, 32>(); (void)set_lds_limit<NC, 1, 64>();                      \
-    (void)set_lds_limit<NC, 2, 64>(); (void)set_lds_limit<NC, 4, 64>();
-            MOE_SET(1) MOE_SET(2) MOE_SET(4) MOE_SET(8)
-#undef MOE_SET
+            set_lds_limits<1>();
+            set_lds_limits<2>();
+            set_lds_limits<4>();
+            set_lds_limits<8>();
             return true;
         }();
         (void)once;

@@ -19,9 +19,10 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
                                const float *bias, int H, int E, uint32_t flags, float *logits,
                                hipStream_t st);
 // top-K + softmax per row; when gate_w != NULL also gamma[t] = sigmoid(gate_w . x[t])
+// packed: every logit is a plain bf16 value (no bias, bf16 rounding on)
 hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids,
                              float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
-                             float *gamma, hipStream_t st);
+                             float *gamma, bool packed, hipStream_t st);
 
 // ---- decode.hip (row-at-a-time path: one persistent kernel per call)
 struct FusedArgs {
@@ -32,16 +33,20 @@ struct FusedArgs {
     const uint8_t *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
-    float *logits;    // [T, E]
-    float *gamma;     // [T]
-    uint16_t *hs;     // [T, Is] bf16 shared-expert SwiGLU output
-    float *h;         // [T*K, I] routed SwiGLU output (fp32)
-    uint32_t *sync;   // [0] generation, [32] error, [64 + b*nwg + w] handoff flags
+    // values that cross workgroups are kept in DECODE_REPLICAS copies, so
+    // each copy is read by 1/DECODE_REPLICAS of the workgroups
+    float *logits;    // [R][T, E]
+    float *gamma;     // [R][T]
+    uint16_t *hs;     // [R][T, Is] bf16 shared-expert SwiGLU output
+    float *h;         // [R][T*K, I] routed SwiGLU output (fp32)
+    uint32_t *sync;   // generation, error, go words and arrival flags
     uint16_t *y;      // [T, H]
     int nwg;          // workgroups = compute units (all co-resident)
 };
 constexpr int DECODE_MAX_ROWS = 16;
-constexpr int SYNC_WORDS = 64 + 2 * 1024;
+constexpr int DECODE_REPLICAS = 8;
+constexpr int SYNC_FLAGS = 64;
+constexpr int SYNC_WORDS = SYNC_FLAGS + 2 * DECODE_REPLICAS * 1024;
 bool decode_fits(int T, int H, int K, int I);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
 

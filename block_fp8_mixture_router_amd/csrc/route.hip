@@ -113,11 +113,12 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float *__restrict__ logits, int T, int E, int K, int32_t *__restrict__ ids,
     float *__restrict__ wts, const uint16_t *__restrict__ x,
-    const uint16_t *__restrict__ gate_w, int H, float *__restrict__ gamma) {
+    const uint16_t *__restrict__ gate_w, int H, float *__restrict__ gamma, bool packed) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= T) return;  // whole waves leave together
-    topk_row(logits + (int64_t)t * E, E, K, lane, ids + (int64_t)t * K, wts + (int64_t)t * K);
+    topk_row<false>(logits + (int64_t)t * E, E, K, lane, ids + (int64_t)t * K,
+                    wts + (int64_t)t * K, packed);
     if (gate_w) {
         const uint16_t *xr = x + (int64_t)t * H;
         float z = 0.0f;
@@ -137,10 +138,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
 hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids,
                              float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
-                             float *gamma, hipStream_t st) {
+                             float *gamma, bool packed, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K,
-                       ids, weights, x, gate_w, H, gamma);
+                       ids, weights, x, gate_w, H, gamma, packed);
     return hipGetLastError();
 }
 

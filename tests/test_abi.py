@@ -116,3 +116,11 @@ def test_supported_is_false_without_gpu():
         pytest.skip("a GPU is present")
     assert moe.supported(0) is False
     assert moe.supported(-1) is False
+
+
+def test_workspace_is_monotonic_in_rows():
+    """A workspace sized for max_rows must serve every call with fewer rows."""
+    for shape in (inputs.TINY, inputs.DECODE):
+        c = moe.config(shape)
+        sizes = [moe.workspace_bytes(c, T) for T in range(1, 1100)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:]))
