@@ -179,7 +179,8 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
                                 cfg->hidden, cfg->n_experts, cfg->flags, lg, st));
     MOE_TRY(launch_route_topk(lg, T, cfg->n_experts, cfg->top_k, ids, weights, nullptr, nullptr,
                               cfg->hidden, nullptr,
-                              !router_bias && !(cfg->flags & MOE_LOGITS_FP32), st));
+                              !router_bias && !(cfg->flags & MOE_LOGITS_FP32), nullptr, nullptr,
+                              st));
     return MOE_OK;
 }
 
@@ -247,9 +248,6 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     }
     MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(w->router_w),
                                 w->router_bias, H, E, cfg->flags, lg, st));
-    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
-                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
-                              gamma, !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32), st));
     GroupedArgs g{};
     g.T = T; g.H = H; g.E = E; g.K = K; g.I = cfg->inter; g.Is = cfg->shared_inter;
     g.x = xb;
@@ -271,11 +269,13 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     g.hs = at<uint16_t>(workspace, L.hs);
     g.stage = at<uint16_t>(workspace, L.stage);
     g.y = static_cast<uint16_t *>(y);
-    MOE_TRY(launch_quant_act(xb, (int64_t)T * (H / 128), const_cast<uint8_t *>(g.qx),
-                             const_cast<float *>(g.sx), st));
+    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
+                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
+                              gamma, !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32),
+                              at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
+    MOE_TRY(launch_shared_gateup(g, st));
     MOE_TRY(launch_group_sort(g, st));
     MOE_TRY(launch_grouped_gateup(g, st));
-    MOE_TRY(launch_shared_gateup(g, st));
     MOE_TRY(launch_grouped_down(g, st));
     MOE_TRY(launch_shared_down_combine(g, st));
     return MOE_OK;

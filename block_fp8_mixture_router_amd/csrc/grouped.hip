@@ -18,7 +18,7 @@
 //  - A work tile is up to 64 sorted (row, slot) pairs of one expert times 128
 //    output columns; activations are staged through LDS (shared by the four
 //    waves), weights stream straight from HBM into registers (each weight
-//    byte is used by one wave only), double-buffered one K step ahead.
+//    byte is used by one wave only) through a ring several K steps deep.
 //  - The gate/up epilogue applies SwiGLU and re-quantises each pair's 128
 //    columns (one group) to e4m3 before anything leaves the CU.
 //  - No floating-point atomics anywhere: every sum has a fixed order, so
@@ -147,9 +147,14 @@ __device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
 // ----------------------------------------------------------- gate / up
 // grid.x = max_tiles * (I / 128). Wave w owns output columns
 // [nb*128 + 32w, +32): two 16-column MFMA tiles for gate and two for up.
+// Weights stream through a register ring PD K-steps deep (HBM latency needs
+// about 100 KiB in flight per CU); activations for each K-step go through a
+// double-buffered LDS tile, so each step needs a single barrier.
 
-__global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[GR][GROUP + APAD];
+// PD = K steps of loads in flight; the host picks PD dividing H / 128.
+template <int PD>
+__global__ __launch_bounds__(256, 2) void grouped_gateup_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[2][GR][GROUP + APAD];
     __shared__ float sxs[GR][64];
     __shared__ int toks[GR];
     __shared__ float amax_part[4][GR];
@@ -189,64 +194,71 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) accg[rt][ct] = accu[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    uint4 bg[2][2], bu[2][2], av[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        bg[ct][0] = ld16(wgp[ct]);
-        bg[ct][1] = ld16(wgp[ct] + 16);
-        bu[ct][0] = ld16(wup[ct]);
-        bu[ct][1] = ld16(wup[ct] + 16);
-    }
-    av[0] = atok >= 0 ? ld16(aptr) : make_uint4(0, 0, 0, 0);
-    av[1] = atok >= 0 ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
-
-    for (int kb = 0; kb < KB; ++kb) {
-        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
-        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
-        __syncthreads();
-        v8i cg[2], cu[2];
+    uint4 bg[PD][2][2], bu[PD][2][2], av[PD][2];
+    // Every load is unconditional and each K step of the main loop issues the
+    // same loads (those of step kb + PD), so the compiler's wait counts stay
+    // exact across the loop; rows past the tile read a valid row whose
+    // results are never stored. The last PD steps issue no loads.
+    auto load_a = [&](int kb, uint4 (&dst)[2]) {
+        dst[0] = ld16(aptr + kb * GROUP);
+        dst[1] = ld16(aptr + kb * GROUP + 16);
+    };
+    auto load_b = [&](int kb, uint4 (&g)[2][2], uint4 (&u)[2][2]) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            cg[ct] = as_v8i(bg[ct][0], bg[ct][1]);
-            cu[ct] = as_v8i(bu[ct][0], bu[ct][1]);
+            g[ct][0] = ld16(wgp[ct] + kb * GROUP);
+            g[ct][1] = ld16(wgp[ct] + kb * GROUP + 16);
+            u[ct][0] = ld16(wup[ct] + kb * GROUP);
+            u[ct][1] = ld16(wup[ct] + kb * GROUP + 16);
         }
-        if (kb + 1 < KB) {
-            const int off = (kb + 1) * GROUP;
+    };
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+        load_a(d, av[d]);
+        load_b(d, bg[d], bu[d]);
+    }
+    __syncthreads();  // toks / sxs ready
+
+    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
+        const bool more = kb0 + PD < KB;  // uniform: the main loop or the last group
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int kb = kb0 + d;
+            uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
+            *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+            *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+            if (more) load_a(kb + PD, av[d]);
+            __syncthreads();
+            const float sgk = sgr[kb], suk = sur[kb];
+            v8i cg[2], cu[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                bg[ct][0] = ld16(wgp[ct] + off);
-                bg[ct][1] = ld16(wgp[ct] + off + 16);
-                bu[ct][0] = ld16(wup[ct] + off);
-                bu[ct][1] = ld16(wup[ct] + off + 16);
+                cg[ct] = as_v8i(bg[d][ct][0], bg[d][ct][1]);
+                cu[ct] = as_v8i(bu[d][ct][0], bu[d][ct][1]);
             }
-            if (atok >= 0) {
-                av[0] = ld16(aptr + off);
-                av[1] = ld16(aptr + off + 16);
-            }
-        }
-        const float sgk = sgr[kb], suk = sur[kb];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            if (rt < nrt) {
-                const uint8_t *ar = &As[rt * 16 + l16][32 * kq];
-                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
-                                      *reinterpret_cast<const uint4 *>(ar + 16));
-                float sxr[4];
+            for (int rt = 0; rt < 4; ++rt) {
+                if (rt < nrt) {
+                    const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
+                    const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                          *reinterpret_cast<const uint4 *>(ar + 16));
+                    float sxr[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sxr[i] = sxs[rt * 16 + 4 * kq + i][kb];
+                    for (int i = 0; i < 4; ++i) sxr[i] = sxs[rt * 16 + 4 * kq + i][kb];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const v4f pg = mfma_fp8_k128(af, cg[ct]);
-                    const v4f pu = mfma_fp8_k128(af, cu[ct]);
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const v4f pg = mfma_fp8_k128(af, cg[ct]);
+                        const v4f pu = mfma_fp8_k128(af, cu[ct]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        accg[rt][ct][i] = fmaf(sxr[i] * sgk, pg[i], accg[rt][ct][i]);
-                        accu[rt][ct][i] = fmaf(sxr[i] * suk, pu[i], accu[rt][ct][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            accg[rt][ct][i] = fmaf(sxr[i] * sgk, pg[i], accg[rt][ct][i]);
+                            accu[rt][ct][i] = fmaf(sxr[i] * suk, pu[i], accu[rt][ct][i]);
+                        }
                     }
                 }
             }
+            if (more) load_b(kb + PD, bg[d], bu[d]);
         }
-        __syncthreads();
     }
 
     // epilogue: h = silu(g) * u, per-row amax over the 128 columns, e4m3
@@ -263,12 +275,12 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
             }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float m = wave_max<16>(m4[i]);
+            const float m = group16_max(m4[i]);
             if (l16 == 0) amax_part[wave][rt * 16 + 4 * kq + i] = m;
         }
     }
     __syncthreads();
-    uint8_t(*Cs)[GROUP + APAD] = As;  // reuse the staging buffer for codes
+    uint8_t(*Cs)[GROUP + APAD] = As[0];  // reuse the staging buffer for codes
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -296,16 +308,21 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupedArgs a) {
 
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.max_tiles * (a.I / GROUP)));
-    hipLaunchKernelGGL(grouped_gateup_kernel, grid, dim3(256), 0, st, a);
+    if ((a.H / GROUP) % 2 == 0)
+        hipLaunchKernelGGL(grouped_gateup_kernel<2>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(grouped_gateup_kernel<1>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- down
 // grid.x = max_tiles * (H / 128). Outputs e_j in bf16, written to the
-// (row, slot) pair's own row of the stage buffer.
+// (row, slot) pair's own row of the stage buffer. Up to four K steps
+// (the whole K = I = 512 extent) are kept in flight.
 
-__global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[GR][GROUP + APAD];
+template <int PD>
+__global__ __launch_bounds__(256, 2) void grouped_down_kernel(GroupedArgs a) {
+    __shared__ __align__(16) uint8_t As[2][GR][GROUP + APAD];
     __shared__ float shs[GR][32];
     __shared__ int pairs[GR];
     __shared__ __align__(16) uint16_t Ys[GR][GROUP + 8];
@@ -338,55 +355,60 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-    uint4 bd[2][2], av[2];
+    uint4 bd[PD][2][2], av[PD][2];
+    // unconditional loads (see the gate/up kernel)
+    auto load_a = [&](int kb, uint4 (&dst)[2]) {
+        dst[0] = ld16(aptr + kb * GROUP);
+        dst[1] = ld16(aptr + kb * GROUP + 16);
+    };
+    auto load_b = [&](int kb, uint4 (&b)[2][2]) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        bd[ct][0] = ld16(wdp[ct]);
-        bd[ct][1] = ld16(wdp[ct] + 16);
+        for (int ct = 0; ct < 2; ++ct) {
+            b[ct][0] = ld16(wdp[ct] + kb * GROUP);
+            b[ct][1] = ld16(wdp[ct] + kb * GROUP + 16);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+        load_a(d, av[d]);
+        load_b(d, bd[d]);
     }
-    av[0] = arv ? ld16(aptr) : make_uint4(0, 0, 0, 0);
-    av[1] = arv ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
     __syncthreads();  // shs and pairs ready
 
-    for (int kb = 0; kb < KB; ++kb) {
-        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
-        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
-        __syncthreads();
-        v8i cd[2];
+    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
+        const bool more = kb0 + PD < KB;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) cd[ct] = as_v8i(bd[ct][0], bd[ct][1]);
-        if (kb + 1 < KB) {
-            const int off = (kb + 1) * GROUP;
+        for (int d = 0; d < PD; ++d) {
+            const int kb = kb0 + d;
+            uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
+            *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+            *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+            if (more) load_a(kb + PD, av[d]);
+            __syncthreads();
+            const float sdk = sdr[kb];
+            v8i cd[2];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                bd[ct][0] = ld16(wdp[ct] + off);
-                bd[ct][1] = ld16(wdp[ct] + off + 16);
-            }
-            if (arv) {
-                av[0] = ld16(aptr + off);
-                av[1] = ld16(aptr + off + 16);
-            }
-        }
-        const float sdk = sdr[kb];
+            for (int ct = 0; ct < 2; ++ct) cd[ct] = as_v8i(bd[d][ct][0], bd[d][ct][1]);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            if (rt < nrt) {
-                const uint8_t *ar = &As[rt * 16 + l16][32 * kq];
-                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
-                                      *reinterpret_cast<const uint4 *>(ar + 16));
-                float shr[4];
+            for (int rt = 0; rt < 4; ++rt) {
+                if (rt < nrt) {
+                    const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
+                    const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                          *reinterpret_cast<const uint4 *>(ar + 16));
+                    float shr[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) shr[i] = shs[rt * 16 + 4 * kq + i][kb];
+                    for (int i = 0; i < 4; ++i) shr[i] = shs[rt * 16 + 4 * kq + i][kb];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const v4f p = mfma_fp8_k128(af, cd[ct]);
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const v4f p = mfma_fp8_k128(af, cd[ct]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[rt][ct][i] = fmaf(shr[i] * sdk, p[i], acc[rt][ct][i]);
+                        for (int i = 0; i < 4; ++i)
+                            acc[rt][ct][i] = fmaf(shr[i] * sdk, p[i], acc[rt][ct][i]);
+                    }
                 }
             }
+            if (more) load_b(kb + PD, bd[d]);
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -407,7 +429,13 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedArgs a) {
 
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.max_tiles * (a.H / GROUP)));
-    hipLaunchKernelGGL(grouped_down_kernel, grid, dim3(256), 0, st, a);
+    const int kb = a.I / GROUP;
+    if (kb % 4 == 0)
+        hipLaunchKernelGGL(grouped_down_kernel<4>, grid, dim3(256), 0, st, a);
+    else if (kb % 2 == 0)
+        hipLaunchKernelGGL(grouped_down_kernel<2>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(grouped_down_kernel<1>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -420,70 +448,78 @@ __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
 }
 
 // ---------------------------------------------------- shared gate / up
-// Tile: 32 rows x 64 columns of Is; grid (ceil(T/32), Is/64). Wave w owns
-// 16 columns of gate and up. Each lane reads 64 contiguous bytes of its
-// weight row per 128 columns of H and splits them over four MFMAs; the LDS
-// activation fragments follow the same column split.
+// Tile: 32 rows x 64 columns of Is. Wave w owns 16 columns of gate and up.
+// All 32 row tiles of a column block read the same weight rows; walking K in
+// the same order they would request the same lines at the same moment, which
+// measured over 2x slower. So tile r walks the K steps starting at step
+// 2r (mod KB). Each K step's partial product (four chained MFMAs from zero,
+// 128 columns) does not depend on the tile, and the partials are added in
+// fp64, so a row's result does not depend on which tile it sits in (up to
+// fp64 rounding, far below the bf16 rounding that follows). Each lane reads 64 contiguous bytes
+// of its weight row per 128 columns of H and splits them over four MFMAs;
+// the LDS activation fragments follow the same column split. Loads run two
+// K steps ahead, unconditionally (see the routed kernels).
 
 constexpr int SR = 32;  // rows per shared-expert tile
 
+template <int PD>
 __global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[SR][GROUP * 2 + APAD];
-    const int H = a.H, Is = a.Is;
-    const int t0 = blockIdx.x * SR, nb = blockIdx.y;
+    __shared__ __align__(16) uint8_t Ash[2][SR][GROUP * 2 + APAD];
+    const int H = a.H, Is = a.Is, KB = H / GROUP;
+    const int snb = Is / 64;
+    const int t0 = (blockIdx.x / snb) * SR, nb = blockIdx.x % snb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, kq = lane >> 4;
     const int arow = tid >> 3, acol = (tid & 7) * 32;  // bytes
-    const bool arv = t0 + arow < a.T;
-    const uint8_t *aptr =
-        reinterpret_cast<const uint8_t *>(a.x + (int64_t)(arv ? t0 + arow : 0) * H) + acol;
+    const int at = min(t0 + arow, a.T - 1);            // rows past T read a valid row
+    const uint8_t *aptr = reinterpret_cast<const uint8_t *>(a.x + (int64_t)at * H) + acol;
     const int n = nb * 64 + 16 * wave + l16;
     const uint8_t *gp = reinterpret_cast<const uint8_t *>(a.sh_gate + (int64_t)n * H) + 64 * kq;
     const uint8_t *up = reinterpret_cast<const uint8_t *>(a.sh_up + (int64_t)n * H) + 64 * kq;
-    v4f accg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    v4f accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    uint4 bg[4], bu[4], av[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bg[i] = ld16(gp + 16 * i);
-        bu[i] = ld16(up + 16 * i);
-    }
-    av[0] = arv ? ld16(aptr) : make_uint4(0, 0, 0, 0);
-    av[1] = arv ? ld16(aptr + 16) : make_uint4(0, 0, 0, 0);
-    const int KB = H / GROUP;
-    for (int kb = 0; kb < KB; ++kb) {
-        *reinterpret_cast<uint4 *>(&As[arow][acol]) = av[0];
-        *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = av[1];
-        __syncthreads();
-        uint4 cg[4], cu[4];
+    double dg[2][4] = {}, du[2][4] = {};
+    const int krot = (2 * (int)(blockIdx.x / snb)) % KB;
+    uint4 bg[PD][4], bu[PD][4], av[PD][2];
+    auto load = [&](int kb, uint4 (&g)[4], uint4 (&u)[4], uint4 (&x)[2]) {
+        const int off = ((kb + krot) % KB) * GROUP * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            cg[i] = bg[i];
-            cu[i] = bu[i];
+            g[i] = ld16(gp + off + 16 * i);
+            u[i] = ld16(up + off + 16 * i);
         }
-        if (kb + 1 < KB) {
-            const int off = (kb + 1) * GROUP * 2;
+        x[0] = ld16(aptr + off);
+        x[1] = ld16(aptr + off + 16);
+    };
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bg[i] = ld16(gp + off + 16 * i);
-                bu[i] = ld16(up + off + 16 * i);
-            }
-            if (arv) {
-                av[0] = ld16(aptr + off);
-                av[1] = ld16(aptr + off + 16);
+    for (int d = 0; d < PD; ++d) load(d, bg[d], bu[d], av[d]);
+    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
+        const bool more = kb0 + PD < KB;
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int kb = kb0 + d;
+            {
+                uint8_t(*Ab)[GROUP * 2 + APAD] = Ash[kb & 1];
+                *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+                *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+                __syncthreads();
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
+                    v4f pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+                        pg = mfma_bf16_k32(af, as_v8bf(bg[d][i]), pg);
+                        pu = mfma_bf16_k32(af, as_v8bf(bu[d][i]), pu);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        dg[rt][i] += (double)pg[i];
+                        du[rt][i] += (double)pu[i];
+                    }
+                }
+                if (more) load(kb + PD, bg[d], bu[d], av[d]);
             }
         }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const uint8_t *ar = &As[rt * 16 + l16][64 * kq];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
-                accg[rt] = mfma_bf16_k32(af, as_v8bf(cg[i]), accg[rt]);
-                accu[rt] = mfma_bf16_k32(af, as_v8bf(cu[i]), accu[rt]);
-            }
-        }
-        __syncthreads();
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -491,35 +527,50 @@ __global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + rt * 16 + 4 * kq + i;
             if (t < a.T)
-                a.hs[(int64_t)t * Is + n] = (uint16_t)f32_to_bf16(silu(accg[rt][i]) * accu[rt][i]);
+                a.hs[(int64_t)t * Is + n] =
+                    (uint16_t)f32_to_bf16(silu((float)dg[rt][i]) * (float)du[rt][i]);
         }
 }
 
 hipError_t launch_shared_gateup(const GroupedArgs &a, hipStream_t st) {
     if (a.Is == 0) return hipSuccess;
-    hipLaunchKernelGGL(shared_gateup_kernel, dim3((a.T + SR - 1) / SR, a.Is / 64), dim3(256), 0,
-                       st, a);
+    const dim3 grid(((a.T + SR - 1) / SR) * (a.Is / 64));
+    if ((a.H / GROUP) % 2 == 0)
+        hipLaunchKernelGGL(shared_gateup_kernel<2>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(shared_gateup_kernel<1>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 // ------------------------------------------- shared down + combine
-// Tile: 32 rows x 128 columns of H; grid (ceil(T/32), H/128). The shared
-// expert's down product s lands in LDS; then each thread produces 8
-// contiguous outputs y = bf16(sum_j w_j e_j + gamma s) from 16-byte loads of
-// the staged e_j, summing the slots in order.
+// Tile: 32 rows x 128 columns of H; grid (ceil(T/32), H/128). Each thread
+// first issues the loads of the staged e_j it will combine (two 8-column
+// items, K slots each), then the shared expert's down product runs on
+// bf16 MFMA into LDS, then each thread produces 8 contiguous outputs
+// y = bf16(sum_j w_j e_j + gamma s) from its 16-byte loads, slots in order.
 
+template <int KMAX, int PD>
 __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[SR][GROUP * 2 + APAD];
+    __shared__ __align__(16) uint8_t As[2][SR][GROUP * 2 + APAD];
     __shared__ __align__(16) float Ss[SR][GROUP + 4];
     const int H = a.H, Is = a.Is, K = a.K;
     const int t0 = blockIdx.x * SR, mb = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, kq = lane >> 4;
+    // the combine items of this thread: (row, 8-column chunk) = idx, idx + 256
+    uint4 ev[2][KMAX];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = tid + 256 * it;
+        const int t = min(t0 + (idx >> 4), a.T - 1), c = idx & 15;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < K) ev[it][j] = ld16(a.stage + ((int64_t)t * K + j) * H + mb * GROUP + c * 8);
+    }
     if (Is > 0) {
         const int arow = tid >> 3, acol = (tid & 7) * 32;
-        const bool arv = t0 + arow < a.T;
-        const uint8_t *aptr =
-            reinterpret_cast<const uint8_t *>(a.hs + (int64_t)(arv ? t0 + arow : 0) * Is) + acol;
+        const int at = min(t0 + arow, a.T - 1);
+        const uint8_t *aptr = reinterpret_cast<const uint8_t *>(a.hs + (int64_t)at * Is) + acol;
         const uint8_t *wp[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
@@ -532,30 +583,42 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
         const int KB = Is / GROUP;
-        for (int kb = 0; kb < KB; ++kb) {
+        uint4 b[PD][2][4], av[PD][2];
+        auto load = [&](int kb, uint4 (&bb)[2][4], uint4 (&x)[2]) {
             const int off = kb * GROUP * 2;
-            const uint4 a0 = arv ? ld16(aptr + off) : make_uint4(0, 0, 0, 0);
-            const uint4 a1 = arv ? ld16(aptr + off + 16) : make_uint4(0, 0, 0, 0);
-            uint4 b[2][4];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) b[ct][i] = ld16(wp[ct] + off + 16 * i);
-            *reinterpret_cast<uint4 *>(&As[arow][acol]) = a0;
-            *reinterpret_cast<uint4 *>(&As[arow][acol + 16]) = a1;
-            __syncthreads();
+                for (int i = 0; i < 4; ++i) bb[ct][i] = ld16(wp[ct] + off + 16 * i);
+            x[0] = ld16(aptr + off);
+            x[1] = ld16(aptr + off + 16);
+        };
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const uint8_t *ar = &As[rt * 16 + l16][64 * kq];
+        for (int d = 0; d < PD; ++d) load(d, b[d], av[d]);
+        for (int kb0 = 0; kb0 < KB; kb0 += PD) {
+            const bool more = kb0 + PD < KB;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+            for (int d = 0; d < PD; ++d) {
+                const int kb = kb0 + d;
+                {
+                    uint8_t(*Ab)[GROUP * 2 + APAD] = As[kb & 1];
+                    *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+                    *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+                    __syncthreads();
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
-                        acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[ct][i]), acc[rt][ct]);
+                    for (int rt = 0; rt < 2; ++rt) {
+                        const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct)
+                                acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[d][ct][i]), acc[rt][ct]);
+                        }
+                    }
+                    if (more) load(kb + PD, b[d], av[d]);
                 }
             }
-            __syncthreads();
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -566,21 +629,24 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
                     Ss[rt * 16 + 4 * kq + i][32 * wave + 16 * ct + l16] = acc[rt][ct][i];
         __syncthreads();
     }
-    for (int idx = tid; idx < SR * 16; idx += 256) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = tid + 256 * it;
         const int row = idx >> 4, c = idx & 15;
         const int t = t0 + row;
         if (t >= a.T) continue;
         float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < K; ++j) {
-            const float w = a.wts[(int64_t)t * K + j];
-            const uint4 v = ld16(a.stage + ((int64_t)t * K + j) * H + mb * GROUP + c * 8);
-            const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc8[2 * i] = fmaf(w, bf16_lo(vs[i]), acc8[2 * i]);
-                acc8[2 * i + 1] = fmaf(w, bf16_hi(vs[i]), acc8[2 * i + 1]);
+        for (int j = 0; j < KMAX; ++j)
+            if (j < K) {
+                const float w = a.wts[(int64_t)t * K + j];
+                const uint32_t vs[4] = {ev[it][j].x, ev[it][j].y, ev[it][j].z, ev[it][j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc8[2 * i] = fmaf(w, bf16_lo(vs[i]), acc8[2 * i]);
+                    acc8[2 * i + 1] = fmaf(w, bf16_hi(vs[i]), acc8[2 * i + 1]);
+                }
             }
-        }
         if (Is > 0) {
             const float g = a.gamma[t];
 #pragma unroll
@@ -596,8 +662,18 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
 }
 
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(shared_down_combine_kernel, dim3((a.T + SR - 1) / SR, a.H / GROUP),
-                       dim3(256), 0, st, a);
+    const dim3 grid((a.T + SR - 1) / SR, a.H / GROUP);
+    const bool even = (a.Is / GROUP) % 2 == 0;  // Is = 0 counts as even
+    if (a.K <= 4) {
+        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<4, 2>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((shared_down_combine_kernel<4, 1>), grid, dim3(256), 0, st, a);
+    } else if (a.K <= 8) {
+        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<8, 2>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((shared_down_combine_kernel<8, 1>), grid, dim3(256), 0, st, a);
+    } else {
+        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<16, 2>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((shared_down_combine_kernel<16, 1>), grid, dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 

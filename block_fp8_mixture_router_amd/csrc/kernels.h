@@ -19,10 +19,12 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
                                const float *bias, int H, int E, uint32_t flags, float *logits,
                                hipStream_t st);
 // top-K + softmax per row; when gate_w != NULL also gamma[t] = sigmoid(gate_w . x[t])
-// packed: every logit is a plain bf16 value (no bias, bf16 rounding on)
+// packed: every logit is a plain bf16 value (no bias, bf16 rounding on);
+// qx/sx (or NULL): also write the 1x128 e4m3 quantisation of x
 hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids,
                              float *weights, const uint16_t *x, const uint16_t *gate_w, int H,
-                             float *gamma, bool packed, hipStream_t st);
+                             float *gamma, bool packed, uint8_t *qx, float *sx,
+                             hipStream_t st);
 
 // ---- decode.hip (row-at-a-time path: one persistent kernel per call)
 struct FusedArgs {
