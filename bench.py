@@ -8,13 +8,19 @@ cannot hold the working set (one layer touches 32.5 MB). The K timed steps
 are captured once in a HIP graph (the way a frame step runs) and replayed.
 
 The JSON line's `value` is the decode layer's algorithmic HBM bytes per step
-divided by the time per step, in TB/s; `us_per_layer` is that time. The same
-run also times 1024-row chunks (uniform and skewed routing) and reports FP8
-TFLOP/s, and times the CPU oracle on a bounded sample for context.
+divided by the time per step, in TB/s; `us_per_layer` is that time. The
+decode layer is one kernel launch; its own duration is also timed live with
+HIP events around eager launches on the stream it runs on, which gives the
+roofline's `achieved`. `traffic` comes from the committed rocprofv3 counter
+summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
+when the kernel sources still hash to the value recorded with it, else null.
+The same run also times 1024-row chunks (uniform and skewed routing) and
+reports FP8 TFLOP/s, and times the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -47,6 +53,64 @@ def decode_bytes(shape, rows=1, experts_touched=None) -> int:
 
 def fp8_flops(shape, rows) -> int:
     return 2 * rows * shape.top_k * 3 * shape.hidden * shape.inter
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_fp8_mixture_router_amd", "csrc")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources (the counters are void once these change)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str, src_hash: str):
+    """HBM bytes per launch from a committed counter summary, if still valid."""
+    path = os.path.join(PROFILES, name)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def kernel_time_live(step_fn, n, stream, batches=5):
+    """Average duration of one launch, from HIP events on the stream the
+    kernel runs on, each pair bracketing n back-to-back eager launches (a
+    spin kernel keeps the GPU busy while the host enqueues, so no host gap
+    lands inside a bracket). Returns (mean, min) over the batches."""
+    per = []
+    for b in range(batches):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(50e6))
+            a_ev.record(stream)
+            for i in range(n):
+                step_fn(b * n + i)
+            b_ev.record(stream)
+        torch.cuda.synchronize()
+        per.append(a_ev.elapsed_time(b_ev) / 1e3 / n)
+    return sum(per) / len(per), min(per)
+
+
+def copy_calibration(nbytes=256 << 20, reps=10):
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (run this under rocprofv3 --pmc)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
 def graph_time(step_fn, n_steps, warmup, stream):
@@ -106,7 +170,14 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--live-launches", type=int, default=200)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        torch.cuda.set_device(0)
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is benchmarked at its single-GPU shape)", file=sys.stderr)
@@ -148,11 +219,18 @@ def main():
         rec["value"] = round(gbs / 1e3, 4)
         rec["ms_per_step"] = secs / args.steps * 1e3
         rec["us_per_layer"] = round(us, 3)
-        rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                           "traffic": None,
-                           "kernel": "whole decode layer (graph of its launches)",
-                           "bytes_per_launch": nbytes}
+        # the decode layer is one kernel launch: time those launches live
+        k_avg, k_min = kernel_time_live(step, args.live_launches, stream)
+        kgbs = nbytes / k_avg / 1e9
+        traffic = measured_traffic("decode_fused_kernel.decode_1row.pmc.json", source_hash())
+        rec["roofline"] = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                           "traffic": traffic,
+                           "kernel": "moe::decode_fused_kernel (the whole layer, one launch)",
+                           "bytes_per_launch": nbytes,
+                           "kernel_us_avg": round(k_avg * 1e6, 3),
+                           "kernel_us_min_batch": round(k_min * 1e6, 3),
+                           "launches_timed": 5 * args.live_launches}
     if not args.no_chunk:
         chunk = {}
         xc = inputs.make_x(shape, 1024, seed=1, device="cuda")
@@ -192,6 +270,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))
+    rec["source_hash"] = source_hash()
     print(json.dumps(rec), flush=True)
 
 
