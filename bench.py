@@ -236,8 +236,13 @@ def main():
         xc = inputs.make_x(shape, 1024, seed=1, device="cuda")
         yc = torch.empty_like(xc)
         nrot = min(4, L)
-        for name, skew in (("chunk1024_uniform", False), ("chunk1024_skewed", True)):
-            bias = inputs.skew_bias(shape.n_experts).cuda() if skew else None
+        # the uniform and skewed chunks are HBM-bound; the concentrated one (all
+        # rows on 16 experts, ~512 rows each) is bound by the FP8 matrix cores
+        for name, bias_fn in (("chunk1024_uniform", None),
+                              ("chunk1024_skewed", inputs.skew_bias),
+                              ("chunk1024_16experts", inputs.concentrated_bias)):
+            bias = bias_fn(shape.n_experts).cuda() if bias_fn else None
+            skew = bias is not None
             ls = []
             for l in range(nrot):
                 lw = layers[l]
