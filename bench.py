@@ -3,8 +3,8 @@
 A step is one pass of the whole layer (router, activation quantisation,
 routed FP8 experts, SwiGLU, shared expert, gate, combine) on one bf16 row of
 the decode layer (H 2048, 256 experts top-8, I = Is = 512). Steps rotate over
-16 independently generated layers and rows, so the 256 MB Infinity Cache
-cannot hold the working set (one layer touches 32.5 MB). The K timed steps
+40 independently generated layers and rows (32.5 GB of weights), so the
+256 MB Infinity Cache cannot hold the working set (one layer touches 32.5 MB). The K timed steps
 are captured once in a HIP graph (the way a frame step runs) and replayed.
 
 The JSON line's `value` is the decode layer's algorithmic HBM bytes per step
@@ -14,8 +14,10 @@ HIP events around eager launches on the stream it runs on, which gives the
 roofline's `achieved`. `traffic` comes from the committed rocprofv3 counter
 summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
 when the kernel sources still hash to the value recorded with it, else null.
-The same run also times 1024-row chunks (uniform and skewed routing) and
-reports FP8 TFLOP/s, and times the CPU oracle on a bounded sample.
+The same run also times 1024-row chunks (uniform, skewed and all-on-16-experts
+routing) and reports FP8 TFLOP/s; times the per-frame stack (the 40 layers
+chained on one row with an RMS renormalisation between layers); and times
+the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -59,13 +61,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "block_fp8_mixture_router_amd", "csrc")
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources (the counters are void once these change)."""
+DECODE_SOURCES = ("decode.hip", "topk.h", "common.h", "kernels.h")
+
+
+def source_hash(files=DECODE_SOURCES) -> str:
+    """Hash of the HIP sources a kernel is built from (its counters are void
+    once these change)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(files):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -115,6 +120,7 @@ def copy_calibration(nbytes=256 << 20, reps=10):
 
 def graph_time(step_fn, n_steps, warmup, stream):
     """Capture n_steps calls in one graph; returns seconds for one replay."""
+    torch.cuda.synchronize()  # inputs were prepared on the default stream
     with torch.cuda.stream(stream):
         for i in range(warmup):
             step_fn(i)
@@ -165,7 +171,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1600)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--stack-passes", type=int, default=25)
+    ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--chunk-steps", type=int, default=16)
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -272,6 +280,28 @@ def main():
                            "hbm_tbs_algorithmic": round(cb / (cus * 1e-6) / 1e12, 3),
                            "experts_touched": touched, "algorithmic_bytes": cb}
         rec["chunk"] = chunk
+    if not args.no_stack and L >= 2:
+        # the per-frame stack: L independent decode layers chained on one row,
+        # RMS-renormalised between layers, one graph per pass
+        xs_st = [torch.empty(1, shape.hidden, dtype=torch.bfloat16, device="cuda")
+                 for _ in range(L + 1)]
+        ys_st = [torch.empty_like(xs_st[0]) for _ in range(L)]
+        xs_st[0].copy_(inputs.make_x(shape, 1, seed=7, device="cuda"))
+
+        def spass(i):
+            for l in range(L):
+                moe.forward(cfg, layers[l], xs_st[l], y=ys_st[l], workspace=ws,
+                            wstruct=wstructs[l], stream=stream)
+                moe.rms_renorm(ys_st[l], x=xs_st[l + 1], eps=1e-6, stream=stream)
+
+        print(f"[bench] stack of {L} layers: {args.stack_passes} passes", file=sys.stderr,
+              flush=True)
+        ssecs, _ = graph_time(spass, args.stack_passes, 2, stream)
+        sus = ssecs / args.stack_passes * 1e6
+        rec["stack"] = {"workload": f"stack{L}_decode", "layers": L,
+                        "us_per_pass": round(sus, 2), "us_per_layer": round(sus / L, 3),
+                        "hbm_tbs_algorithmic": round(L * nbytes / (sus * 1e-6) / 1e12, 4),
+                        "passes_timed": args.stack_passes}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))

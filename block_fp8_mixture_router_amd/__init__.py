@@ -22,7 +22,7 @@ FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
-           "moe_forward")
+           "moe_forward", "moe_rms_renorm")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +67,8 @@ def lib():
         L.moe_quant_act.restype = ctypes.c_int
         L.moe_forward.argtypes = [vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
+        L.moe_rms_renorm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -105,6 +107,16 @@ def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
     if n == 0:
         raise MoeError("moe_workspace_bytes", -2)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def rms_renorm(y, x=None, eps: float = 1e-6, stream=None):
+    """Row RMS normalisation between stacked layers: x = bf16(y / rms(y))."""
+    import torch
+    T, H = y.shape
+    if x is None:
+        x = torch.empty_like(y)
+    _check("moe_rms_renorm", lib().moe_rms_renorm(_ptr(y), T, H, eps, _ptr(x), _stream(stream)))
+    return x
 
 
 def quant_act(x, q=None, scales=None, stream=None):

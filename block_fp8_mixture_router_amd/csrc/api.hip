@@ -153,6 +153,19 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
     return MOE_OK;
 }
 
+moe_status moe_rms_renorm(const void *y, int32_t T, int32_t H, float eps, void *x,
+                          void *stream) {
+    if (T < 0 || T > MAX_ROWS || H < 128 || H > 8192 || H % 128) return MOE_E_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!y || !x) return MOE_E_NULL;
+    if (!al16(y) || !al16(x)) return MOE_E_ALIGN;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    MOE_TRY(launch_rms_renorm(static_cast<const uint16_t *>(y), T, H, eps,
+                              static_cast<uint16_t *>(x), static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void *router_w,
                      const float *router_bias, int32_t *ids, float *weights, float *logits,
                      void *workspace, size_t workspace_bytes, void *stream) {

@@ -14,6 +14,10 @@ constexpr uint32_t K_LOGITS_FP32 = 1u << 1;
 hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, float *s,
                             hipStream_t st);
 
+// ---- renorm.hip (row RMS normalisation between stacked layers)
+hipError_t launch_rms_renorm(const uint16_t *y, int T, int H, float eps, uint16_t *x,
+                             hipStream_t st);
+
 // ---- route.hip
 hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_w,
                                const float *bias, int H, int E, uint32_t flags, float *logits,

@@ -27,8 +27,9 @@
  *    MOE_E_LAUNCH reports a failed kernel launch. Faults inside kernels
  *    surface at the caller's next synchronisation.
  *  - Results are deterministic: the same inputs give the same bytes on every
- *    call. Calls keep no state between them and may run on several streams
- *    at once when their workspaces and outputs are distinct.
+ *    call. The only state kept between calls is moe_forward's bookkeeping in
+ *    the caller's workspace (see there); calls may run on several streams at
+ *    once when their workspaces and outputs are distinct.
  *
  * Supported shapes: hidden H and expert intermediate I are multiples of 128
  * with 128 <= H <= 8192 and 128 <= I <= 4096; the shared intermediate Is is a
@@ -152,6 +153,19 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * RMS renormalisation of rows, the step between the layers of a stack of
+ * decode layers (the backbone normalises each row before its MoE layer: PR
+ * #925 backbone commit summaries; here without a learned gain). Per row:
+ *   ms   = fp32(sum_h y[h]^2 / H), the squares exact and summed in fp64;
+ *   r    = 1 / sqrt(ms + eps), fp32 with correctly rounded sqrt and division;
+ *   x[h] = bf16(fp32(y[h] * r)).
+ * y, x: bf16 [T, H], H a multiple of 128 up to 8192; x may equal y (in
+ * place); 0 <= eps <= 1.
+ */
+moe_status moe_rms_renorm(const void *y, int32_t T, int32_t H, float eps, void *x,
+                          void *stream);
 
 #ifdef __cplusplus
 }

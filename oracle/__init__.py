@@ -72,6 +72,7 @@ def lib():
         L.oracle_quant_act.argtypes = [vp, i64, i64, vp, vp]
         L.oracle_route.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp]
+        L.oracle_rms_renorm.argtypes = [vp, i64, i64, ctypes.c_float, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,6 +141,15 @@ def quant_act(x):
     s = np.empty((T, C // 128), dtype=np.float32)
     lib().oracle_quant_act(_p(xa), T, C, _p(q), _p(s))
     return q, s
+
+
+def rms_renorm(y, eps: float = 1e-6):
+    """Stack renormalisation: y bf16 [T, H] -> x bf16 bits uint16 [T, H]."""
+    ya = _np(y, np.uint16)
+    T, H = ya.shape
+    x = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_rms_renorm(_p(ya), T, H, eps, _p(x))
+    return x
 
 
 def route(shape, x, router_w, router_bias=None, flags: int = 0):

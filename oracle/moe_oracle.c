@@ -169,6 +169,24 @@ void oracle_quant_act(const uint16_t *x, int64_t T, int64_t C, uint8_t *q, float
     }
 }
 
+/* ------------------------------------------------ stack renormalisation */
+
+void oracle_rms_renorm(const uint16_t *y, int64_t T, int64_t H, float eps, uint16_t *x) {
+    for (int64_t t = 0; t < T; ++t) {
+        double sum = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double v = (double)bf16_to_f32(y[t * H + h]);
+            sum += v * v;
+        }
+        float ms = (float)(sum / (double)H);
+        float r = 1.0f / sqrtf(ms + eps);
+        for (int64_t h = 0; h < H; ++h) {
+            float v = bf16_to_f32(y[t * H + h]) * r;
+            x[t * H + h] = oracle_bf16_round(v);
+        }
+    }
+}
+
 /* ----------------------------------------------------------------- router */
 
 static void route_row(const oracle_cfg *cfg, const uint16_t *xr, const uint16_t *rw,

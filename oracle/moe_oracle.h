@@ -64,6 +64,15 @@ void oracle_forward(const oracle_cfg *cfg, const oracle_weights *w,
                     const uint16_t *x, int64_t T, uint16_t *y, float *acc,
                     int32_t *ids, float *weights);
 
+/* RMS renormalisation between the layers of a decode stack (the backbone's
+ * rows are normalised before each MoE layer; the stack workload keeps only
+ * that step, with no learned gain):
+ *   ms = fp32(sum_h y[h]^2 / H), the sum of exact squares taken in fp64;
+ *   r  = 1 / sqrt(ms + eps) in fp32 (correctly rounded sqrt and division);
+ *   x[h] = bf16(fp32(y[h] * r)).
+ * y, x: bf16 [T, H]; x may equal y. */
+void oracle_rms_renorm(const uint16_t *y, int64_t T, int64_t H, float eps, uint16_t *x);
+
 /* Threads the OpenMP runtime will use (for the baseline record). */
 int oracle_num_threads(void);
 

@@ -110,6 +110,20 @@ def test_quant_and_route_refusals():
     assert L.moe_route(cb, X, 4, Q, None, S, S + 4096, None, WS, 16, None) == -4
 
 
+def test_renorm_refusals():
+    L = moe.lib()
+    Y, X = 0x20000000, 0x30000000
+    assert L.moe_rms_renorm(Y, 4, 100, ctypes.c_float(1e-6), X, None) == -2
+    assert L.moe_rms_renorm(Y, 4, 16384, ctypes.c_float(1e-6), X, None) == -2
+    assert L.moe_rms_renorm(Y, -1, 2048, ctypes.c_float(1e-6), X, None) == -2
+    assert L.moe_rms_renorm(Y, 4, 2048, ctypes.c_float(-1.0), X, None) == -2
+    assert L.moe_rms_renorm(Y, 4, 2048, ctypes.c_float(float("nan")), X, None) == -2
+    assert L.moe_rms_renorm(Y, 0, 2048, ctypes.c_float(1e-6), X, None) == 0
+    assert L.moe_rms_renorm(None, 4, 2048, ctypes.c_float(1e-6), X, None) == -1
+    assert L.moe_rms_renorm(Y + 2, 4, 2048, ctypes.c_float(1e-6), X, None) == -3
+    assert L.moe_rms_renorm(Y, 4, 2048, ctypes.c_float(1e-6), Y, None) == -5  # no device
+
+
 def test_supported_is_false_without_gpu():
     import torch
     if torch.cuda.is_available():
