@@ -102,11 +102,12 @@ def workspace_bytes(cfg: Config, max_rows: int) -> int:
 
 
 def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
+    """A zero-filled workspace (the library requires zero before first use)."""
     import torch
     n = workspace_bytes(cfg, max_rows)
     if n == 0:
         raise MoeError("moe_workspace_bytes", -2)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def rms_renorm(y, x=None, eps: float = 1e-6, stream=None):

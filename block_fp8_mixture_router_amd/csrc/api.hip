@@ -74,8 +74,8 @@ constexpr int MAX_ROWS = 65536;
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t sync, logits, ids, wts, gamma, h, hs, qx, sx, offsets, perm, tiles, n_tiles, qh, sh,
-        stage;
+    size_t sync, dlogits, dgamma, dhs, dh, logits, ids, wts, gamma, hs, qx, sx, offsets, perm,
+        tiles, n_tiles, qh, sh, stage;
     size_t total;
     int max_tiles;
 };
@@ -92,17 +92,22 @@ Layout layout_of(const moe_config *c, int T) {
                  Is = c->shared_inter;
     L.max_tiles = grouped_max_tiles(T, (int)K, (int)E);
     L.sync = take((size_t)SYNC_WORDS * 4);
-    // decode keeps DECODE_REPLICAS copies of logits, gamma, hs and h; the
-    // grouped path uses copy 0. Every size is non-decreasing in T, so a
-    // workspace sized for max_rows serves every T <= max_rows.
+    // The decode path hands logits, gamma, hs and h between workgroups as
+    // 64-bit tagged words in DECODE_REPLICAS copies (regions d*, used by it
+    // alone, so no plain value can ever be read as a tag); the grouped path
+    // keeps one plain copy of logits (fp32), gamma (fp32) and hs (bf16).
+    // Every size is non-decreasing in T, so a workspace sized for max_rows
+    // serves every T <= max_rows.
     const size_t R = DECODE_REPLICAS, td = t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS;
-    const size_t tr = t > R * td ? t : R * td;
-    L.logits = take(tr * E * 4);
+    L.dlogits = take(R * td * E * 8);
+    L.dgamma = take(R * td * 8);
+    L.dhs = take(R * td * Is * 8);
+    L.dh = take(R * td * K * I * 8);
+    L.logits = take(t * E * 4);
     L.ids = take(t * K * 4);
     L.wts = take(t * K * 4);
-    L.gamma = take(tr * 4);
-    L.h = take(R * td * K * I * 4);
-    L.hs = take(tr * Is * 2);
+    L.gamma = take(t * 4);
+    L.hs = take(t * Is * 2);
     L.qx = take(t * H);
     L.sx = take(t * (H / 128) * 4);
     L.offsets = take((E + 1) * 4);
@@ -231,7 +236,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     int32_t *ids = at<int32_t>(workspace, L.ids);
     float *wts = at<float>(workspace, L.wts);
     float *gamma = at<float>(workspace, L.gamma);
-    const bool fits = decode_fits(T, H, K, cfg->inter);
+    const bool fits = decode_fits(T, H, K, cfg->inter, shared ? cfg->shared_inter : 0);
     if ((cfg->flags & MOE_FORCE_GEMV) && !fits) return MOE_E_UNSUPPORTED;
     const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
                       (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4 && fits);
@@ -248,14 +253,14 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
         a.sh_up = static_cast<const uint16_t *>(w->sh_up);
         a.sh_down = static_cast<const uint16_t *>(w->sh_down);
         a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
-        a.logits = lg;
-        a.gamma = gamma;
-        a.hs = at<uint16_t>(workspace, L.hs);
-        a.h = at<float>(workspace, L.h);
+        a.logits = at<uint64_t>(workspace, L.dlogits);
+        a.gamma = at<uint64_t>(workspace, L.dgamma);
+        a.hs = at<uint64_t>(workspace, L.dhs);
+        a.h = at<uint64_t>(workspace, L.dh);
         a.sync = at<uint32_t>(workspace, L.sync);
         a.y = static_cast<uint16_t *>(y);
         a.nwg = device_cus();
-        if (a.nwg <= 0) return MOE_E_UNSUPPORTED;
+        if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
         MOE_TRY(launch_decode_fused(a, st));
         return MOE_OK;
     }

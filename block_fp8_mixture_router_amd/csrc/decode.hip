@@ -8,40 +8,44 @@
 // projection; PR #927, "What this changes"). On gfx950 the layer for one row
 // is purely HBM-bound (1.5 FLOP per weight byte) and latency-bound by its
 // three dependent steps, so it runs as ONE launch of one workgroup per
-// compute unit, with two grid-wide handoffs instead of kernel boundaries:
+// compute unit, with no grid-wide barrier at all:
 //
 //  A. router logits (exact fp64 sums), shared-expert gate/up rows
 //     (hs = bf16(silu(gs) * us)) and the shared gate; every load that does not
 //     depend on the routing, the phase-C shared down rows included, is issued
 //     here; every workgroup also quantises x (1x128) into LDS;
-//     -- handoff 1: logits, hs and gamma visible --
-//  B. every workgroup selects the top-K itself (wave argmax, DPP lane moves),
-//     issues the loads of its phase-C routed down rows, and streams its share
-//     of the routed gate/up rows: h = silu(g) * u;
-//     -- handoff 2: h visible --
-//  C. every workgroup re-quantises h (1x128) into LDS and owns whole output
-//     rows m: all K down rows plus the shared down row, then writes
-//     y = bf16(sum_j w_j e_j + gamma s) in slot order. No third handoff.
+//  B. every workgroup waits for the logits of its rows, selects the top-K
+//     itself (wave argmax, DPP lane moves), issues the loads of its phase-C
+//     routed down rows, and streams its share of the routed gate/up rows:
+//     h = silu(g) * u;
+//  C. every workgroup waits for h, hs and gamma, re-quantises h (1x128) into
+//     LDS and owns whole output rows m: all K down rows plus the shared down
+//     row, then writes y = bf16(sum_j w_j e_j + gamma s) in slot order.
 //
 // Work is spread over waves workgroup-major, so consecutive items land on
 // different compute units. Each lane streams 16 contiguous weight bytes per
 // load; a wave covers 1 KiB of a weight row per load.
 //
-// Handoffs: every value that crosses workgroups (logits, hs, gamma, h, the
-// flags) is written and read with device-coherent (sc1) loads and stores,
-// which bypass the per-XCD L2 for that access only; a device-scope fence
-// would instead write back or invalidate a whole L2, and a thousand of them
-// per handoff cost tens of microseconds. A producer drains its own stores
-// (s_waitcnt) before its workgroup's arrival flag is stored. Every such value
-// is stored in DECODE_REPLICAS copies and each workgroup reads copy
-// blockIdx % DECODE_REPLICAS, so no cache line is read by more than 1/8 of
-// the workgroups (one copy per XCD when workgroups are dealt round-robin).
-// Flag values are the call's generation + 1; the
-// generation word lives in the workspace and advances by 2 per call, so
-// neither an uninitialised workspace nor flags left by an earlier call (or an
-// earlier replay of a captured graph) can satisfy a wait. Waits are bounded:
-// a spin-out (workgroups not co-resident) sets an error word and the kernel
-// still finishes.
+// Cross-workgroup values carry their call's epoch. Every value one workgroup
+// hands to others (a logit, an hs or h element, gamma) is one 64-bit word:
+// the value's 32 bits and the epoch of the call that wrote it, stored and
+// loaded with device-coherent (sc1) accesses that bypass the per-XCD L2 for
+// that access only. A consumer polls the words themselves until all carry
+// the current epoch, so there is no flag, no fence and no barrier: each
+// workgroup moves on as soon as its own inputs exist. (A device-scope fence
+// would write back or invalidate a whole L2, and a flag costs an extra round
+// trip to memory after the payload's stores drain.) Each word is stored in
+// DECODE_REPLICAS copies and workgroup b reads copy b % DECODE_REPLICAS, so no
+// cache line is polled by more than 1/8 of the workgroups.
+//
+// Epochs: every workgroup keeps its own call counter in the workspace, reads
+// it at the start and writes the next value at the end; all counters advance
+// together, so all workgroups of a call agree on its epoch as long as the
+// workspace started out filled with one repeated byte. Epochs are odd, below
+// 2^30 and differ from the counter they come from, so neither such a fill nor
+// words left by an earlier call (or an earlier replay of a captured graph)
+// can satisfy a wait. Waits are bounded: a spin-out (workgroups not co-resident)
+// sets an error word and the kernel still finishes.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -75,7 +79,7 @@ __device__ __forceinline__ void decode16(uint4 q, float (&f)[16]) {
     e4m3x4_to_f32(q.w, f[12], f[13], f[14], f[15]);
 }
 
-// ------------------------------------------------------------ handoffs
+// ------------------------------------------------------ tagged handoffs
 
 template <typename T>
 __device__ __forceinline__ T ld_dev(const T *p) {
@@ -86,67 +90,56 @@ __device__ __forceinline__ void st_dev(T *p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// sync words: [0] generation, [32] error, [SYNC_FLAGS + (b * REPL + r) * nwg + w]
-// replica r of workgroup w's arrival flag at handoff b. Each workgroup writes
-// its flag into every replica and polls replica blockIdx % REPL.
-__device__ __forceinline__ void handoff(const FusedArgs &a, int b, uint32_t target) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-coherent stores are done
-    __syncthreads();
-    uint32_t *flags = a.sync + SYNC_FLAGS + b * REPL * a.nwg;
-    if (threadIdx.x < REPL) st_dev(flags + threadIdx.x * a.nwg + blockIdx.x, target);
-    if (threadIdx.x < WAVE) {
-        const uint32_t *mine = flags + (blockIdx.x % REPL) * a.nwg;
-        for (uint32_t spin = 0;; ++spin) {
-            bool ok = true;
-            for (int i = threadIdx.x; i < a.nwg; i += WAVE) ok &= ld_dev(mine + i) == target;
-            if (__all(ok)) break;
-            if (spin >= SPIN_LIMIT) {
-                if (threadIdx.x == 0) st_dev(a.sync + 32, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+// a value handed to other workgroups: its 32 bits and the call's epoch
+__device__ __forceinline__ uint64_t tagged(uint32_t bits, uint32_t epoch) {
+    return ((uint64_t)epoch << 32) | bits;
+}
+__device__ __forceinline__ bool has_epoch(uint64_t w, uint32_t epoch) {
+    return (uint32_t)(w >> 32) == epoch;
+}
+
+// sync words: [ERR_WORD] spin-out flag; [SYNC_FLAGS + b] workgroup b's call
+// counter
+constexpr int ERR_WORD = 32;
+
+// Loads the tagged words p[idx[i]], i < n (valid entries form a prefix), and
+// polls the ones that do not yet carry `epoch` until all do (bounded). The
+// words' value halves are returned in v.
+template <int N>
+__device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
+                                           const int (&idx)[N], int n, uint32_t epoch,
+                                           uint32_t (&v)[N]) {
+    uint64_t w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = i < n ? ld_dev(p + idx[i]) : tagged(0u, epoch);
+    for (uint32_t spin = 0;; ++spin) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < N; ++i) ok &= has_epoch(w[i], epoch);
+        if (ok) break;
+        if (spin >= SPIN_LIMIT) {
+            st_dev(err, 1u);
+            break;
         }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n && !has_epoch(w[i], epoch)) w[i] = ld_dev(p + idx[i]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (uint32_t)w[i];
 }
 
 // ------------------------------------------------------------- phase A
 
-// NB = 16-byte chunks of a bf16 H-row per lane (H / 512, rounded up). All of
-// an item's loads are issued before any arithmetic.
-
-// logit of (row t, expert e): exact fp64 sum of bf16 products, one rounding
+// NB = 16-byte chunks of a bf16 H-row per lane (H / 512, rounded up). An
+// item is one router logit, one shared-expert row or the shared gate of one
+// row of x; all of an item's loads are issued before any of its arithmetic,
+// and the kernel can do other work between the two.
 template <int NB>
-__device__ void router_item(const FusedArgs &a, int t, int e, int lane) {
-    const uint16_t *xr = a.x + (int64_t)t * a.H;
-    const uint16_t *wr = a.router_w + (int64_t)e * a.H;
-    const int nc8 = a.H / 8;
-    uint4 xv[NB], wv[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = lane + WAVE * i;
-        xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-        wv[i] = c < nc8 ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    double acc0 = 0.0, acc1 = 0.0;  // two independent chains
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const uint32_t xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-        const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
-            acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
-        }
-    }
-    const double acc = wave_allsum_d(acc0 + acc1);
-    if (lane < REPL) {
-        float l = (float)acc;
-        if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
-        if (a.bias) l = l + a.bias[e];
-        st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e, l);
-    }
-}
+struct ItemARegs {
+    uint4 x[NB], w0[NB], w1[NB];
+};
 
 __device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
     const uint32_t as[4] = {a.x, a.y, a.z, a.w}, bs[4] = {b.x, b.y, b.z, b.w};
@@ -158,66 +151,133 @@ __device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
     return acc;
 }
 
-// one shared-expert row n of row t: hs = bf16(silu(g) * u); loads first
+// item `it`: [0, T*E) router logits (t, e); [T*E, T*E + T*Is) shared rows
+// (t, n); then T shared gates
 template <int NB>
-struct SharedRegs {
-    uint4 x[NB], g[NB], u[NB];
-};
-
-template <int NB>
-__device__ __forceinline__ void shared_load(const FusedArgs &a, int t, int n, int lane,
-                                            SharedRegs<NB> &r) {
+__device__ __forceinline__ void itemA_load(const FusedArgs &a, int it, int lane,
+                                           ItemARegs<NB> &r) {
+    const int n_router = a.T * a.E, n_sh = a.T * a.Is, nc8 = a.H / 8;
+    int t;
+    const uint16_t *w0, *w1 = nullptr;
+    if (it < n_router) {
+        t = it / a.E;
+        w0 = a.router_w + (int64_t)(it % a.E) * a.H;
+    } else if (it < n_router + n_sh) {
+        t = (it - n_router) / a.Is;
+        const int n = (it - n_router) % a.Is;
+        w0 = a.sh_gate + (int64_t)n * a.H;
+        w1 = a.sh_up + (int64_t)n * a.H;
+    } else {
+        t = it - n_router - n_sh;
+        w0 = a.sh_gate_w;
+    }
     const uint16_t *xr = a.x + (int64_t)t * a.H;
-    const int nc8 = a.H / 8;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int c = lane + WAVE * i;
         const bool ok = c < nc8;
         r.x[i] = ok ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-        r.g[i] = ok ? ld16(a.sh_gate + (int64_t)n * a.H + c * 8) : make_uint4(0, 0, 0, 0);
-        r.u[i] = ok ? ld16(a.sh_up + (int64_t)n * a.H + c * 8) : make_uint4(0, 0, 0, 0);
+        r.w0[i] = ok ? ld16(w0 + c * 8) : make_uint4(0, 0, 0, 0);
+        r.w1[i] = ok && w1 ? ld16(w1 + c * 8) : make_uint4(0, 0, 0, 0);
     }
 }
 
 template <int NB>
-__device__ __forceinline__ void shared_compute(const FusedArgs &a, int t, int n, int lane,
-                                               const SharedRegs<NB> &r) {
-    float g = 0.0f, u = 0.0f;
+__device__ __forceinline__ void itemA_compute(const FusedArgs &a, int it, int lane,
+                                              const ItemARegs<NB> &r, uint32_t epoch) {
+    const int n_router = a.T * a.E, n_sh = a.T * a.Is;
+    if (it < n_router) {
+        // logit of (t, e): exact fp64 sum of bf16 products, one rounding
+        const int t = it / a.E, e = it % a.E;
+        double acc0 = 0.0, acc1 = 0.0;  // two independent chains
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        g = dot8_bf16_regs(r.x[i], r.g[i], g);
-        u = dot8_bf16_regs(r.x[i], r.u[i], u);
+        for (int i = 0; i < NB; ++i) {
+            const uint32_t xs[4] = {r.x[i].x, r.x[i].y, r.x[i].z, r.x[i].w};
+            const uint32_t ws[4] = {r.w0[i].x, r.w0[i].y, r.w0[i].z, r.w0[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
+                acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
+            }
+        }
+        const double acc = wave_allsum_d(acc0 + acc1);
+        if (lane < REPL) {
+            float l = (float)acc;
+            if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
+            if (a.bias) l = l + a.bias[e];
+            st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e,
+                   tagged(__float_as_uint(l), epoch));
+        }
+    } else if (it < n_router + n_sh) {
+        // shared-expert row n of row t: hs = bf16(silu(g) * u)
+        const int t = (it - n_router) / a.Is, n = (it - n_router) % a.Is;
+        float g = 0.0f, u = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            g = dot8_bf16_regs(r.x[i], r.w0[i], g);
+            u = dot8_bf16_regs(r.x[i], r.w1[i], u);
+        }
+        g = wave_allsum(g);
+        u = wave_allsum(u);
+        if (lane < REPL)
+            st_dev(a.hs + (int64_t)(lane * a.T + t) * a.Is + n,
+                   tagged(f32_to_bf16(silu(g) * u), epoch));
+    } else {
+        // shared gate of row t
+        const int t = it - n_router - n_sh;
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) z = dot8_bf16_regs(r.x[i], r.w0[i], z);
+        z = wave_allsum(z);
+        if (lane < REPL)
+            st_dev(a.gamma + lane * a.T + t,
+                   tagged(__float_as_uint(1.0f / (1.0f + expf(-z))), epoch));
     }
-    g = wave_allsum(g);
-    u = wave_allsum(u);
-    if (lane < REPL)
-        st_dev(a.hs + (int64_t)(lane * a.T + t) * a.Is + n, (uint16_t)f32_to_bf16(silu(g) * u));
-}
-
-template <int NB>
-__device__ void gamma_item(const FusedArgs &a, int t, int lane) {
-    const uint16_t *xr = a.x + (int64_t)t * a.H;
-    const int nc8 = a.H / 8;
-    uint4 xv[NB], wv[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = lane + WAVE * i;
-        xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-        wv[i] = c < nc8 ? ld16(a.sh_gate_w + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    float z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) z = dot8_bf16_regs(xv[i], wv[i], z);
-    z = wave_allsum(z);
-    if (lane < REPL) st_dev(a.gamma + lane * a.T + t, 1.0f / (1.0f + expf(-z)));
 }
 
 // ------------------------------------------------------------- phase B
+
+// top-K of row t from this workgroup's copy of the tagged logits
+template <int NL>
+__device__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
+                              int lane, int32_t *ids, float *wts, bool packed) {
+    int idx[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) idx[i] = lane + WAVE * i;
+    const int n = min(NL, max(0, (E - lane + WAVE - 1) / WAVE));
+    uint32_t bits[NL];
+    poll_words<NL>(err, lr, idx, n, epoch, bits);
+    if (packed) {
+        uint32_t k[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) k[i] = i < n ? bf16_order_key(__uint_as_float(bits[i]), idx[i]) : 0u;
+        topk_select_packed<NL>(k, K, lane, ids, wts);
+    } else {
+        float v[NL];
+        int ix[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            v[i] = i < n ? __uint_as_float(bits[i]) : -INFINITY;
+            ix[i] = i < n ? idx[i] : 0x7FFFFFFF;
+        }
+        topk_select_n<NL>(v, ix, K, lane, ids, wts);
+    }
+}
+
+__device__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
+                            int lane, int32_t *ids, float *wts, bool packed) {
+    if (E <= 64) topk_tagged_n<1>(lr, E, K, epoch, err, lane, ids, wts, packed);
+    else if (E <= 128) topk_tagged_n<2>(lr, E, K, epoch, err, lane, ids, wts, packed);
+    else if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed);
+    else if (E <= 512) topk_tagged_n<8>(lr, E, K, epoch, err, lane, ids, wts, packed);
+    else topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed);
+}
 
 // routed rows n0..n0+GU_ROWS-1 of pair p: h = silu(g) * u (fp32); loads first
 template <int NC>
 struct GateUpRegs {
     uint4 g[NC][GU_ROWS], u[NC][GU_ROWS];
+    float sg[NC], su[NC];  // block scales of each chunk's 128-column block
 };
 
 template <int NC>
@@ -226,9 +286,14 @@ __device__ __forceinline__ void gateup_load(const FusedArgs &a, int n0, int e, i
     const int H = a.H, I = a.I, nchunk = H / 16;
     const uint8_t *wg = a.w_gate + ((int64_t)e * I + n0) * H;
     const uint8_t *wu = a.w_up + ((int64_t)e * I + n0) * H;
+    const int KB = H / GROUP;
+    const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+    const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + WAVE * i;
+        r.sg[i] = c < nchunk ? sg[c / 8] : 0.0f;
+        r.su[i] = c < nchunk ? su[c / 8] : 0.0f;
 #pragma unroll
         for (int q = 0; q < GU_ROWS; ++q) {
             if (c < nchunk) {
@@ -244,10 +309,8 @@ __device__ __forceinline__ void gateup_load(const FusedArgs &a, int n0, int e, i
 template <int NC>
 __device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0, int e,
                                                const uint8_t *qx, const float *sx, int lane,
-                                               const GateUpRegs<NC> &r) {
-    const int H = a.H, I = a.I, nchunk = H / 16, KB = H / GROUP;
-    const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
-    const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+                                               const GateUpRegs<NC> &r, uint32_t epoch) {
+    const int I = a.I, nchunk = a.H / 16;
     float accg[GU_ROWS] = {}, accu[GU_ROWS] = {};
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -255,12 +318,11 @@ __device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0
         if (c < nchunk) {
             float xq[16];
             decode16(*reinterpret_cast<const uint4 *>(qx + c * 16), xq);
-            const int b = c / 8;
-            const float s = sx[b];
+            const float s = sx[c / 8];
 #pragma unroll
             for (int q = 0; q < GU_ROWS; ++q) {
-                accg[q] = fmaf(s * sg[b], dot16_fp8(xq, r.g[i][q]), accg[q]);
-                accu[q] = fmaf(s * su[b], dot16_fp8(xq, r.u[i][q]), accu[q]);
+                accg[q] = fmaf(s * r.sg[i], dot16_fp8(xq, r.g[i][q]), accg[q]);
+                accu[q] = fmaf(s * r.su[i], dot16_fp8(xq, r.u[i][q]), accu[q]);
             }
         }
     }
@@ -271,7 +333,8 @@ __device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0
         if (lane % GU_ROWS == q) hv = silu(g) * u;
     }
     if (lane < GU_ROWS * REPL)
-        st_dev(a.h + ((int64_t)(lane / GU_ROWS) * a.T * a.K + p) * I + n0 + lane % GU_ROWS, hv);
+        st_dev(a.h + ((int64_t)(lane / GU_ROWS) * a.T * a.K + p) * I + n0 + lane % GU_ROWS,
+               tagged(__float_as_uint(hv), epoch));
 }
 
 // ------------------------------------------------------------- phase C
@@ -294,8 +357,9 @@ constexpr int SD_CH = 4;  // shared down-row chunks per lane held in registers
 
 template <int KMAX, int CPL>
 struct DownRegs {
-    uint4 w[KMAX][CPL];  // routed down rows (known after routing)
-    uint4 s[SD_CH];      // shared down row (known at kernel start)
+    uint4 w[KMAX][CPL];   // routed down rows (known after routing)
+    float sd[KMAX][CPL];  // their block scales, per chunk
+    uint4 s[SD_CH];       // shared down row (known at kernel start)
 };
 
 template <int KMAX, int CPL, int LPR>
@@ -316,70 +380,39 @@ __device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int 
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (j < K) {
-            const uint8_t *row = a.w_down + ((int64_t)ids[t * K + j] * H + m) * I;
+            const int e = ids[t * K + j];
+            const uint8_t *row = a.w_down + ((int64_t)e * H + m) * I;
+            const float *sd = a.s_down + ((int64_t)e * (H / GROUP) + m / GROUP) * (I / GROUP);
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = sub + LPR * i;
                 r.w[j][i] = c < I / 16 ? ld16(row + c * 16) : make_uint4(0, 0, 0, 0);
+                r.sd[j][i] = c < I / 16 ? sd[c / 8] : 0.0f;
             }
         }
 }
 
-// hs chunks and gamma of row t for one shared down row, from this
-// workgroup's replica (written by other workgroups: device-coherent loads)
-struct HsRegs {
-    uint64_t h[SD_CH][2];
-    float gamma;
-};
-
-template <int LPR>
-__device__ __forceinline__ void hs_load(const FusedArgs &a, int t, int sub, HsRegs &r) {
-    const int rp = blockIdx.x % REPL;
-    const uint64_t *hsr =
-        reinterpret_cast<const uint64_t *>(a.hs + (int64_t)(rp * a.T + t) * a.Is);
-#pragma unroll
-    for (int i = 0; i < SD_CH; ++i) {
-        const int c = sub + LPR * i;
-        r.h[i][0] = c < a.Is / 8 ? ld_dev(hsr + 2 * c) : 0ull;
-        r.h[i][1] = c < a.Is / 8 ? ld_dev(hsr + 2 * c + 1) : 0ull;
-    }
-    r.gamma = ld_dev(a.gamma + rp * a.T + t);
-}
-
-__device__ __forceinline__ float dot8_bf16_pair(uint4 w8, uint64_t h01, uint64_t h23) {
-    const uint32_t hs[4] = {(uint32_t)h01, (uint32_t)(h01 >> 32), (uint32_t)h23,
-                            (uint32_t)(h23 >> 32)};
-    const uint32_t ws[4] = {w8.x, w8.y, w8.z, w8.w};
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc = fmaf(bf16_lo(hs[i]), bf16_lo(ws[i]), acc);
-        acc = fmaf(bf16_hi(hs[i]), bf16_hi(ws[i]), acc);
-    }
-    return acc;
-}
-
-// gamma * (shared down row m . hs[t]), reduced over the row's LPR lanes
+// gamma * (shared down row m . hs[t]), reduced over the row's LPR lanes;
+// hs and gamma were staged in LDS
 template <int KMAX, int CPL, int LPR>
 __device__ float shared_down(const FusedArgs &a, int t, int m, int sub,
-                             const DownRegs<KMAX, CPL> &r, const HsRegs &hr) {
+                             const DownRegs<KMAX, CPL> &r, const uint16_t *hs_l,
+                             const float *gam_l) {
     const int Is = a.Is;
     if (Is == 0) return 0.0f;
+    const uint16_t *hr = hs_l + t * Is;
     float sacc = 0.0f;
 #pragma unroll
     for (int i = 0; i < SD_CH; ++i) {
         const int c = sub + LPR * i;
-        if (c < Is / 8) sacc += dot8_bf16_pair(r.s[i], hr.h[i][0], hr.h[i][1]);
+        if (c < Is / 8) sacc += dot8_bf16_regs(ld16(hr + c * 8), r.s[i], 0.0f);
     }
     if (Is / 8 > LPR * SD_CH) {  // rows longer than the register copy
-        const int rp = blockIdx.x % REPL;
-        const uint64_t *hsr =
-            reinterpret_cast<const uint64_t *>(a.hs + (int64_t)(rp * a.T + t) * Is);
         const uint16_t *srow = a.sh_down + (int64_t)m * Is;
         for (int c = sub + LPR * SD_CH; c < Is / 8; c += LPR)
-            sacc += dot8_bf16_pair(ld16(srow + c * 8), ld_dev(hsr + 2 * c), ld_dev(hsr + 2 * c + 1));
+            sacc += dot8_bf16_regs(ld16(hr + c * 8), ld16(srow + c * 8), 0.0f);
     }
-    return hr.gamma * seg_sum<LPR>(sacc);
+    return gam_l[t] * seg_sum<LPR>(sacc);
 }
 
 // routed down rows and the combine: y = bf16(sum_j w_j e_j + gs), gs from
@@ -396,7 +429,6 @@ __device__ void down_compute(const FusedArgs &a, int t, int m, int sub, const ui
     for (int j = 0; j < KMAX; ++j)
         if (j < K) {
             const int p = t * K + j;
-            const float *sd = a.s_down + ((int64_t)ids[p] * (H / GROUP) + m / GROUP) * IB;
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
@@ -404,8 +436,7 @@ __device__ void down_compute(const FusedArgs &a, int t, int m, int sub, const ui
                 if (c < I / 16) {
                     float hq[16];
                     decode16(*reinterpret_cast<const uint4 *>(qh + (int64_t)p * I + c * 16), hq);
-                    const int b = c / 8;
-                    acc = fmaf(shs[p * IB + b] * sd[b], dot16_fp8(hq, r.w[j][i]), acc);
+                    acc = fmaf(shs[p * IB + c / 8] * r.sd[j][i], dot16_fp8(hq, r.w[j][i]), acc);
                 }
             }
             yacc = fmaf(wts[p], acc, yacc);
@@ -418,10 +449,10 @@ __device__ void down_compute(const FusedArgs &a, int t, int m, int sub, const ui
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
-__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I) {
+__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is) {
     LdsPlan L;
     const int P = T * K;
     L.qx = 0;
@@ -430,45 +461,83 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I) {
     L.shs = L.qh + al16i(P * I);
     L.ids = L.shs + al16i(P * (I / GROUP) * 4);
     L.wts = L.ids + al16i(P * 4);
-    L.total = L.wts + al16i(P * 4);
+    L.hs = L.wts + al16i(P * 4);
+    L.gam = L.hs + al16i(T * Is * 2);
+    L.total = L.gam + al16i(T * 4);
     return L;
 }
 
-bool decode_fits(int T, int H, int K, int I) {
-    return T >= 1 && T <= DECODE_MAX_ROWS && lds_plan(T, H, K, I).total <= 150 * 1024;
+bool decode_fits(int T, int H, int K, int I, int Is) {
+    return T >= 1 && T <= DECODE_MAX_ROWS && lds_plan(T, H, K, I, Is).total <= 150 * 1024;
 }
 
-// quantise n_groups 128-groups of fp32 or bf16 values into LDS codes/scales
-template <bool BF16>
-__device__ void quant_to_lds(const void *src, int n_groups, uint8_t *q, float *s) {
+// 1x128 quantisation of 8 values per lane (16 lanes per group) into LDS
+__device__ __forceinline__ void quant8_to_lds(const float (&f)[8], int g, int sub, uint8_t *q,
+                                              float *s) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = group16_max(amax);
+    const float sc = group_scale(amax);
+    uint2 out;
+    out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+    out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+    *reinterpret_cast<uint2 *>(q + g * GROUP + sub * 8) = out;
+    if (sub == 0) s[g] = sc;
+}
+
+// x (bf16, [T][H]) -> LDS codes and scales
+__device__ void quant_x_to_lds(const uint16_t *x, int n_groups, uint8_t *q, float *s) {
     const int sub = threadIdx.x & 15;
     for (int g = threadIdx.x >> 4; g < n_groups; g += blockDim.x >> 4) {
+        const uint4 v = ld16(x + (int64_t)g * GROUP + sub * 8);
+        const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        quant8_to_lds(f, g, sub, q, s);
+    }
+}
+
+// Phase C inputs from this workgroup's copy, waiting for each word's epoch:
+// h (fp32, re-quantised 1x128 into LDS codes and scales), hs (bf16) and
+// gamma into LDS.
+__device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint64_t *gamma,
+                              int T, int P, int I, int Is, uint32_t epoch, uint32_t *err,
+                              uint8_t *qh, float *shs, uint16_t *hs_l, float *gam_l) {
+    const int rp = blockIdx.x % REPL;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    // h: 16 lanes per 128-group, 8 words per lane
+    const uint64_t *hsrc = h + (int64_t)rp * P * I;
+    const int sub = tid & 15;
+    for (int g = tid >> 4; g < P * (I / GROUP); g += nth >> 4) {
+        int idx[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) idx[i] = g * GROUP + sub * 8 + i;
+        uint32_t bits[8];
+        poll_words<8>(err, hsrc, idx, 8, epoch, bits);
         float f[8];
-        if constexpr (BF16) {
-            const uint4 v = ld16(static_cast<const uint16_t *>(src) + (int64_t)g * GROUP + sub * 8);
-            f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-            f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-        } else {
-            // h was written by other workgroups: device-coherent loads
-            const uint64_t *p = reinterpret_cast<const uint64_t *>(
-                static_cast<const float *>(src) + (int64_t)g * GROUP + sub * 8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t v = ld_dev(p + i);
-                f[2 * i] = __uint_as_float((uint32_t)v);
-                f[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
-            }
-        }
-        float amax = 0.0f;
+        for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[i]);
+        quant8_to_lds(f, g, sub, qh, shs);
+    }
+    // hs: up to 8 words per thread per pass
+    const uint64_t *ssrc = hs + (int64_t)rp * T * Is;
+    const int n_hs = T * Is;
+    for (int base = 0; base < n_hs; base += nth * 8) {
+        int idx[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = group16_max(amax);
-        const float sc = group_scale(amax);
-        uint2 out;
-        out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
-        out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
-        *reinterpret_cast<uint2 *>(q + g * GROUP + sub * 8) = out;
-        if (sub == 0) s[g] = sc;
+        for (int i = 0; i < 8; ++i) idx[i] = base + tid + nth * i;
+        const int n = min(8, max(0, (n_hs - base - tid + nth - 1) / nth));
+        uint32_t bits[8];
+        poll_words<8>(err, ssrc, idx, n, epoch, bits);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < n) hs_l[idx[i]] = (uint16_t)bits[i];
+    }
+    if (Is > 0 && tid < T) {
+        const int idx[1] = {rp * T + tid};
+        uint32_t bits[1];
+        poll_words<1>(err, gamma, idx, 1, epoch, bits);
+        gam_l[tid] = __uint_as_float(bits[0]);
     }
 }
 
@@ -476,20 +545,26 @@ template <int NC, int KMAX, int CPL, int LPR>
 __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a.T, H = a.H, K = a.K, I = a.I, P = T * K;
-    const LdsPlan L = lds_plan(T, H, K, I);
+    const LdsPlan L = lds_plan(T, H, K, I, a.Is);
     uint8_t *qx = lds + L.qx;                                 // [T][H]
     float *sx = reinterpret_cast<float *>(lds + L.sx);        // [T][H/128]
     uint8_t *qh = lds + L.qh;                                 // [P][I]
     float *shs = reinterpret_cast<float *>(lds + L.shs);      // [P][I/128]
     int32_t *ids = reinterpret_cast<int32_t *>(lds + L.ids);  // [P]
     float *wts = reinterpret_cast<float *>(lds + L.wts);      // [P]
-    __shared__ uint32_t s_target;
+    uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Is]
+    float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nw = a.nwg * 4;
     constexpr int NB = 2 * NC;  // bf16 H-row chunks per lane
     const int gw = wave * a.nwg + blockIdx.x;  // workgroup-major wave index
-    if (threadIdx.x == 0) s_target = ld_dev(a.sync) + 1u;
+    // this call's epoch from this workgroup's call counter c: odd, below 2^30
+    // and never equal to c itself, so a workspace filled with one repeated
+    // byte (zeros included) holds no word tagged with the first epoch
+    uint32_t *counter = a.sync + SYNC_FLAGS + blockIdx.x;
+    const uint32_t epoch =
+        __builtin_amdgcn_readfirstlane((ld_dev(counter) & 0x3FFFFFFEu) + 3u);
 
     constexpr int RPP = WAVE / LPR;
     const int sub = lane % LPR, rsel = lane / LPR;
@@ -501,66 +576,54 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     // load that does not depend on the routing is issued here, including
     // this wave's first shared down row (kept in registers until phase C).
     if (gw < items && a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m_first, sub, dr);
-    const int n_router = T * a.E, n_shrows = T * a.Is, n_gamma = a.Is > 0 ? T : 0;
-    for (int it = gw; it < n_router + n_shrows + n_gamma; it += nw) {
-        if (it < n_router) {
-            router_item<NB>(a, it / a.E, it % a.E, lane);
-        } else if (it < n_router + n_shrows) {
-            const int sidx = it - n_router;
-            SharedRegs<NB> sr;
-            shared_load<NB>(a, sidx / a.Is, sidx % a.Is, lane, sr);
-            shared_compute<NB>(a, sidx / a.Is, sidx % a.Is, lane, sr);
-        } else {
-            gamma_item<NB>(a, it - n_router - n_shrows, lane);
-        }
+    const int n_items = T * a.E + (a.Is > 0 ? T * a.Is + T : 0);
+    {
+        // the first item's loads fly while this workgroup quantises x
+        ItemARegs<NB> ir;
+        if (gw < n_items) itemA_load<NB>(a, gw, lane, ir);
+        quant_x_to_lds(a.x, T * (H / GROUP), qx, sx);  // needed from phase B on
+        if (gw < n_items) itemA_compute<NB>(a, gw, lane, ir, epoch);
     }
-    quant_to_lds<true>(a.x, T * (H / GROUP), qx, sx);  // needed from phase B on
-    __syncthreads();
-    const uint32_t target = s_target;
-    handoff(a, 0, target);
-    // every workgroup has read the generation word: advance it for the next call
-    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev(a.sync, target + 1u);
+    for (int it = gw + nw; it < n_items; it += nw) {
+        ItemARegs<NB> ir;
+        itemA_load<NB>(a, it, lane, ir);
+        itemA_compute<NB>(a, it, lane, ir, epoch);
+    }
 
-    // B: top-K per row (one wave per row); issue this wave's first block of
-    // routed down rows; then the routed gate/up rows
+    // B: top-K per row (one wave per row) once its logits exist; issue this
+    // wave's first block of routed down rows; then the routed gate/up rows
     for (int t = wave; t < T; t += 4)
-        topk_row<true>(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * a.E, a.E, K, lane,
-                       ids + t * K, wts + t * K, !a.bias && !(a.flags & K_LOGITS_FP32));
+        topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * a.E, a.E, K, epoch,
+                    a.sync + ERR_WORD, lane, ids + t * K, wts + t * K,
+                    !a.bias && !(a.flags & K_LOGITS_FP32));
     __syncthreads();
-    HsRegs hr;
-    if (gw < items) {
-        down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
-        if (a.Is > 0) hs_load<LPR>(a, t_first, sub, hr);
-    }
+    if (gw < items) down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
     const int per_pair = I / GU_ROWS;
     for (int it = gw; it < P * per_pair; it += nw) {
         const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
         GateUpRegs<NC> gr;
         gateup_load<NC>(a, n0, ids[p], lane, gr);
-        gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr);
+        gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr, epoch);
     }
-    // the first item's shared-expert term needs only phase-A results
-    float gs_first = 0.0f;
-    if (gw < items) gs_first = shared_down<KMAX, CPL, LPR>(a, t_first, m_first, sub, dr, hr);
-    handoff(a, 1, target);
 
-    // C: re-quantise h, then whole output rows with the combine
-    quant_to_lds<false>(a.h + (int64_t)(blockIdx.x % REPL) * P * I, P * (I / GROUP), qh, shs);
+    // C: h (re-quantised), hs and gamma into LDS once they exist, then whole
+    // output rows with the combine
+    stage_phase_c(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, a.sync + ERR_WORD, qh, shs, hs_l,
+                  gam_l);
     __syncthreads();
     for (int it = gw; it < items; it += nw) {
         const int t = it / (H / RPP);
         const int m = (it % (H / RPP)) * RPP + rsel;
-        float gsv = gs_first;
         if (it != gw) {
-            if (a.Is > 0) {
-                down_load_shared<KMAX, CPL, LPR>(a, m, sub, dr);
-                hs_load<LPR>(a, t, sub, hr);
-            }
+            if (a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m, sub, dr);
             down_load_routed<KMAX, CPL, LPR>(a, t, m, sub, ids, dr);
-            gsv = shared_down<KMAX, CPL, LPR>(a, t, m, sub, dr, hr);
         }
+        const float gsv = shared_down<KMAX, CPL, LPR>(a, t, m, sub, dr, hs_l, gam_l);
         down_compute<KMAX, CPL, LPR>(a, t, m, sub, qh, shs, ids, wts, dr, gsv);
     }
+    // every wave has read the counter: advance it for the next call
+    __syncthreads();
+    if (threadIdx.x == 0) st_dev(counter, epoch + 1u);
 }
 
 template <int NC, int KMAX>
@@ -614,7 +677,7 @@ static void set_lds_limits() {
 }
 
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I).total;
+    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I, a.Is).total;
     if (lds > 64 * 1024) {
         static const bool once = [] {
             set_lds_limits<1>();

@@ -39,21 +39,22 @@ struct FusedArgs {
     const uint8_t *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
-    // values that cross workgroups are kept in DECODE_REPLICAS copies, so
-    // each copy is read by 1/DECODE_REPLICAS of the workgroups
-    float *logits;    // [R][T, E]
-    float *gamma;     // [R][T]
-    uint16_t *hs;     // [R][T, Is] bf16 shared-expert SwiGLU output
-    float *h;         // [R][T*K, I] routed SwiGLU output (fp32)
-    uint32_t *sync;   // generation, error, go words and arrival flags
+    // values that cross workgroups are 64-bit words (32-bit value, call
+    // epoch) kept in DECODE_REPLICAS copies, so each copy is read by
+    // 1/DECODE_REPLICAS of the workgroups
+    uint64_t *logits;  // [R][T, E] fp32 logits
+    uint64_t *gamma;   // [R][T] fp32
+    uint64_t *hs;      // [R][T, Is] bf16 shared-expert SwiGLU output
+    uint64_t *h;       // [R][T*K, I] fp32 routed SwiGLU output
+    uint32_t *sync;    // [32] spin-out flag, [SYNC_FLAGS + b] workgroup b's call counter
     uint16_t *y;      // [T, H]
     int nwg;          // workgroups = compute units (all co-resident)
 };
 constexpr int DECODE_MAX_ROWS = 16;
 constexpr int DECODE_REPLICAS = 8;
 constexpr int SYNC_FLAGS = 64;
-constexpr int SYNC_WORDS = SYNC_FLAGS + 2 * DECODE_REPLICAS * 1024;
-bool decode_fits(int T, int H, int K, int I);
+constexpr int SYNC_WORDS = SYNC_FLAGS + 1024;  // up to 1024 workgroups
+bool decode_fits(int T, int H, int K, int I, int Is);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
 
 // ---- grouped.hip (expert-grouped MFMA path)

@@ -13,23 +13,11 @@ namespace moe {
 // winning lane. +0 and -0 compare equal, as floats do.
 // COHERENT: the logits were written by other workgroups of the same kernel
 // and are read with device-coherent (sc1) loads.
-template <bool COHERENT, int NL>
-__device__ inline void topk_row_n(const float *lr, int E, int K, int lane, int32_t *ids,
-                                  float *wts) {
-    float v[NL];
-    int ix[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int e = lane + WAVE * i;
-        if (e < E) {
-            v[i] = COHERENT ? __hip_atomic_load(lr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : lr[e];
-            ix[i] = e;
-        } else {
-            v[i] = -INFINITY;
-            ix[i] = 0x7FFFFFFF;
-        }
-    }
+// Selection on values already in registers: lane l holds experts l, l + 64,
+// ... (v = -inf, ix = INT_MAX beyond E). Results (slot order) to ids/wts.
+template <int NL>
+__device__ inline void topk_select_n(float (&v)[NL], int (&ix)[NL], int K, int lane,
+                                     int32_t *ids, float *wts) {
     // odd-even transposition sort of the lane's NL entries
 #pragma unroll
     for (int r = 0; r < NL; ++r)
@@ -72,6 +60,26 @@ __device__ inline void topk_row_n(const float *lr, int E, int K, int lane, int32
     }
 }
 
+template <bool COHERENT, int NL>
+__device__ inline void topk_row_n(const float *lr, int E, int K, int lane, int32_t *ids,
+                                  float *wts) {
+    float v[NL];
+    int ix[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = lane + WAVE * i;
+        if (e < E) {
+            v[i] = COHERENT ? __hip_atomic_load(lr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : lr[e];
+            ix[i] = e;
+        } else {
+            v[i] = -INFINITY;
+            ix[i] = 0x7FFFFFFF;
+        }
+    }
+    topk_select_n<NL>(v, ix, K, lane, ids, wts);
+}
+
 // When every logit is a bf16 value (no bias, bf16 rounding on), a logit
 // and its expert index pack into one 32-bit key whose unsigned order is
 // (logit descending, expert ascending): each round is then a single wave
@@ -94,19 +102,10 @@ __device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
                    (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
-template <bool COHERENT, int NL>
-__device__ inline void topk_row_packed(const float *lr, int E, int K, int lane, int32_t *ids,
-                                       float *wts) {
-    uint32_t k[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int e = lane + WAVE * i;
-        float v = 0.0f;
-        if (e < E)
-            v = COHERENT ? __hip_atomic_load(lr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : lr[e];
-        k[i] = e < E ? bf16_order_key(v, e) : 0u;  // valid keys are never 0
-    }
+// Selection on packed keys already in registers (0 beyond E).
+template <int NL>
+__device__ inline void topk_select_packed(uint32_t (&k)[NL], int K, int lane, int32_t *ids,
+                                          float *wts) {
 #pragma unroll
     for (int r = 0; r < NL; ++r)
 #pragma unroll
@@ -140,6 +139,22 @@ __device__ inline void topk_row_packed(const float *lr, int E, int K, int lane, 
         ids[lane] = (int)(0xFFFF - (my_k & 0xFFFFu));
         wts[lane] = ex / sum;
     }
+}
+
+template <bool COHERENT, int NL>
+__device__ inline void topk_row_packed(const float *lr, int E, int K, int lane, int32_t *ids,
+                                       float *wts) {
+    uint32_t k[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = lane + WAVE * i;
+        float v = 0.0f;
+        if (e < E)
+            v = COHERENT ? __hip_atomic_load(lr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : lr[e];
+        k[i] = e < E ? bf16_order_key(v, e) : 0u;  // valid keys are never 0
+    }
+    topk_select_packed<NL>(k, K, lane, ids, wts);
 }
 
 // PACKED: the logits are plain bf16 values (see bf16_order_key).

@@ -145,10 +145,16 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
  *   gamma     = sigmoid(sh_gate_w . x);
  *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
  * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
- * workspace: >= moe_workspace_bytes(cfg, T) bytes; its contents need not be
- * initialised. The decode path (T <= 4 by default) keeps a generation word
- * and handoff flags in it between calls, so two calls that overlap in time
- * must not share a workspace; calls ordered on one stream may.
+ * workspace: >= moe_workspace_bytes(cfg, T) bytes, zero-filled once before
+ * the first moe_forward call that uses it (any single repeated byte value
+ * also works); from then on the library keeps it valid, so later calls need
+ * no clearing. The decode path (T <= 4 by default) keeps per-workgroup call
+ * counters and epoch-tagged handoff words in it between calls, so two calls
+ * that overlap in time must not share a workspace; calls ordered on one
+ * stream may. If the decode kernel's workgroups cannot all be resident at
+ * once within about 0.1 s, its bounded waits give up, the output is
+ * undefined, and the 32-bit word at byte offset 128 of the workspace is set
+ * to nonzero (it is never cleared by the library).
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,

@@ -90,6 +90,25 @@ def test_forward_deterministic_and_poison_proof():
         assert int(ws[128:132].view(torch.int32).item()) == 0
 
 
+def test_workspace_fills_and_path_mixing():
+    """A workspace filled with any one repeated byte serves the decode path,
+    and decode and grouped calls can alternate on one workspace."""
+    shape, dev, host = layer("DECODE", 0, False)
+    x1, _ = x_rows(shape, 1, seed=21)
+    x3, _ = x_rows(shape, 300, seed=22)
+    ref1, ref3 = run_forward(shape, dev, x1), run_forward(shape, dev, x3)
+    cfg = moe.config(shape)
+    for fill in (0x00, 0x01, 0x3F, 0xA5, 0xFF):
+        say(f"workspace fill {fill:#04x}")
+        ws = moe.alloc_workspace(cfg, 300)
+        ws.fill_(fill)
+        ws[128:132].zero_()  # the decode kernel's spin-out word
+        for xx, ref in ((x1, ref1), (x3, ref3), (x1, ref1), (x1, ref1), (x3, ref3), (x1, ref1)):
+            y = run_forward(shape, dev, xx, workspace=ws)
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+        assert int(ws[128:132].view(torch.int32).item()) == 0
+
+
 def test_grouped_rows_independent_of_order():
     shape, dev, host = layer("DECODE", 0, False)
     x, _ = x_rows(shape, 200, seed=6)
