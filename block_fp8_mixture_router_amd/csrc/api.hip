@@ -70,12 +70,15 @@ moe_status check_cfg(const moe_config *c) {
 }
 
 constexpr int MAX_ROWS = 65536;
+// above this many rows the router ranks bf16 MFMA scores with an error bound
+// and computes exact logits only where the bound leaves the pick undecided
+constexpr int BOUNDED_MIN_ROWS = 16;
 
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t sync, dlogits, dgamma, dhs, dh, logits, ids, wts, gamma, hs, qx, sx, offsets, perm,
-        tiles, n_tiles, qh, sh, stage;
+    size_t sync, dlogits, dgamma, dhs, dh, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
+        perm, tiles, n_tiles, qh, sh, stage;
     size_t total;
     int max_tiles;
 };
@@ -103,7 +106,8 @@ Layout layout_of(const moe_config *c, int T) {
     L.dgamma = take(R * td * 8);
     L.dhs = take(R * td * Is * 8);
     L.dh = take(R * td * K * I * 8);
-    L.logits = take(t * E * 4);
+    L.logits = take(t * E * 4);  // exact logits, or the bounded scores S
+    L.absums = take(t * E * 4);  // the bounded scores' sums of |x||w|
     L.ids = take(t * K * 4);
     L.wts = take(t * K * 4);
     L.gamma = take(t * 4);
@@ -191,8 +195,19 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
     }
     if (!current_device_ok()) return MOE_E_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float *lg = logits ? logits : at<float>(workspace, layout_of(cfg, T).logits);
     const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if (!logits && T > BOUNDED_MIN_ROWS) {
+        const Layout L = layout_of(cfg, T);
+        float *S = at<float>(workspace, L.logits), *A = at<float>(workspace, L.absums);
+        MOE_TRY(launch_route_scores(xb, T, static_cast<const uint16_t *>(router_w), cfg->hidden,
+                                    cfg->n_experts, S, A, st));
+        MOE_TRY(launch_route_topk_bounded(S, A, T, cfg->n_experts, cfg->top_k, xb,
+                                          static_cast<const uint16_t *>(router_w), router_bias,
+                                          cfg->flags, cfg->hidden, ids, weights, nullptr, nullptr,
+                                          nullptr, nullptr, st));
+        return MOE_OK;
+    }
+    float *lg = logits ? logits : at<float>(workspace, layout_of(cfg, T).logits);
     MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(router_w), router_bias,
                                 cfg->hidden, cfg->n_experts, cfg->flags, lg, st));
     MOE_TRY(launch_route_topk(lg, T, cfg->n_experts, cfg->top_k, ids, weights, nullptr, nullptr,
@@ -264,8 +279,6 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
         MOE_TRY(launch_decode_fused(a, st));
         return MOE_OK;
     }
-    MOE_TRY(launch_route_logits(xb, T, static_cast<const uint16_t *>(w->router_w),
-                                w->router_bias, H, E, cfg->flags, lg, st));
     GroupedArgs g{};
     g.T = T; g.H = H; g.E = E; g.K = K; g.I = cfg->inter; g.Is = cfg->shared_inter;
     g.x = xb;
@@ -287,12 +300,21 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     g.hs = at<uint16_t>(workspace, L.hs);
     g.stage = at<uint16_t>(workspace, L.stage);
     g.y = static_cast<uint16_t *>(y);
-    MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb,
-                              shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr, H,
-                              gamma, !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32),
-                              at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
-    MOE_TRY(launch_shared_gateup(g, st));
-    MOE_TRY(launch_group_sort(g, st));
+    const uint16_t *rw = static_cast<const uint16_t *>(w->router_w);
+    const uint16_t *gw = shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr;
+    if (T > BOUNDED_MIN_ROWS) {
+        float *A = at<float>(workspace, L.absums);
+        MOE_TRY(launch_route_scores(xb, T, rw, H, E, lg, A, st));
+        MOE_TRY(launch_route_topk_bounded(lg, A, T, E, K, xb, rw, w->router_bias, cfg->flags, H,
+                                          ids, wts, gw, gamma, at<uint8_t>(workspace, L.qx),
+                                          at<float>(workspace, L.sx), st));
+    } else {
+        MOE_TRY(launch_route_logits(xb, T, rw, w->router_bias, H, E, cfg->flags, lg, st));
+        MOE_TRY(launch_route_topk(lg, T, E, K, ids, wts, xb, gw, H, gamma,
+                                  !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32),
+                                  at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
+    }
+    MOE_TRY(launch_sort_and_shared_gateup(g, st));
     MOE_TRY(launch_grouped_gateup(g, st));
     MOE_TRY(launch_grouped_down(g, st));
     MOE_TRY(launch_shared_down_combine(g, st));

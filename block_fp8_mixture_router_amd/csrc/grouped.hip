@@ -38,44 +38,66 @@ int grouped_max_tiles(int T, int K, int E) {
 }
 
 // ------------------------------------------------------------- group sort
-// One workgroup of 1024 threads. Stable counting sort of the T*K (row,slot)
+// One workgroup of SORT_THREADS. Stable counting sort of the T*K (row, slot)
 // pairs by expert: wave w owns a contiguous segment of pairs; pass A counts
 // per (wave, expert); pass B walks the segment in order, 64 pairs at a time,
 // and ranks equal experts within the step with ballots over the key bits.
+// Both passes load SORT_BATCH steps of ids at once, so a segment costs one
+// memory round trip per batch rather than one per step. The sort runs as
+// the first workgroup of the shared-expert gate/up launch (which needs only
+// x), so its latency hides behind that kernel.
+constexpr int SORT_THREADS = 256;
+constexpr int SORT_WAVES = SORT_THREADS / 64;
+constexpr int SORT_BATCH = 8;
+constexpr int SORT_E = 1024;                       // experts supported
+constexpr int SORT_EPT = SORT_E / SORT_THREADS;    // experts per thread in the scan
 
-__global__ __launch_bounds__(1024) void group_sort_kernel(const int32_t *__restrict__ ids,
-                                                          int P, int E,
-                                                          int32_t *__restrict__ offsets,
-                                                          int32_t *__restrict__ perm,
-                                                          int32_t *__restrict__ tiles,
-                                                          int32_t *__restrict__ n_tiles) {
-    __shared__ int wbase[16][1024];
-    __shared__ int offs[1024];
-    __shared__ int scan_c[1024];
-    __shared__ int scan_t[1024];
+__device__ void group_sort_block(const GroupedArgs &a) {
+    __shared__ int wbase[SORT_WAVES][SORT_E];
+    __shared__ int offs[SORT_E];
+    __shared__ int scan_c[SORT_THREADS];
+    __shared__ int scan_t[SORT_THREADS];
+    const int P = a.T * a.K, E = a.E;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int e = tid; e < 1024; e += 1024)
-        for (int w = 0; w < 16; ++w) wbase[w][e] = 0;
+    for (int i = tid; i < SORT_WAVES * SORT_E; i += SORT_THREADS) (&wbase[0][0])[i] = 0;
     __syncthreads();
-    const int seg = (P + 15) / 16;
+    const int seg = (P + SORT_WAVES - 1) / SORT_WAVES;
     const int p_begin = wave * seg;
     const int p_end = min(P, p_begin + seg);
-    for (int p = p_begin + lane; p < p_end; p += 64) atomicAdd(&wbase[wave][ids[p]], 1);
-    __syncthreads();
-    int total = 0;
-    if (tid < E) {
-        for (int w = 0; w < 16; ++w) {
-            const int c = wbase[w][tid];
-            wbase[w][tid] = total;
-            total += c;
+    for (int p0 = p_begin; p0 < p_end; p0 += 64 * SORT_BATCH) {
+        int ev[SORT_BATCH];
+#pragma unroll
+        for (int u = 0; u < SORT_BATCH; ++u) {
+            const int p = p0 + 64 * u + lane;
+            ev[u] = p < p_end ? a.ids[p] : -1;
         }
+#pragma unroll
+        for (int u = 0; u < SORT_BATCH; ++u)
+            if (ev[u] >= 0) atomicAdd(&wbase[wave][ev[u]], 1);
     }
-    const int ntile = (total + GR - 1) / GR;
-    scan_c[tid] = total;
-    scan_t[tid] = ntile;
     __syncthreads();
-    // inclusive Hillis-Steele scans over the 1024 experts
-    for (int o = 1; o < 1024; o <<= 1) {
+    // experts [SORT_EPT * tid, +SORT_EPT): per-wave bases, totals and tiles
+    int tot[SORT_EPT], nt[SORT_EPT], csum = 0, tsum = 0;
+#pragma unroll
+    for (int k = 0; k < SORT_EPT; ++k) {
+        const int e = SORT_EPT * tid + k;
+        int total = 0;
+        if (e < E)
+            for (int w = 0; w < SORT_WAVES; ++w) {
+                const int c = wbase[w][e];
+                wbase[w][e] = total;
+                total += c;
+            }
+        tot[k] = total;
+        nt[k] = (total + GR - 1) / GR;
+        csum += total;
+        tsum += nt[k];
+    }
+    scan_c[tid] = csum;
+    scan_t[tid] = tsum;
+    __syncthreads();
+    // inclusive Hillis-Steele scans over the threads
+    for (int o = 1; o < SORT_THREADS; o <<= 1) {
         const int c = tid >= o ? scan_c[tid - o] : 0;
         const int t = tid >= o ? scan_t[tid - o] : 0;
         __syncthreads();
@@ -83,50 +105,58 @@ __global__ __launch_bounds__(1024) void group_sort_kernel(const int32_t *__restr
         scan_t[tid] += t;
         __syncthreads();
     }
-    if (tid < E) {
-        const int off = scan_c[tid] - total;
-        const int tb = scan_t[tid] - ntile;
-        offs[tid] = off;
-        offsets[tid] = off;
-        for (int i = 0; i < ntile; ++i) {
-            int32_t *tl = tiles + 4 * (tb + i);
-            tl[0] = tid;
-            tl[1] = off + i * GR;
-            tl[2] = min(GR, total - i * GR);
-            tl[3] = 0;
+    int off = scan_c[tid] - csum, tb = scan_t[tid] - tsum;
+#pragma unroll
+    for (int k = 0; k < SORT_EPT; ++k) {
+        const int e = SORT_EPT * tid + k;
+        if (e < E) {
+            offs[e] = off;
+            a.offsets[e] = off;
+            for (int i = 0; i < nt[k]; ++i) {
+                int32_t *tl = a.tiles + 4 * (tb + i);
+                tl[0] = e;
+                tl[1] = off + i * GR;
+                tl[2] = min(GR, tot[k] - i * GR);
+                tl[3] = 0;
+            }
+            if (e == E - 1) {
+                a.offsets[E] = off + tot[k];
+                *a.n_tiles = tb + nt[k];
+            }
         }
-        if (tid == E - 1) {
-            offsets[E] = scan_c[tid];
-            *n_tiles = scan_t[tid];
-        }
+        off += tot[k];
+        tb += nt[k];
     }
     __syncthreads();
     int kbits = 0;
     while ((1 << kbits) < E) ++kbits;
-    for (int p0 = p_begin; p0 < p_end; p0 += 64) {
-        const int p = p0 + lane;
-        const bool valid = p < p_end;
-        const int e = valid ? ids[p] : 0;
-        uint64_t mask = __ballot(valid);
-        for (int b = 0; b < kbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = __ballot(valid && bit);
-            mask &= bit ? bal : ~bal;
+    for (int pb = p_begin; pb < p_end; pb += 64 * SORT_BATCH) {
+        int ev[SORT_BATCH];
+#pragma unroll
+        for (int u = 0; u < SORT_BATCH; ++u) {
+            const int p = pb + 64 * u + lane;
+            ev[u] = p < p_end ? a.ids[p] : 0;
         }
-        const uint64_t below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
-        const int rank = __popcll(below);
-        const int n = __popcll(mask);
-        int base = 0;
-        if (valid) base = wbase[wave][e];
-        if (valid) perm[offs[e] + base + rank] = p;
-        if (valid && rank == 0) wbase[wave][e] = base + n;
+#pragma unroll
+        for (int u = 0; u < SORT_BATCH; ++u) {
+            const int p = pb + 64 * u + lane;
+            const bool valid = p < p_end;
+            const int e = ev[u];
+            uint64_t mask = __ballot(valid);
+            for (int b = 0; b < kbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t bal = __ballot(valid && bit);
+                mask &= bit ? bal : ~bal;
+            }
+            const uint64_t below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
+            const int rank = __popcll(below);
+            const int n = __popcll(mask);
+            int base = 0;
+            if (valid) base = wbase[wave][e];
+            if (valid) a.perm[offs[e] + base + rank] = p;
+            if (valid && rank == 0) wbase[wave][e] = base + n;
+        }
     }
-}
-
-hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(group_sort_kernel, dim3(1), dim3(1024), 0, st, a.ids, a.T * a.K, a.E,
-                       a.offsets, a.perm, a.tiles, a.n_tiles);
-    return hipGetLastError();
 }
 
 // ------------------------------------------------------- FP8 MFMA helpers
@@ -463,11 +493,11 @@ __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
 constexpr int SR = 32;  // rows per shared-expert tile
 
 template <int PD>
-__global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
+__device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
     __shared__ __align__(16) uint8_t Ash[2][SR][GROUP * 2 + APAD];
     const int H = a.H, Is = a.Is, KB = H / GROUP;
     const int snb = Is / 64;
-    const int t0 = (blockIdx.x / snb) * SR, nb = blockIdx.x % snb;
+    const int t0 = (blk / snb) * SR, nb = blk % snb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, kq = lane >> 4;
     const int arow = tid >> 3, acol = (tid & 7) * 32;  // bytes
@@ -477,7 +507,7 @@ __global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
     const uint8_t *gp = reinterpret_cast<const uint8_t *>(a.sh_gate + (int64_t)n * H) + 64 * kq;
     const uint8_t *up = reinterpret_cast<const uint8_t *>(a.sh_up + (int64_t)n * H) + 64 * kq;
     double dg[2][4] = {}, du[2][4] = {};
-    const int krot = (2 * (int)(blockIdx.x / snb)) % KB;
+    const int krot = (2 * (blk / snb)) % KB;
     uint4 bg[PD][4], bu[PD][4], av[PD][2];
     auto load = [&](int kb, uint4 (&g)[4], uint4 (&u)[4], uint4 (&x)[2]) {
         const int off = ((kb + krot) % KB) * GROUP * 2;
@@ -532,13 +562,24 @@ __global__ __launch_bounds__(256) void shared_gateup_kernel(GroupedArgs a) {
         }
 }
 
-hipError_t launch_shared_gateup(const GroupedArgs &a, hipStream_t st) {
-    if (a.Is == 0) return hipSuccess;
-    const dim3 grid(((a.T + SR - 1) / SR) * (a.Is / 64));
+// workgroup 0 sorts the pairs by expert; the others run the shared expert's
+// gate/up tiles (when the layer has one)
+template <int PD>
+__global__ __launch_bounds__(256) void sort_and_shared_gateup_kernel(GroupedArgs a) {
+    if (blockIdx.x == 0) {
+        group_sort_block(a);
+        return;
+    }
+    shared_gateup_block<PD>(a, blockIdx.x - 1);
+}
+
+hipError_t launch_sort_and_shared_gateup(const GroupedArgs &a, hipStream_t st) {
+    const int n_shared = a.Is > 0 ? ((a.T + SR - 1) / SR) * (a.Is / 64) : 0;
+    const dim3 grid(1 + n_shared);
     if ((a.H / GROUP) % 2 == 0)
-        hipLaunchKernelGGL(shared_gateup_kernel<2>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(sort_and_shared_gateup_kernel<2>, grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(shared_gateup_kernel<1>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(sort_and_shared_gateup_kernel<1>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -22,6 +22,16 @@ hipError_t launch_rms_renorm(const uint16_t *y, int T, int H, float eps, uint16_
 hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_w,
                                const float *bias, int H, int E, uint32_t flags, float *logits,
                                hipStream_t st);
+// many rows: bf16 MFMA scores S (approximate logits) and A (sums of |x||w|)
+hipError_t launch_route_scores(const uint16_t *x, int T, const uint16_t *router_w, int H, int E,
+                               float *S, float *A, hipStream_t st);
+// top-K + softmax per row from bounded scores, with exact logits for the
+// experts the bound leaves undecided; gate_w/gamma and qx/sx as below
+hipError_t launch_route_topk_bounded(const float *S, const float *A, int T, int E, int K,
+                                     const uint16_t *x, const uint16_t *router_w,
+                                     const float *bias, uint32_t flags, int H, int32_t *ids,
+                                     float *weights, const uint16_t *gate_w, float *gamma,
+                                     uint8_t *qx, float *sx, hipStream_t st);
 // top-K + softmax per row; when gate_w != NULL also gamma[t] = sigmoid(gate_w . x[t])
 // packed: every logit is a plain bf16 value (no bias, bf16 rounding on);
 // qx/sx (or NULL): also write the 1x128 e4m3 quantisation of x
@@ -82,10 +92,10 @@ struct GroupedArgs {
 };
 constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
 int grouped_max_tiles(int T, int K, int E);
-hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st);
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st);
-hipError_t launch_shared_gateup(const GroupedArgs &a, hipStream_t st);
+// the expert sort (one workgroup) and the shared expert's gate/up, one launch
+hipError_t launch_sort_and_shared_gateup(const GroupedArgs &a, hipStream_t st);
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
 
 }  // namespace moe

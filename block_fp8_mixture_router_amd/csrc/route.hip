@@ -7,12 +7,19 @@
 // move picks; each logit here is the exact sum of the exact bf16 x bf16
 // products, accumulated in fp64 and rounded once to fp32, then to bf16.
 //
-// Two logit kernels:
+// Logit kernels:
 //  - few rows (decode): one wave per (row, expert), 16-byte loads, fp64 FMA,
 //    a wave reduction; the 1 MiB router matrix streams once per row.
-//  - many rows (prompt chunks): fp64 MFMA 16x16x4 tiles; each lane streams 32
-//    contiguous bytes of its row and of its experts per 64 columns and the
-//    MFMA sums over the lanes' column slices.
+//  - many rows, every logit wanted (moe_route with a logits buffer): fp64
+//    MFMA 16x16x4 tiles; each lane streams 32 contiguous bytes of its row and
+//    of its experts per 64 columns and the MFMA sums over the lanes' column
+//    slices.
+//  - many rows, only the top-K wanted (the layer): bf16 MFMA scores S (fp32
+//    sums of the exact products) and A (the same for |x||w|), which bound
+//    the exact sum to S +- delta(A); each row's wave rules out every expert
+//    whose upper bound falls below the K-th largest lower bound and computes
+//    the exact logits (fp64) of the few that remain. The picks and weights
+//    are those of the exact logits.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -139,6 +146,119 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
     return hipGetLastError();
 }
 
+// ------------------------------------------------------ bounded scores
+
+// A workgroup owns 16 rows x 64 experts; wave w sums the 128-column blocks
+// w, w+4, ...; lane (l16, kq) supplies columns [32kq, 32kq + 32) of each
+// block of its row (A operand) and of its experts' rows (B operands), split
+// over four 16x16x32 MFMAs. Each MFMA starts from zero and its 32-product
+// partial is added in fp64, so a score carries the rounding error of one
+// 32-term fp32 sum per chunk only. A second MFMA on the sign-stripped
+// operands sums |x||w| in fp32 (chained), for the bound. The four waves'
+// partials are added in LDS in a fixed order.
+// 1-D grid: the four expert blocks of a row tile sit 8 workgroups apart, so
+// with workgroups dealt round-robin over the 8 XCDs they share one L2 and
+// the tile's rows come from memory once.
+__global__ __launch_bounds__(256) void route_scores_bf16(const uint16_t *__restrict__ x, int T,
+                                                         const uint16_t *__restrict__ rw, int H,
+                                                         int E, float *__restrict__ S,
+                                                         float *__restrict__ A) {
+    __shared__ double sp[4][4][64][4];  // [wave][expert tile][lane][element]
+    __shared__ float ap[4][4][64][4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int nE = (E + 63) / 64, nT = (T + 15) / 16;
+    // linear id L -> (row tile, expert block): L = 8 * (nE * g + eb) + r, tile = 8g + r
+    const int L = blockIdx.x, r8 = L % 8, q = L / 8;
+    const int eb = q % nE, tt = (q / nE) * 8 + r8;
+    if (tt >= nT) return;
+    const int e0 = eb * 64, t0 = tt * 16;
+    // rows and experts past the end read a valid row; their results are dropped
+    const uint16_t *xr = x + (int64_t)min(t0 + l16, T - 1) * H + 32 * kq;
+    const uint16_t *wr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wr[j] = rw + (int64_t)min(e0 + 16 * j + l16, E - 1) * H + 32 * kq;
+    double sd[4][4] = {};
+    v4f aa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aa[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    const int KB = H / GROUP;
+    uint4 xv[2][4], wv[2][4][4];
+    auto load = [&](int kb, uint4 (&xs)[4], uint4 (&ws)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] = ld16(xr + kb * GROUP + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ws[j][i] = ld16(wr[j] + kb * GROUP + 8 * i);
+    };
+    auto step = [&](const uint4 (&xs)[4], const uint4 (&ws)[4][4]) {
+        constexpr uint32_t M = 0x7FFF7FFFu;  // clears both bf16 sign bits
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v8bf af = __builtin_bit_cast(v8bf, xs[i]);
+            const v8bf aabs = __builtin_bit_cast(
+                v8bf, make_uint4(xs[i].x & M, xs[i].y & M, xs[i].z & M, xs[i].w & M));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 w = ws[j][i];
+                const v4f p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    af, __builtin_bit_cast(v8bf, w), z, 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) sd[j][k] += (double)p[k];
+                aa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    aabs, __builtin_bit_cast(v8bf, make_uint4(w.x & M, w.y & M, w.z & M, w.w & M)),
+                    aa[j], 0, 0, 0);
+            }
+        }
+    };
+    // this wave's blocks kb = wave + 4i, i < nit; two blocks of loads in flight
+    const int nit = KB > wave ? (KB - wave + 3) / 4 : 0;
+    if (nit > 0) load(wave, xv[0], wv[0]);
+    if (nit > 1) load(wave + 4, xv[1], wv[1]);
+    for (int it = 0; it < nit; it += 2) {
+        step(xv[0], wv[0]);
+        if (it + 2 < nit) load(wave + 4 * (it + 2), xv[0], wv[0]);
+        if (it + 1 < nit) {
+            step(xv[1], wv[1]);
+            if (it + 3 < nit) load(wave + 4 * (it + 3), xv[1], wv[1]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sp[wave][j][lane][i] = sd[j][i];
+            ap[wave][j][lane][i] = aa[j][i];
+        }
+    __syncthreads();
+    // wave w finishes expert tile w; element i of lane (l16, kq) = row 4kq + i
+    const int j = wave, e = e0 + 16 * j + l16;
+    if (e >= E) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * kq + i;
+        if (t >= T) continue;
+        const double sv = ((sp[0][j][lane][i] + sp[1][j][lane][i]) + sp[2][j][lane][i]) +
+                          sp[3][j][lane][i];
+        const float av = ((ap[0][j][lane][i] + ap[1][j][lane][i]) + ap[2][j][lane][i]) +
+                         ap[3][j][lane][i];
+        S[(int64_t)t * E + e] = (float)sv;
+        A[(int64_t)t * E + e] = av;
+    }
+}
+
+hipError_t launch_route_scores(const uint16_t *x, int T, const uint16_t *router_w, int H, int E,
+                               float *S, float *A, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int nE = (E + 63) / 64, nT = (T + 15) / 16;
+    const int groups = (nT + 7) / 8;  // row tiles come in groups of 8 (one per XCD)
+    hipLaunchKernelGGL(route_scores_bf16, dim3(groups * nE * 8), dim3(256), 0, st, x, T,
+                       router_w, H, E, S, A);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ top-K
 
 // One wave per row: the shared top-K routine, then (forward only) the
@@ -199,6 +319,250 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K,
                        ids, weights, x, gate_w, H, gamma, packed, qx, sx);
     return hipGetLastError();
+}
+
+// ------------------------------------------- top-K from bounded scores
+
+// How far the exact sum can lie from the stored score s, given the stored
+// |x||w| sum a. Every product is exact in fp32 (bf16 x bf16); each MFMA
+// sums 32 of them from zero with at most 31 roundings plus one for its
+// output, each of relative size at most u = 2^-23 (truncation allowed), so
+// a chunk partial errs by at most 32u/(1 - 32u) times its sum of |p|. The
+// fp64 sum of the H/32 partials adds at most (H/32 + 4) 2^-53 of the same,
+// and storing the score as fp32 adds half an fp32 ulp of |s|. a itself
+// went through at most c = 33 H/32 + 3 roundings and may fall short of
+// sum |p| by the factor (1 - c u). Products below 2^-126, which the matrix
+// cores may flush, add at most H 2^-126.
+__device__ __forceinline__ double score_delta(float s, float a, int H) {
+    const double u = 1.0 / 8388608.0;
+    const double c = 33.0 * H / 32.0 + 3.0;
+    const double chunk = 32.0 * u / (1.0 - 32.0 * u) + (H / 32.0 + 4.0) * 0x1p-53;
+    const double sum_abs = (double)a / (1.0 - c * u);
+    return chunk * sum_abs * (1.0 + 0x1p-40) + fabs((double)s) * 0x1p-24 + (double)H * 0x1p-126;
+}
+
+// Exact logit (fp64 sum of exact products, one rounding to fp32) of expert e
+// for the row held in xv (chunk c = lane + 64i of 8 bf16 per lane).
+template <int NB>
+__device__ __forceinline__ double exact_dot(const uint4 (&xv)[NB], const uint4 (&wv)[NB]) {
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const uint32_t xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t ws[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
+            acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
+        }
+    }
+    return wave_allsum_d(acc0 + acc1);
+}
+
+constexpr int EXACT_BATCH = 4;  // candidate rows fetched per round trip
+
+// One wave per row t. NL logits per lane (expert e = lane + 64i), NB 16-byte
+// chunks of the x row per lane. Writes ids/weights; with gate_w also gamma;
+// with qx also the 1x128 quantisation of x[t].
+template <int NL, int NB>
+__global__ __launch_bounds__(256) void route_topk_bounded_kernel(
+    const float *__restrict__ S, const float *__restrict__ A, int T, int E, int K,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ rw,
+    const float *__restrict__ bias, uint32_t flags, int H, int32_t *__restrict__ ids,
+    float *__restrict__ wts, const uint16_t *__restrict__ gate_w, float *__restrict__ gamma,
+    uint8_t *__restrict__ qx, float *__restrict__ sx) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= T) return;  // whole waves leave together
+    const int nc8 = H / 8;
+    const uint16_t *xr = x + (int64_t)t * H;
+    uint4 xv[NB], gv[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = lane + WAVE * i;
+        xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        gv[i] = (gate_w && c < nc8) ? ld16(gate_w + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    // intervals [lo, hi] that hold each exact logit
+    float lo[NL], hi[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = lane + WAVE * i;
+        if (e < E) {
+            const float sf = S[(int64_t)t * E + e];
+            const double sv = sf, d = score_delta(sf, A[(int64_t)t * E + e], H);
+            lo[i] = finish_logit(sv - d, bias, e, flags);
+            hi[i] = finish_logit(sv + d, bias, e, flags);
+        } else {
+            lo[i] = hi[i] = -INFINITY;
+        }
+    }
+    // LK = K-th largest lower bound; an expert with hi < LK trails K others
+    float LK;
+    {
+        float v[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) v[i] = lo[i];
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+#pragma unroll
+            for (int i = r & 1; i + 1 < NL; i += 2)
+                if (v[i + 1] > v[i]) {
+                    const float tv = v[i];
+                    v[i] = v[i + 1];
+                    v[i + 1] = tv;
+                }
+        LK = -INFINITY;
+        for (int j = 0; j < K; ++j) {
+            LK = wave_allmax(v[0]);
+            // remove one copy of the maximum (the lowest lane holding it)
+            const uint64_t holders = __ballot(v[0] == LK);
+            if (lane == (int)__builtin_ctzll(holders)) {
+#pragma unroll
+                for (int i = 0; i + 1 < NL; ++i) v[i] = v[i + 1];
+                v[NL - 1] = -INFINITY;
+            }
+        }
+    }
+    // candidates keep their logit once it is exact; the rest drop out
+    float val[NL];
+    uint64_t pending[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const bool cand = hi[i] >= LK && lane + WAVE * i < E;
+        val[i] = cand ? lo[i] : -INFINITY;
+        pending[i] = __ballot(cand && lo[i] != hi[i]);
+    }
+    // exact logits of the undecided candidates, EXACT_BATCH rows per round trip
+    for (int i0 = 0; i0 < NL; ++i0) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            if (i == i0) m = pending[i];
+        while (m) {
+            int eb[EXACT_BATCH];
+            int nb = 0;
+#pragma unroll
+            for (int b = 0; b < EXACT_BATCH; ++b) {
+                eb[b] = -1;
+                if (m) {
+                    const int l = (int)__builtin_ctzll(m);
+                    m &= m - 1;
+                    eb[b] = l + WAVE * i0;
+                    ++nb;
+                }
+            }
+            uint4 wv[EXACT_BATCH][NB];
+#pragma unroll
+            for (int b = 0; b < EXACT_BATCH; ++b) {
+                const uint16_t *wr = rw + (int64_t)(eb[b] >= 0 ? eb[b] : 0) * H;
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    const int c = lane + WAVE * i;
+                    wv[b][i] = (b < nb && c < nc8) ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < EXACT_BATCH; ++b)
+                if (b < nb) {
+                    const float l = finish_logit(exact_dot<NB>(xv, wv[b]), bias, eb[b], flags);
+                    const int owner = eb[b] - WAVE * i0;
+#pragma unroll
+                    for (int i = 0; i < NL; ++i)
+                        if (i == i0 && lane == owner) val[i] = l;
+                }
+        }
+    }
+    {
+        int ix[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) ix[i] = lane + WAVE * i < E ? lane + WAVE * i : 0x7FFFFFFF;
+        topk_select_n<NL>(val, ix, K, lane, ids + (int64_t)t * K, wts + (int64_t)t * K);
+    }
+    if (gate_w) {
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = lane + WAVE * i;
+            if (c < nc8) {
+                const uint4 b = gv[i];
+                const uint32_t av[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    z = fmaf(bf16_lo(av[k]), bf16_lo(bv[k]), z);
+                    z = fmaf(bf16_hi(av[k]), bf16_hi(bv[k]), z);
+                }
+            }
+        }
+        z = wave_allsum(z);
+        if (lane == 0) gamma[t] = 1.0f / (1.0f + expf(-z));
+    }
+    if (qx) {
+        // 16 lanes per 128-column group: chunk c = lane + 64i is in group c / 16
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = lane + WAVE * i;
+            if (WAVE * i >= nc8) break;  // wave-uniform
+            const uint4 v = xv[i];
+            float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
+            amax = group16_max(amax);
+            const float sc = group_scale(amax);
+            if (c < nc8) {
+                uint2 out;
+                out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+                out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+                *reinterpret_cast<uint2 *>(qx + (int64_t)t * H + c * 8) = out;
+                if ((c & 15) == 0) sx[(int64_t)t * (H / GROUP) + c / 16] = sc;
+            }
+        }
+    }
+}
+
+template <int NL>
+static hipError_t launch_bounded_nl(const float *S, const float *A, int T, int E, int K,
+                                    const uint16_t *x, const uint16_t *rw, const float *bias,
+                                    uint32_t flags, int H, int32_t *ids, float *wts,
+                                    const uint16_t *gate_w, float *gamma, uint8_t *qx,
+                                    float *sx, hipStream_t st) {
+    const dim3 grid((T + 3) / 4), block(256);
+    const int nb = (H / 8 + WAVE - 1) / WAVE;
+#define MOE_BOUNDED(NBV)                                                                     \
+    hipLaunchKernelGGL((route_topk_bounded_kernel<NL, NBV>), grid, block, 0, st, S, A, T, E, \
+                       K, x, rw, bias, flags, H, ids, wts, gate_w, gamma, qx, sx)
+    if (nb <= 1) MOE_BOUNDED(1);
+    else if (nb <= 2) MOE_BOUNDED(2);
+    else if (nb <= 4) MOE_BOUNDED(4);
+    else if (nb <= 8) MOE_BOUNDED(8);
+    else MOE_BOUNDED(16);
+#undef MOE_BOUNDED
+    return hipGetLastError();
+}
+
+hipError_t launch_route_topk_bounded(const float *S, const float *A, int T, int E, int K,
+                                     const uint16_t *x, const uint16_t *router_w,
+                                     const float *bias, uint32_t flags, int H, int32_t *ids,
+                                     float *weights, const uint16_t *gate_w, float *gamma,
+                                     uint8_t *qx, float *sx, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (E <= 64)
+        return launch_bounded_nl<1>(S, A, T, E, K, x, router_w, bias, flags, H, ids, weights,
+                                    gate_w, gamma, qx, sx, st);
+    if (E <= 128)
+        return launch_bounded_nl<2>(S, A, T, E, K, x, router_w, bias, flags, H, ids, weights,
+                                    gate_w, gamma, qx, sx, st);
+    if (E <= 256)
+        return launch_bounded_nl<4>(S, A, T, E, K, x, router_w, bias, flags, H, ids, weights,
+                                    gate_w, gamma, qx, sx, st);
+    if (E <= 512)
+        return launch_bounded_nl<8>(S, A, T, E, K, x, router_w, bias, flags, H, ids, weights,
+                                    gate_w, gamma, qx, sx, st);
+    return launch_bounded_nl<16>(S, A, T, E, K, x, router_w, bias, flags, H, ids, weights,
+                                 gate_w, gamma, qx, sx, st);
 }
 
 }  // namespace moe

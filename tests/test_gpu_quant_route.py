@@ -111,6 +111,49 @@ def test_route_bit_exact(shape_name, T, skewed, dup, flags):
         say(f"  hot share {share:.3f}, empty experts {256 - len(np.unique(ids))}")
 
 
+@pytest.mark.parametrize("shape_name,T,case,flags", [
+    ("TINY", 40, "dup", 0), ("DECODE", 17, "dup", 0), ("DECODE", 300, "plain", 0),
+    ("DECODE", 1024, "plain", 0), ("DECODE", 1024, "skewed", 0), ("DECODE", 1024, "dup", 0),
+    ("DECODE", 513, "plain", moe.LOGITS_FP32), ("DECODE", 200, "concentrated", 0),
+    ("DECODE", 64, "zero_router", 0), ("DECODE", 64, "tied_block", 0),
+])
+def test_route_bounded_scores_bit_exact(shape_name, T, case, flags):
+    """Without a logits buffer and above 16 rows, moe_route ranks bf16 MFMA
+    scores with an error bound and computes exact logits only for the
+    experts the bound leaves undecided. ids must equal the oracle's, and the
+    weights must equal, bit for bit, those of the path that computes every
+    logit exactly."""
+    shape = getattr(inputs, shape_name)
+    say(f"bounded route {shape_name} T={T} case={case} flags={flags}")
+    x = inputs.make_x(shape, T, seed=T + 7, device="cuda")
+    rw = inputs.make_router(shape, seed=T + 7, device="cuda")
+    bias = None
+    if case == "dup":
+        rw[9] = rw[2]
+        rw[shape.n_experts - 1] = rw[0]
+    elif case == "skewed":
+        bias = inputs.skew_bias(shape.n_experts)
+    elif case == "concentrated":
+        bias = inputs.concentrated_bias(shape.n_experts)
+    elif case == "zero_router":
+        rw.zero_()
+    elif case == "tied_block":
+        rw[16:48] = rw[16]  # 32 identical experts: exact ties decided by index
+    b = None if bias is None else bias.cuda()
+    cfg = moe.config(shape, flags)
+    ws = moe.alloc_workspace(cfg, T)
+    ids, w, _ = moe.route(cfg, x, rw, b, workspace=ws)
+    logits = torch.empty(T, shape.n_experts, dtype=torch.float32, device="cuda")
+    ids_x, w_x, _ = moe.route(cfg, x, rw, b, logits=logits)
+    torch.cuda.synchronize()
+    ido, wo, _ = oracle.route(shape, x.cpu(), rw.cpu(), bias,
+                              flags=(oracle.LOGITS_FP32 if flags & moe.LOGITS_FP32 else 0))
+    assert np.array_equal(ids.cpu().numpy(), ido)
+    assert np.array_equal(ids.cpu().numpy(), ids_x.cpu().numpy())
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_x.cpu().numpy().view(np.uint32))
+    assert np.max(np.abs(w.cpu().numpy() - wo)) <= 1e-6
+
+
 def test_route_logits_in_workspace():
     shape = inputs.DECODE
     x = inputs.make_x(shape, 20, seed=1, device="cuda")
