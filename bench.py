@@ -282,7 +282,7 @@ def main():
         rec["chunk"] = chunk
     if not args.no_stack and L >= 2:
         # the per-frame stack: L independent decode layers chained on one row,
-        # RMS-renormalised between layers, one graph per pass
+        # RMS-renormalised between layers, one graph of 2L launches per pass
         xs_st = [torch.empty(1, shape.hidden, dtype=torch.bfloat16, device="cuda")
                  for _ in range(L + 1)]
         ys_st = [torch.empty_like(xs_st[0]) for _ in range(L)]
@@ -301,6 +301,7 @@ def main():
         rec["stack"] = {"workload": f"stack{L}_decode", "layers": L,
                         "us_per_pass": round(sus, 2), "us_per_layer": round(sus / L, 3),
                         "hbm_tbs_algorithmic": round(L * nbytes / (sus * 1e-6) / 1e12, 4),
+                        "launches_per_pass": 2 * L,
                         "passes_timed": args.stack_passes}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

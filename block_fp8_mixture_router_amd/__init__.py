@@ -22,7 +22,7 @@ FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
-           "moe_forward", "moe_rms_renorm")
+           "moe_forward", "moe_rms_renorm", "moe_forward_stack")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,8 @@ def lib():
         L.moe_forward.restype = ctypes.c_int
         L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_rms_renorm.restype = ctypes.c_int
+        L.moe_forward_stack.argtypes = [vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+        L.moe_forward_stack.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -108,6 +110,30 @@ def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
     if n == 0:
         raise MoeError("moe_workspace_bytes", -2)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def layer_table(layers, device="cuda"):
+    """Device array of moe_weights structs for moe_forward_stack (the caller
+    keeps the layers' tensors alive while the table is in use)."""
+    import torch
+    rows = [[getattr(weights_struct(lw), k) or 0 for k, _ in Weights._fields_] for lw in layers]
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def forward_stack(cfg: Config, table, n_layers: int, x, y=None, ys=None, eps: float = 1e-6,
+                  workspace=None, stream=None):
+    """n_layers layers in sequence with RMS renormalisation between them, one
+    launch; table from layer_table(). Returns the last layer's output."""
+    import torch
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, max(T, 1), x.device)
+    _check("moe_forward_stack", lib().moe_forward_stack(
+        ctypes.byref(cfg), _ptr(table), n_layers, _ptr(x), T, eps, _ptr(y), _ptr(ys),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
 
 
 def rms_renorm(y, x=None, eps: float = 1e-6, stream=None):

@@ -70,6 +70,7 @@ moe_status check_cfg(const moe_config *c) {
 }
 
 constexpr int MAX_ROWS = 65536;
+constexpr int MAX_STACK_LAYERS = 4096;
 // above this many rows the router ranks bf16 MFMA scores with an error bound
 // and computes exact logits only where the bound leaves the pick undecided
 constexpr int BOUNDED_MIN_ROWS = 16;
@@ -77,7 +78,7 @@ constexpr int BOUNDED_MIN_ROWS = 16;
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t sync, dlogits, dgamma, dhs, dh, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
+    size_t sync, dlogits, dgamma, dhs, dh, dy, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
         perm, tiles, n_tiles, qh, sh, stage;
     size_t total;
     int max_tiles;
@@ -102,10 +103,12 @@ Layout layout_of(const moe_config *c, int T) {
     // Every size is non-decreasing in T, so a workspace sized for max_rows
     // serves every T <= max_rows.
     const size_t R = DECODE_REPLICAS, td = t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS;
-    L.dlogits = take(R * td * E * 8);
-    L.dgamma = take(R * td * 8);
-    L.dhs = take(R * td * Is * 8);
-    L.dh = take(R * td * K * I * 8);
+    // (two halves each: consecutive layers of a stack alternate between them)
+    L.dlogits = take(2 * R * td * E * 8);
+    L.dgamma = take(2 * R * td * 8);
+    L.dhs = take(2 * R * td * Is * 8);
+    L.dh = take(2 * R * td * K * I * 8);
+    L.dy = take(2 * R * td * H * 8);
     L.logits = take(t * E * 4);  // exact logits, or the bounded scores S
     L.absums = take(t * E * 4);  // the bounded scores' sums of |x||w|
     L.ids = take(t * K * 4);
@@ -217,6 +220,33 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
     return MOE_OK;
 }
 
+namespace {
+void fill_decode_args(FusedArgs &a, const moe_config *cfg, const moe_weights *w, const void *x,
+                      int T, void *y, void *workspace, const Layout &L) {
+    a.T = T; a.H = cfg->hidden; a.E = cfg->n_experts; a.K = cfg->top_k; a.I = cfg->inter;
+    a.Is = cfg->shared_inter;
+    a.flags = cfg->flags;
+    a.x = static_cast<const uint16_t *>(x);
+    if (w) {
+        a.router_w = static_cast<const uint16_t *>(w->router_w);
+        a.bias = w->router_bias;
+        a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+        a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+        a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
+        a.sh_up = static_cast<const uint16_t *>(w->sh_up);
+        a.sh_down = static_cast<const uint16_t *>(w->sh_down);
+        a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
+    }
+    a.logits = at<uint64_t>(workspace, L.dlogits);
+    a.gamma = at<uint64_t>(workspace, L.dgamma);
+    a.hs = at<uint64_t>(workspace, L.dhs);
+    a.h = at<uint64_t>(workspace, L.dh);
+    a.sync = at<uint32_t>(workspace, L.sync);
+    a.y = static_cast<uint16_t *>(y);
+    a.nwg = device_cus();
+}
+}  // namespace
+
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int32_t T,
                        void *y, void *workspace, size_t workspace_bytes, void *stream) {
     moe_status s = check_cfg(cfg);
@@ -257,24 +287,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                       (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4 && fits);
     if (gemv) {
         FusedArgs a{};
-        a.T = T; a.H = H; a.E = E; a.K = K; a.I = cfg->inter; a.Is = cfg->shared_inter;
-        a.flags = cfg->flags;
-        a.x = xb;
-        a.router_w = static_cast<const uint16_t *>(w->router_w);
-        a.bias = w->router_bias;
-        a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
-        a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
-        a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
-        a.sh_up = static_cast<const uint16_t *>(w->sh_up);
-        a.sh_down = static_cast<const uint16_t *>(w->sh_down);
-        a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
-        a.logits = at<uint64_t>(workspace, L.dlogits);
-        a.gamma = at<uint64_t>(workspace, L.dgamma);
-        a.hs = at<uint64_t>(workspace, L.dhs);
-        a.h = at<uint64_t>(workspace, L.dh);
-        a.sync = at<uint32_t>(workspace, L.sync);
-        a.y = static_cast<uint16_t *>(y);
-        a.nwg = device_cus();
+        fill_decode_args(a, cfg, w, x, T, y, workspace, L);
         if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
         MOE_TRY(launch_decode_fused(a, st));
         return MOE_OK;
@@ -314,11 +327,45 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                                   !w->router_bias && !(cfg->flags & MOE_LOGITS_FP32),
                                   at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
     }
-    MOE_TRY(launch_sort_and_shared_gateup(g, st));
-    MOE_TRY(launch_grouped_gateup(g, st));
+    MOE_TRY(launch_group_sort(g, st));
+    MOE_TRY(launch_expert_gateup(g, st));
     MOE_TRY(launch_grouped_down(g, st));
     MOE_TRY(launch_shared_down_combine(g, st));
     return MOE_OK;
+}
+
+moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, int32_t n_layers,
+                             const void *x, int32_t T, float eps, void *y, void *ys,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    static_assert(sizeof(LayerPtrs) == sizeof(moe_weights), "layer table layout");
+    moe_status s = check_cfg(cfg);
+    if (s != MOE_OK) return s;
+    if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_E_UNSUPPORTED;
+    if (T < 0 || n_layers < 0 || n_layers > MAX_STACK_LAYERS) return MOE_E_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;
+    if (T == 0 || n_layers == 0) return MOE_OK;
+    if (!layers || !x || !y || !workspace) return MOE_E_NULL;
+    if (!al16(x) || !al16(y) || (ys && !al16(ys)) || !al16(layers)) return MOE_E_ALIGN;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
+    const Layout L = layout_of(cfg, T);
+    if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
+    if (x == y) return MOE_E_UNSUPPORTED;
+    if (!decode_fits(T, cfg->hidden, cfg->top_k, cfg->inter, cfg->shared_inter, true))
+        return MOE_E_UNSUPPORTED;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    FusedArgs a{};
+    fill_decode_args(a, cfg, nullptr, x, T, y, workspace, L);
+    if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
+    a.layers = reinterpret_cast<const LayerPtrs *>(layers);
+    a.n_layers = n_layers;
+    a.eps = eps;
+    a.ytag = at<uint64_t>(workspace, L.dy);
+    a.ys = static_cast<uint16_t *>(ys);
+    // the one-launch stack kernel is switched off (launch_decode_stack
+    // refuses): every valid call ends here without touching the device
+    const hipError_t e = launch_decode_stack(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return MOE_E_UNSUPPORTED;
+    return e == hipSuccess ? MOE_OK : MOE_E_LAUNCH;
 }
 
 }  // extern "C"

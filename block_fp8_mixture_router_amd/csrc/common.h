@@ -174,6 +174,21 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Row RMS normalisation between stacked layers, shared by the stand-alone
+// kernel and the multi-layer decode kernel so both give the same bits: each
+// thread adds the exact squares of its 8-value chunks in element order (fp64),
+// then the wave and workgroup sums follow a fixed order; the scale is
+// 1 / sqrt(fp32(sum / H) + eps) in fp32.
+__device__ __forceinline__ double sumsq8(const float (&v)[8], double acc) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = fma((double)v[k], (double)v[k], acc);
+    return acc;
+}
+__device__ __forceinline__ float rms_scale(double sum, int H, float eps) {
+    const float ms = (float)(sum / (double)H);
+    return 1.0f / sqrtf(ms + eps);
+}
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }

@@ -43,16 +43,14 @@ int grouped_max_tiles(int T, int K, int E) {
 // per (wave, expert); pass B walks the segment in order, 64 pairs at a time,
 // and ranks equal experts within the step with ballots over the key bits.
 // Both passes load SORT_BATCH steps of ids at once, so a segment costs one
-// memory round trip per batch rather than one per step. The sort runs as
-// the first workgroup of the shared-expert gate/up launch (which needs only
-// x), so its latency hides behind that kernel.
-constexpr int SORT_THREADS = 256;
+// memory round trip per batch rather than one per step.
+constexpr int SORT_THREADS = 1024;
 constexpr int SORT_WAVES = SORT_THREADS / 64;
 constexpr int SORT_BATCH = 8;
 constexpr int SORT_E = 1024;                       // experts supported
 constexpr int SORT_EPT = SORT_E / SORT_THREADS;    // experts per thread in the scan
 
-__device__ void group_sort_block(const GroupedArgs &a) {
+__global__ __launch_bounds__(SORT_THREADS) void group_sort_kernel(GroupedArgs a) {
     __shared__ int wbase[SORT_WAVES][SORT_E];
     __shared__ int offs[SORT_E];
     __shared__ int scan_c[SORT_THREADS];
@@ -159,6 +157,11 @@ __device__ void group_sort_block(const GroupedArgs &a) {
     }
 }
 
+hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(group_sort_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------- FP8 MFMA helpers
 
 __device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
@@ -183,13 +186,13 @@ __device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
 
 // PD = K steps of loads in flight; the host picks PD dividing H / 128.
 template <int PD>
-__global__ __launch_bounds__(256, 2) void grouped_gateup_kernel(GroupedArgs a) {
+__device__ void grouped_gateup_block(const GroupedArgs &a, int blk) {
     __shared__ __align__(16) uint8_t As[2][GR][GROUP + APAD];
     __shared__ float sxs[GR][64];
     __shared__ int toks[GR];
     __shared__ float amax_part[4][GR];
     const int nbs = a.I / GROUP;
-    const int tile = blockIdx.x / nbs, nb = blockIdx.x % nbs;
+    const int tile = blk / nbs, nb = blk % nbs;
     if (tile >= *a.n_tiles) return;
     const int e = a.tiles[4 * tile], r0 = a.tiles[4 * tile + 1], nr = a.tiles[4 * tile + 2];
     const int H = a.H, I = a.I, KB = H / GROUP;
@@ -336,14 +339,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gateup_kernel(GroupedArgs a) {
     }
 }
 
-hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(a.max_tiles * (a.I / GROUP)));
-    if ((a.H / GROUP) % 2 == 0)
-        hipLaunchKernelGGL(grouped_gateup_kernel<2>, grid, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL(grouped_gateup_kernel<1>, grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-}
 
 // ----------------------------------------------------------------- down
 // grid.x = max_tiles * (H / 128). Outputs e_j in bf16, written to the
@@ -562,24 +557,25 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
         }
 }
 
-// workgroup 0 sorts the pairs by expert; the others run the shared expert's
-// gate/up tiles (when the layer has one)
+// One launch for both gate/up products: the shared expert's tiles come
+// first (they need only x and start at once; bound by L2), then the routed
+// experts' tiles (bound by HBM), so the two overlap.
 template <int PD>
-__global__ __launch_bounds__(256) void sort_and_shared_gateup_kernel(GroupedArgs a) {
-    if (blockIdx.x == 0) {
-        group_sort_block(a);
+__global__ __launch_bounds__(256, 2) void expert_gateup_kernel(GroupedArgs a, int n_shared) {
+    if ((int)blockIdx.x < n_shared) {
+        shared_gateup_block<PD>(a, blockIdx.x);
         return;
     }
-    shared_gateup_block<PD>(a, blockIdx.x - 1);
+    grouped_gateup_block<PD>(a, blockIdx.x - n_shared);
 }
 
-hipError_t launch_sort_and_shared_gateup(const GroupedArgs &a, hipStream_t st) {
+hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st) {
     const int n_shared = a.Is > 0 ? ((a.T + SR - 1) / SR) * (a.Is / 64) : 0;
-    const dim3 grid(1 + n_shared);
+    const dim3 grid((unsigned)(n_shared + a.max_tiles * (a.I / GROUP)));
     if ((a.H / GROUP) % 2 == 0)
-        hipLaunchKernelGGL(sort_and_shared_gateup_kernel<2>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(expert_gateup_kernel<2>, grid, dim3(256), 0, st, a, n_shared);
     else
-        hipLaunchKernelGGL(sort_and_shared_gateup_kernel<1>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(expert_gateup_kernel<1>, grid, dim3(256), 0, st, a, n_shared);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, flo
                             hipStream_t st);
 
 // ---- renorm.hip (row RMS normalisation between stacked layers)
+constexpr int RENORM_CHUNKS = 4;  // 16-byte chunks per thread of 256: H <= 8192
 hipError_t launch_rms_renorm(const uint16_t *y, int T, int H, float eps, uint16_t *x,
                              hipStream_t st);
 
@@ -41,6 +42,18 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *
                              hipStream_t st);
 
 // ---- decode.hip (row-at-a-time path: one persistent kernel per call)
+// one layer's weight pointers, laid out as moe_weights
+struct LayerPtrs {
+    const uint16_t *router_w;
+    const float *bias;
+    const uint8_t *w_gate;
+    const float *s_gate;
+    const uint8_t *w_up;
+    const float *s_up;
+    const uint8_t *w_down;
+    const float *s_down;
+    const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
+};
 struct FusedArgs {
     int T, H, E, K, I, Is;
     uint32_t flags;
@@ -59,13 +72,20 @@ struct FusedArgs {
     uint32_t *sync;    // [32] spin-out flag, [SYNC_FLAGS + b] workgroup b's call counter
     uint16_t *y;      // [T, H]
     int nwg;          // workgroups = compute units (all co-resident)
+    // layer stacks: n_layers layers of this shape, x_{l+1} = renorm(y_l, eps)
+    const LayerPtrs *layers;  // device array [n_layers]
+    int n_layers;
+    float eps;
+    uint64_t *ytag;   // [2][R][T, H] tagged bf16 outputs handed to the next layer
+    uint16_t *ys;     // [n_layers][T, H] every layer's output, or NULL
 };
 constexpr int DECODE_MAX_ROWS = 16;
 constexpr int DECODE_REPLICAS = 8;
 constexpr int SYNC_FLAGS = 64;
 constexpr int SYNC_WORDS = SYNC_FLAGS + 1024;  // up to 1024 workgroups
-bool decode_fits(int T, int H, int K, int I, int Is);
+bool decode_fits(int T, int H, int K, int I, int Is, bool stack = false);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
+hipError_t launch_decode_stack(const FusedArgs &a, hipStream_t st);
 
 // ---- grouped.hip (expert-grouped MFMA path)
 struct GroupedArgs {
@@ -92,10 +112,12 @@ struct GroupedArgs {
 };
 constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
 int grouped_max_tiles(int T, int K, int E);
-hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t st);
+hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st);
+// the shared expert's gate/up (when Is > 0) and the routed experts' gate/up,
+// one launch
+hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st);
-// the expert sort (one workgroup) and the shared expert's gate/up, one launch
-hipError_t launch_sort_and_shared_gateup(const GroupedArgs &a, hipStream_t st);
+
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
 
 }  // namespace moe

@@ -14,8 +14,6 @@
 
 namespace moe {
 
-constexpr int RENORM_CHUNKS = 4;  // 16-byte chunks per thread: H <= 256 * 4 * 8
-
 __global__ __launch_bounds__(256) void rms_renorm_kernel(const uint16_t *__restrict__ y, int H,
                                                          float eps, uint16_t *x) {
     __shared__ double part[4];
@@ -31,20 +29,15 @@ __global__ __launch_bounds__(256) void rms_renorm_kernel(const uint16_t *__restr
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < RENORM_CHUNKS; ++i) {
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double a = bf16_lo(w[k]), b = bf16_hi(w[k]);
-            acc += a * a;  // exact square (16 significant bits)
-            acc += b * b;
-        }
+        const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                            bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        acc = sumsq8(f, acc);  // chunks past H are zero and add nothing
     }
     acc = wave_allsum_d(acc);
     if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = acc;
     __syncthreads();  // every load of this row is done before any store (x may alias y)
     const double sum = ((part[0] + part[1]) + part[2]) + part[3];
-    const float ms = (float)(sum / (double)H);
-    const float r = 1.0f / sqrtf(ms + eps);
+    const float r = rms_scale(sum, H, eps);
     uint16_t *xr = x + row * H;
 #pragma unroll
     for (int i = 0; i < RENORM_CHUNKS; ++i) {

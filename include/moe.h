@@ -161,6 +161,34 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                        void *stream);
 
 /*
+ * A stack of n_layers layers of one shape, run on the same rows in sequence
+ * in ONE launch (the per-frame backbone: PR #925 backbone commit summaries;
+ * each of its 40 layers holds this MoE block, and rows are RMS-normalised
+ * before each). With x_0 = x:
+ *   y_l     = the layer of weights layers[l] applied to x_l (as moe_forward);
+ *   x_{l+1} = moe_rms_renorm(y_l, eps).
+ * The result equals, bit for bit, moe_forward and moe_rms_renorm called in
+ * turn (the decode path) with the same workspace.
+ * layers: DEVICE array of n_layers moe_weights structs, 16-byte aligned; the
+ *   pointers in it cannot be checked on the host and must satisfy every
+ *   rule of moe_forward (shared expert present iff cfg->shared_inter > 0);
+ * x: bf16 [T, H]; y: bf16 [T, H], the last layer's output (must not alias
+ * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL;
+ * T rows of the decode path only (MOE_E_UNSUPPORTED where its LDS plan does
+ * not fit, e.g. beyond 16 rows); cfg->flags may not force a path;
+ * 0 <= n_layers <= 4096; 0 <= eps <= 1; workspace as for moe_forward.
+ * STATUS: switched off. The arguments are checked as above (T = 0 or
+ * n_layers = 0 still returns MOE_OK); every other valid call returns
+ * MOE_E_UNSUPPORTED without touching the device, because the one-launch
+ * kernel took a GPU memory fault on its first run and the cause has not
+ * been found. Call moe_forward and moe_rms_renorm in turn instead (they can
+ * be captured into one graph).
+ */
+moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, int32_t n_layers,
+                             const void *x, int32_t T, float eps, void *y, void *ys,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * RMS renormalisation of rows, the step between the layers of a stack of
  * decode layers (the backbone normalises each row before its MoE layer: PR
  * #925 backbone commit summaries; here without a learned gain). Per row:

@@ -124,6 +124,29 @@ def test_renorm_refusals():
     assert L.moe_rms_renorm(Y, 4, 2048, ctypes.c_float(1e-6), Y, None) == -5  # no device
 
 
+def test_stack_refusals():
+    L = moe.lib()
+    c = _cfg()
+    cb = ctypes.byref(c)
+    n = moe.workspace_bytes(c, 1)
+    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    f = lambda *a: L.moe_forward_stack(*a)  # noqa: E731
+    eps = ctypes.c_float(1e-6)
+    assert f(cb, TB, 40, X, 1, eps, Y, None, WS, n, None) == -5      # no device
+    assert f(cb, TB, 0, X, 1, eps, Y, None, WS, n, None) == 0        # no layers: no-op
+    assert f(cb, TB, 40, X, 0, eps, Y, None, WS, n, None) == 0       # no rows: no-op
+    assert f(cb, None, 40, X, 1, eps, Y, None, WS, n, None) == -1
+    assert f(cb, TB, 40, None, 1, eps, Y, None, WS, n, None) == -1
+    assert f(cb, TB, -1, X, 1, eps, Y, None, WS, n, None) == -2
+    assert f(cb, TB, 40, X, 1, ctypes.c_float(-1.0), Y, None, WS, n, None) == -2
+    assert f(cb, TB, 40, X + 2, 1, eps, Y, None, WS, n, None) == -3
+    assert f(cb, TB, 40, X, 1, eps, Y, Y + 8, WS, n, None) == -3
+    assert f(cb, TB, 40, X, 1, eps, Y, None, WS, n - 1, None) == -4
+    assert f(cb, TB, 40, X, 1, eps, X, None, WS, n, None) == -5      # y aliases x
+    forced = _cfg(flags=moe.FORCE_GROUPED)
+    assert f(ctypes.byref(forced), TB, 40, X, 1, eps, Y, None, WS, n, None) == -5
+
+
 def test_supported_is_false_without_gpu():
     import torch
     if torch.cuda.is_available():
