@@ -102,16 +102,23 @@ __device__ __forceinline__ bool has_epoch(uint64_t w, uint32_t epoch) {
 // counter
 constexpr int ERR_WORD = 32;
 
-// Loads the tagged words p[idx[i]], i < n (valid entries form a prefix), and
-// polls the ones that do not yet carry `epoch` until all do (bounded). The
-// words' value halves are returned in v.
+// First loads of the tagged words p[idx[i]], i < n (valid entries form a
+// prefix; the others read as already carrying `epoch`). Nothing waits for
+// them here, so several sets can be in flight before the first is checked.
 template <int N>
-__device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
-                                           const int (&idx)[N], int n, uint32_t epoch,
-                                           uint32_t (&v)[N]) {
-    uint64_t w[N];
+__device__ __forceinline__ void poll_issue(const uint64_t *p, const int (&idx)[N], int n,
+                                           uint32_t epoch, uint64_t (&w)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) w[i] = i < n ? ld_dev(p + idx[i]) : tagged(0u, epoch);
+}
+
+// Polls the words of an earlier poll_issue that do not yet carry `epoch`
+// until all do (bounded: past SPIN_LIMIT rounds the error word is set and
+// the stale values are returned). The words' value halves go to v.
+template <int N>
+__device__ __forceinline__ void poll_finish(uint32_t *err, const uint64_t *p,
+                                            const int (&idx)[N], int n, uint32_t epoch,
+                                            uint64_t (&w)[N], uint32_t (&v)[N]) {
     for (uint32_t spin = 0;; ++spin) {
         bool ok = true;
 #pragma unroll
@@ -128,6 +135,15 @@ __device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) v[i] = (uint32_t)w[i];
+}
+
+template <int N>
+__device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
+                                           const int (&idx)[N], int n, uint32_t epoch,
+                                           uint32_t (&v)[N]) {
+    uint64_t w[N];
+    poll_issue<N>(p, idx, n, epoch, w);
+    poll_finish<N>(err, p, idx, n, epoch, w, v);
 }
 
 // ------------------------------------------------------------- phase A
@@ -505,57 +521,114 @@ __device__ __forceinline__ void quant8_to_lds(const float (&f)[8], int g, int su
     if (sub == 0) s[g] = sc;
 }
 
-// x (bf16, [T][H]) -> LDS codes and scales
-__device__ void quant_x_to_lds(const uint16_t *x, int n_groups, uint8_t *q, float *s) {
-    const int sub = threadIdx.x & 15;
-    for (int g = threadIdx.x >> 4; g < n_groups; g += blockDim.x >> 4) {
-        const uint4 v = ld16(x + (int64_t)g * GROUP + sub * 8);
-        const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-        quant8_to_lds(f, g, sub, q, s);
+// x (bf16, [T][H]) -> LDS codes and scales. Thread tid owns the 8-value
+// chunks tid + 256 k (16 lanes per 128-group); the first XQ of them are
+// loaded into registers at kernel start (x_load) and quantised later
+// (x_quant), so the quantisation waits on no memory.
+constexpr int XQ = 4;
+struct XRegs {
+    uint4 v[XQ];
+};
+
+__device__ __forceinline__ void x_load(const uint16_t *x, int n_chunks, XRegs &r) {
+#pragma unroll
+    for (int k = 0; k < XQ; ++k) {
+        const int c = threadIdx.x + blockDim.x * k;
+        r.v[k] = c < n_chunks ? ld16(x + (int64_t)c * 8) : make_uint4(0, 0, 0, 0);
     }
 }
 
+__device__ __forceinline__ void quant_chunk_to_lds(uint4 v, int c, uint8_t *q, float *s) {
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    quant8_to_lds(f, c >> 4, c & 15, q, s);
+}
+
+// chunks beyond the register copy (more than XQ per thread) are loaded here
+__device__ __forceinline__ void x_quant(const uint16_t *x, int n_chunks, const XRegs &r,
+                                        uint8_t *q, float *s) {
+#pragma unroll
+    for (int k = 0; k < XQ; ++k) {
+        const int c = threadIdx.x + blockDim.x * k;
+        if (c < n_chunks) quant_chunk_to_lds(r.v[k], c, q, s);
+    }
+    for (int c = threadIdx.x + blockDim.x * XQ; c < n_chunks; c += blockDim.x)
+        quant_chunk_to_lds(ld16(x + (int64_t)c * 8), c, q, s);
+}
+
+// h groups each 16-lane team stages per round of loads
+constexpr int STAGE_HG = 2;
+
 // Phase C inputs from this workgroup's copy, waiting for each word's epoch:
 // h (fp32, re-quantised 1x128 into LDS codes and scales), hs (bf16) and
-// gamma into LDS.
+// gamma into LDS. The first loads of hs and gamma and of the first round of
+// h all go out before any is waited for, so a workgroup pays one handoff
+// round trip here, not one per kind of value.
 __device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint64_t *gamma,
                               int T, int P, int I, int Is, uint32_t epoch, uint32_t *err,
                               uint8_t *qh, float *shs, uint16_t *hs_l, float *gam_l) {
     const int rp = blockIdx.x % REPL;
-    const int tid = threadIdx.x, nth = blockDim.x;
-    // h: 16 lanes per 128-group, 8 words per lane
-    const uint64_t *hsrc = h + (int64_t)rp * P * I;
+    const int tid = threadIdx.x, nth = blockDim.x, teams = nth >> 4, team = tid >> 4;
     const int sub = tid & 15;
-    for (int g = tid >> 4; g < P * (I / GROUP); g += nth >> 4) {
-        int idx[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) idx[i] = g * GROUP + sub * 8 + i;
-        uint32_t bits[8];
-        poll_words<8>(err, hsrc, idx, 8, epoch, bits);
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[i]);
-        quant8_to_lds(f, g, sub, qh, shs);
-    }
-    // hs: up to 8 words per thread per pass
+    const uint64_t *hsrc = h + (int64_t)rp * P * I;
     const uint64_t *ssrc = hs + (int64_t)rp * T * Is;
-    const int n_hs = T * Is;
-    for (int base = 0; base < n_hs; base += nth * 8) {
+    const int n_groups = P * (I / GROUP), n_hs = T * Is;
+
+    // hs: up to 8 words per thread per round; the first round issued now
+    int sidx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sidx[i] = tid + nth * i;
+    const int n_s0 = min(8, max(0, (n_hs - tid + nth - 1) / nth));
+    uint64_t sw[8];
+    poll_issue<8>(ssrc, sidx, n_s0, epoch, sw);
+    const int gidx[1] = {rp * T + tid};
+    const int n_g = Is > 0 && tid < T ? 1 : 0;
+    uint64_t gw[1];
+    poll_issue<1>(gamma, gidx, n_g, epoch, gw);
+
+    // h: team j of a round stages groups base + team + teams * k, k < STAGE_HG
+    for (int base = 0; base < n_groups; base += STAGE_HG * teams) {
+        int idx[8 * STAGE_HG];
+#pragma unroll
+        for (int k = 0; k < STAGE_HG; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                idx[8 * k + i] = (base + team + teams * k) * GROUP + sub * 8 + i;
+        const int nk = min(STAGE_HG, max(0, (n_groups - base - team + teams - 1) / teams));
+        uint32_t bits[8 * STAGE_HG];
+        poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
+#pragma unroll
+        for (int k = 0; k < STAGE_HG; ++k)
+            if (k < nk) {
+                float f[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[8 * k + i]);
+                quant8_to_lds(f, base + team + teams * k, sub, qh, shs);
+            }
+    }
+
+    // hs: finish the first round, then any further rounds
+    {
+        uint32_t bits[8];
+        poll_finish<8>(err, ssrc, sidx, n_s0, epoch, sw, bits);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < n_s0) hs_l[sidx[i]] = (uint16_t)bits[i];
+    }
+    for (int b = nth * 8; b < n_hs; b += nth * 8) {
         int idx[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) idx[i] = base + tid + nth * i;
-        const int n = min(8, max(0, (n_hs - base - tid + nth - 1) / nth));
+        for (int i = 0; i < 8; ++i) idx[i] = b + tid + nth * i;
+        const int n = min(8, max(0, (n_hs - b - tid + nth - 1) / nth));
         uint32_t bits[8];
         poll_words<8>(err, ssrc, idx, n, epoch, bits);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (i < n) hs_l[idx[i]] = (uint16_t)bits[i];
     }
-    if (Is > 0 && tid < T) {
-        const int idx[1] = {rp * T + tid};
+    if (n_g) {
         uint32_t bits[1];
-        poll_words<1>(err, gamma, idx, 1, epoch, bits);
+        poll_finish<1>(err, gamma, gidx, 1, epoch, gw, bits);
         gam_l[tid] = __uint_as_float(bits[0]);
     }
 }
@@ -671,6 +744,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         // awaited.
         if (gw < items && a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m_first, sub, dr);
         const int n_items = T * E + (a.Is > 0 ? T * a.Is + T : 0);
+        XRegs xr;
         {
             ItemARegs<NB> ir;
             if (gw < n_items) itemA_load_w<NB>(a, gw, lane, ir);
@@ -683,10 +757,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
                 }
             }
             if (gw < n_items) itemA_load_x<NB>(a, gw, lane, ir);
-            // the first item's loads fly while this workgroup quantises x
-            quant_x_to_lds(a.x, T * (H / GROUP), qx, sx);  // needed from phase B on
+            x_load(a.x, T * H / 8, xr);
+            // the lowest-numbered items are the router logits, the critical
+            // path: each wave hands its first item off before x is quantised
             if (gw < n_items) itemA_compute<NB>(a, gw, lane, ir, epoch);
         }
+        x_quant(a.x, T * H / 8, xr, qx, sx);  // needed from phase B on
         for (int it = gw + nw; it < n_items; it += nw) {
             ItemARegs<NB> ir;
             itemA_load_w<NB>(a, it, lane, ir);
