@@ -15,9 +15,9 @@
 //     depend on the routing, the phase-C shared down rows included, is issued
 //     here; every workgroup also quantises x (1x128) into LDS;
 //  B. every workgroup waits for the logits of its rows, selects the top-K
-//     itself (wave argmax, DPP lane moves), issues the loads of its phase-C
-//     routed down rows, and streams its share of the routed gate/up rows:
-//     h = silu(g) * u;
+//     itself (wave argmax, DPP lane moves), streams its share of the routed
+//     gate/up rows, h = silu(g) * u, and then issues the loads of its
+//     phase-C routed down rows, which arrive during the h handoff;
 //  C. every workgroup waits for h, hs and gamma, re-quantises h (1x128) into
 //     LDS and owns whole output rows m: all K down rows plus the shared down
 //     row, then writes y = bf16(sum_j w_j e_j + gamma s) in slot order.
@@ -97,6 +97,12 @@ __device__ __forceinline__ uint64_t tagged(uint32_t bits, uint32_t epoch) {
 __device__ __forceinline__ bool has_epoch(uint64_t w, uint32_t epoch) {
     return (uint32_t)(w >> 32) == epoch;
 }
+
+// this call's first epoch from a workgroup's call counter c: odd, below 2^30
+// and never equal to c itself, so a workspace filled with one repeated byte
+// (zeros included) holds no word tagged with it; layer l of a stack uses
+// epoch + 4l
+__device__ __forceinline__ uint32_t call_epoch(uint32_t c) { return (c & 0x3FFFFFFEu) + 3u; }
 
 // sync words: [ERR_WORD] spin-out flag; [SYNC_FLAGS + b] workgroup b's call
 // counter
@@ -559,6 +565,26 @@ __device__ __forceinline__ void x_quant(const uint16_t *x, int n_chunks, const X
 // h groups each 16-lane team stages per round of loads
 constexpr int STAGE_HG = 2;
 
+// 1x128 quantisation of one group held by a 16-lane team, lane `sub` holding
+// the values sub + 16 q (q < 8), into LDS codes and the group's scale
+__device__ __forceinline__ void quant8_strided_to_lds(const float (&f)[8], int g, int sub,
+                                                      uint8_t *q, float *s) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = group16_max(amax);
+    const float sc = group_scale(amax);
+    const uint32_t c0 = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+    const uint32_t c1 = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+    uint8_t *row = q + g * GROUP + sub;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        row[16 * i] = (uint8_t)(c0 >> (8 * i));
+        row[16 * (i + 4)] = (uint8_t)(c1 >> (8 * i));
+    }
+    if (sub == 0) s[g] = sc;
+}
+
 // Phase C inputs from this workgroup's copy, waiting for each word's epoch:
 // h (fp32, re-quantised 1x128 into LDS codes and scales), hs (bf16) and
 // gamma into LDS. The first loads of hs and gamma and of the first round of
@@ -586,14 +612,16 @@ __device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint6
     uint64_t gw[1];
     poll_issue<1>(gamma, gidx, n_g, epoch, gw);
 
-    // h: team j of a round stages groups base + team + teams * k, k < STAGE_HG
+    // h: team j of a round stages groups base + team + teams * k, k < STAGE_HG;
+    // lane `sub` of a team takes the words sub + 16 i of a group, so every
+    // load instruction of a team reads one whole 128-byte line
     for (int base = 0; base < n_groups; base += STAGE_HG * teams) {
         int idx[8 * STAGE_HG];
 #pragma unroll
         for (int k = 0; k < STAGE_HG; ++k)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                idx[8 * k + i] = (base + team + teams * k) * GROUP + sub * 8 + i;
+                idx[8 * k + i] = (base + team + teams * k) * GROUP + 16 * i + sub;
         const int nk = min(STAGE_HG, max(0, (n_groups - base - team + teams - 1) / teams));
         uint32_t bits[8 * STAGE_HG];
         poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
@@ -603,7 +631,7 @@ __device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint6
                 float f[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[8 * k + i]);
-                quant8_to_lds(f, base + team + teams * k, sub, qh, shs);
+                quant8_strided_to_lds(f, base + team + teams * k, sub, qh, shs);
             }
     }
 
@@ -694,13 +722,11 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     const int nw = a0.nwg * 4;
     constexpr int NB = 2 * NC;  // bf16 H-row chunks per lane
     const int gw = wave * a0.nwg + blockIdx.x;  // workgroup-major wave index
-    // this call's first epoch from this workgroup's call counter c: odd, below
-    // 2^30 and never equal to c itself, so a workspace filled with one
-    // repeated byte (zeros included) holds no word tagged with it; layer l of
-    // a stack uses epoch0 + 4l
+    // The counter's load goes out first but is waited for only after the
+    // first weight loads have been issued: it is a full device-coherent round
+    // trip, and nothing before the first tagged store needs the epoch.
     uint32_t *counter = a0.sync + SYNC_FLAGS + blockIdx.x;
-    const uint32_t epoch0 =
-        __builtin_amdgcn_readfirstlane((ld_dev(counter) & 0x3FFFFFFEu) + 3u);
+    const uint32_t cnt = ld_dev(counter);
 
     constexpr int RPP = WAVE / LPR;
     const int sub = lane % LPR, rsel = lane / LPR;
@@ -710,7 +736,6 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
 
     for (int l = 0; l < n_layers; ++l) {
         FusedArgs a = a0;
-        const uint32_t epoch = epoch0 + 4u * (uint32_t)l;
         if constexpr (STACK) {
             const LayerPtrs lw = a0.layers[l];
             a.router_w = lw.router_w;
@@ -745,10 +770,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         if (gw < items && a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m_first, sub, dr);
         const int n_items = T * E + (a.Is > 0 ? T * a.Is + T : 0);
         XRegs xr;
+        uint32_t epoch;
         {
             ItemARegs<NB> ir;
             if (gw < n_items) itemA_load_w<NB>(a, gw, lane, ir);
             if constexpr (STACK) {
+                epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt)) + 4u * (uint32_t)l;
                 if (l > 0) {
                     renorm_rows_to_lds(a0.ytag + (int64_t)((l - 1) & 1) * REPL * T * H, T, H,
                                        a0.eps, epoch - 4u, a0.sync + ERR_WORD,
@@ -758,6 +785,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
             }
             if (gw < n_items) itemA_load_x<NB>(a, gw, lane, ir);
             x_load(a.x, T * H / 8, xr);
+            if constexpr (!STACK) epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt));
             // the lowest-numbered items are the router logits, the critical
             // path: each wave hands its first item off before x is quantised
             if (gw < n_items) itemA_compute<NB>(a, gw, lane, ir, epoch);
@@ -777,7 +805,9 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
                         a.sync + ERR_WORD, lane, ids + t * K, wts + t * K,
                         !a.bias && !(a.flags & K_LOGITS_FP32));
         __syncthreads();
-        if (gw < items) down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
+        // the routed down rows are loaded only once this wave's gate/up rows
+        // are in: phase B is bandwidth-bound and h is on the critical path,
+        // while the down rows arrive during the h handoff
         const int per_pair = I / GU_ROWS;
         for (int it = gw; it < P * per_pair; it += nw) {
             const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
@@ -786,6 +816,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
             gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr,
                                epoch);
         }
+        if (gw < items) down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
 
         // C: h (re-quantised), hs and gamma into LDS once they exist, then
         // whole output rows with the combine
@@ -805,7 +836,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         __syncthreads();  // LDS is reused by the next layer
     }
     // every wave has read the counter: advance it for the next call
-    if (threadIdx.x == 0) st_dev(counter, epoch0 + 4u * (uint32_t)(n_layers - 1) + 1u);
+    if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 4u * (uint32_t)(n_layers - 1) + 1u);
 }
 
 template <int NC, int KMAX, bool STACK>
