@@ -122,10 +122,20 @@ __device__ __forceinline__ void poll_issue(const uint64_t *p, const int (&idx)[N
 // until all do (bounded: past SPIN_LIMIT rounds the error word is set and
 // the stale values are returned). The words' value halves go to v.
 template <int N>
+__device__ __forceinline__ bool all_have_epoch(const uint64_t (&w)[N], uint32_t epoch) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok &= has_epoch(w[i], epoch);
+    return ok;
+}
+
+template <int N>
 __device__ __forceinline__ void poll_finish(uint32_t *err, const uint64_t *p,
                                             const int (&idx)[N], int n, uint32_t epoch,
                                             uint64_t (&w)[N], uint32_t (&v)[N]) {
-    for (uint32_t spin = 0;; ++spin) {
+    // the first check stands outside the loop, so the wait for these words
+    // does not also wait for loads issued after them
+    if (!all_have_epoch<N>(w, epoch)) for (uint32_t spin = 0;; ++spin) {
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < N; ++i) ok &= has_epoch(w[i], epoch);
@@ -372,122 +382,182 @@ __device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0
 
 // ------------------------------------------------------------- phase C
 
-template <int WIDTH>
-__device__ __forceinline__ float seg_sum(float v) {
-    if constexpr (WIDTH == 64) return wave_allsum(v);
-    if constexpr (WIDTH == 32) return group32_sum(v);
-    if constexpr (WIDTH == 16) return group16_sum(v);
-    v += dpp_f<DPP_XOR1>(v);
-    v += dpp_f<DPP_XOR2>(v);
-    return v + dpp_f<DPP_HALF_MIRROR>(v);
-}
+// A phase-C unit is a block of MB output rows m0..m0+MB-1 of one row t of x:
+// the routed down rows of all K slots, the shared down rows and the combine.
+//
+// The routed part runs on the FP8 matrix cores. A 16x16x128 MFMA takes as A
+// the rows (slot j, row m) of two slots, 2 x MB = 16 rows of 128 codes of
+// one K block, and as B the same K block of h for all 16 slot columns (the
+// same B for every tile); only the products of slot j's rows with slot j's
+// column are kept. That is 8x the matrix work needed, on matrix cores that
+// are idle here, instead of several hundred dependent vector instructions
+// per wave with no other wave on the SIMD to hide their latency. Every MFMA
+// starts from zero and covers exactly one 128x128 weight block, so the lane
+// folds (h scale x weight block scale) into its fp32 sum per K block.
+//
+// Operand layouts of v_mfma_scale_f32_16x16x128_f8f6f4, lane = 16 kq + l16:
+// A row l16 and B column l16 hold bytes [32 kq, 32 kq + 32) of the K block;
+// D element i of a lane is row 4 kq + i, column l16.
+constexpr int MB = 8;      // output rows per phase-C unit
+constexpr int SD_CH = 2;   // shared down-row chunks (8 bf16) per thread held in registers
 
-// Output rows of row t: RPP = 64 / LPR rows per wave item, LPR lanes per
-// row, CPL 16-byte chunks per lane of one I-long down row. The weight loads
-// are split from the arithmetic so a wave can issue its first item's down
-// rows before the routed gate/up work and the second handoff.
-constexpr int SD_CH = 4;  // shared down-row chunks per lane held in registers
-
-template <int KMAX, int CPL>
+template <int KBR, int TPW>
 struct DownRegs {
-    uint4 w[KMAX][CPL];   // routed down rows (known after routing)
-    float sd[KMAX][CPL];  // their block scales, per chunk
-    uint4 s[SD_CH];       // shared down row (known at kernel start)
+    uint4 w[TPW][KBR][2];  // A operands: tile, K block, two 16-byte halves
+    float sd[TPW][KBR];    // weight block scale of this lane's D rows
+    uint4 s[SD_CH];        // shared down row chunks
 };
 
-template <int KMAX, int CPL, int LPR>
-__device__ __forceinline__ void down_load_shared(const FusedArgs &a, int m, int sub,
-                                                 DownRegs<KMAX, CPL> &r) {
-    const uint16_t *srow = a.sh_down + (int64_t)m * a.Is;
+__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// 16x16 output, K = 128 e4m3 per operand; E8M0 scales 127 = x1.
+__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// shared down rows of unit (t, m0): thread -> row m0 + tid / 32, 8-value
+// chunks tid % 32 + 32 i
+template <int KBR, int TPW>
+__device__ __forceinline__ void down_load_shared(const FusedArgs &a, int m0,
+                                                 DownRegs<KBR, TPW> &r) {
+    const int l32 = threadIdx.x & 31, nch = a.Is / 8;
+    const uint16_t *srow = a.sh_down + (int64_t)(m0 + (threadIdx.x >> 5)) * a.Is;
 #pragma unroll
     for (int i = 0; i < SD_CH; ++i) {
-        const int c = sub + LPR * i;
-        r.s[i] = c < a.Is / 8 ? ld16(srow + c * 8) : make_uint4(0, 0, 0, 0);
+        const int c = l32 + 32 * i;
+        r.s[i] = c < nch ? ld16(srow + c * 8) : make_uint4(0, 0, 0, 0);
     }
 }
 
-template <int KMAX, int CPL, int LPR>
-__device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int m, int sub,
-                                                 const int32_t *ids, DownRegs<KMAX, CPL> &r) {
-    const int H = a.H, I = a.I, K = a.K;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < K) {
-            const int e = ids[t * K + j];
-            const uint8_t *row = a.w_down + ((int64_t)e * H + m) * I;
-            const float *sd = a.s_down + ((int64_t)e * (H / GROUP) + m / GROUP) * (I / GROUP);
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = sub + LPR * i;
-                r.w[j][i] = c < I / 16 ? ld16(row + c * 16) : make_uint4(0, 0, 0, 0);
-                r.sd[j][i] = c < I / 16 ? sd[c / 8] : 0.0f;
-            }
-        }
-}
-
-// gamma * (shared down row m . hs[t]), reduced over the row's LPR lanes;
-// hs and gamma were staged in LDS
-template <int KMAX, int CPL, int LPR>
-__device__ __forceinline__ float shared_down(const FusedArgs &a, int t, int m, int sub,
-                             const DownRegs<KMAX, CPL> &r, const uint16_t *hs_l,
-                             const float *gam_l) {
-    const int Is = a.Is;
-    if (Is == 0) return 0.0f;
-    const uint16_t *hr = hs_l + t * Is;
-    float sacc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < SD_CH; ++i) {
-        const int c = sub + LPR * i;
-        if (c < Is / 8) sacc += dot8_bf16_regs(ld16(hr + c * 8), r.s[i], 0.0f);
-    }
-    if (Is / 8 > LPR * SD_CH) {  // rows longer than the register copy
-        const uint16_t *srow = a.sh_down + (int64_t)m * Is;
-        for (int c = sub + LPR * SD_CH; c < Is / 8; c += LPR)
-            sacc += dot8_bf16_regs(ld16(hr + c * 8), ld16(srow + c * 8), 0.0f);
-    }
-    return gam_l[t] * seg_sum<LPR>(sacc);
-}
-
-// routed down rows and the combine: y = bf16(sum_j w_j e_j + gs), gs from
-// shared_down
-template <int KMAX, int CPL, int LPR>
-__device__ __forceinline__ void down_compute(const FusedArgs &a, int t, int m, int sub,
-                                             const uint8_t *qh, const float *shs,
-                                             const int32_t *ids, const float *wts,
-                                             const DownRegs<KMAX, CPL> &r, float gs,
-                                             uint32_t epoch) {
+// Routed A operands and block scales of unit (t, m0) for this wave's tiles,
+// K blocks [0, KBR). Branch-free: slots past K reload slot K - 1 and K
+// blocks past the row reload the last one (the MFMA loop skips both), so the
+// loads form one straight run and a later wait on earlier loads does not
+// also wait for these.
+template <int KBR, int TPW>
+__device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int m0,
+                                                 const int32_t *ids, DownRegs<KBR, TPW> &r) {
     const int H = a.H, I = a.I, K = a.K, IB = I / GROUP;
-    // each lane sums its slots' partial products (weight applied per slot,
-    // slots in order), then one reduction over the row's lanes
-    float yacc = 0.0f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < K) {
-            const int p = t * K + j;
-            float acc = 0.0f;
+    for (int u = 0; u < TPW; ++u) {
+        const int tau = wave + 4 * u;
+        const int e = ids[t * K + min(2 * tau + (l16 >> 3), K - 1)];
+        const uint8_t *row = a.w_down + ((int64_t)e * H + m0 + (l16 & 7)) * I + 32 * kq;
+        const int es = ids[t * K + min(2 * tau + (kq >> 1), K - 1)];
+        const float *sd = a.s_down + ((int64_t)es * (H / GROUP) + m0 / GROUP) * IB;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = sub + LPR * i;
-                if (c < I / 16) {
-                    float hq[16];
-                    decode16(*reinterpret_cast<const uint4 *>(qh + (int64_t)p * I + c * 16), hq);
-                    acc = fmaf(shs[p * IB + c / 8] * r.sd[j][i], dot16_fp8(hq, r.w[j][i]), acc);
-                }
-            }
-            yacc = fmaf(wts[p], acc, yacc);
+        for (int b = 0; b < KBR; ++b) {
+            const int bc = min(b, IB - 1);
+            r.w[u][b][0] = ld16(row + bc * GROUP);
+            r.w[u][b][1] = ld16(row + bc * GROUP + 16);
+            r.sd[u][b] = sd[bc];
         }
-    yacc = seg_sum<LPR>(yacc) + gs;
-    const uint32_t yb = f32_to_bf16(yacc);
-    if (sub == 0 && a.y) a.y[(int64_t)t * H + m] = (uint16_t)yb;
-    // in a layer stack, the next layer's input row, in every copy
-    if (a.ytag && sub < REPL) st_dev(a.ytag + ((int64_t)sub * a.T + t) * H + m, tagged(yb, epoch));
+    }
+}
+
+// The unit's output: every routed slot's e_j (MFMA), the gated shared row
+// and the combine y = bf16(sum_j w_j e_j + gamma s), slots in order. ej and
+// gsl are LDS scratch ([K][MB] and [MB] fp32); hs and gamma were staged in
+// LDS. Every thread of the workgroup calls this (it has barriers).
+template <int KBR, int TPW>
+__device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
+                                          const DownRegs<KBR, TPW> &r, const uint8_t *qh,
+                                          const float *shs, const int32_t *ids,
+                                          const float *wts, const uint16_t *hs_l,
+                                          const float *gam_l, float *ej, float *gsl,
+                                          uint32_t epoch) {
+    const int H = a.H, I = a.I, K = a.K, IB = I / GROUP, Is = a.Is;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kq = lane >> 4;
+
+    // gamma * (shared down row . hs[t]): 32 lanes per row
+    if (Is > 0) {
+        const uint16_t *hr = hs_l + t * Is;
+        const uint16_t *srow = a.sh_down + (int64_t)(m0 + (tid >> 5)) * Is;
+        const int l32 = tid & 31, nch = Is / 8;
+        float sacc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SD_CH; ++i) {
+            const int c = l32 + 32 * i;
+            if (c < nch) sacc += dot8_bf16_regs(ld16(hr + c * 8), r.s[i], 0.0f);
+        }
+        for (int c = l32 + 32 * SD_CH; c < nch; c += 32)  // rows past the register copy
+            sacc += dot8_bf16_regs(ld16(hr + c * 8), ld16(srow + c * 8), 0.0f);
+        sacc = group32_sum(sacc);
+        if (l32 == 0) gsl[tid >> 5] = gam_l[t] * sacc;
+    }
+
+    // routed slots: tile tau = wave + 4u holds slots 2 tau, 2 tau + 1
+    const int ntiles = (K + 1) / 2;
+    const int jb = min(l16, K - 1);  // this lane's B column: slot l16
+    const uint8_t *qb = qh + (int64_t)(t * K + jb) * I + 32 * kq;
+    const uint8_t *wrow[TPW];
+    float acc[TPW][4] = {};
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tau = wave + 4 * u;
+        const int e = ids[t * K + min(2 * tau + (l16 >> 3), K - 1)];
+        wrow[u] = a.w_down + ((int64_t)e * H + m0 + (l16 & 7)) * I + 32 * kq;
+    }
+    const int js_lane = 2 * wave + (kq >> 1);  // slot of this lane's D rows (tile u adds 8u)
+    for (int b = 0; b < IB; ++b) {
+        const v8i bq = as_v8i(*reinterpret_cast<const uint4 *>(qb + b * GROUP),
+                              *reinterpret_cast<const uint4 *>(qb + b * GROUP + 16));
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            if (wave + 4 * u >= ntiles) continue;
+            v8i aw;
+            float sdv;
+            if (b < KBR) {
+                aw = as_v8i(r.w[u][b][0], r.w[u][b][1]);
+                sdv = r.sd[u][b];
+            } else {  // K blocks past the register copy
+                aw = as_v8i(ld16(wrow[u] + b * GROUP), ld16(wrow[u] + b * GROUP + 16));
+                const int es = ids[t * K + min(js_lane + 8 * u, K - 1)];
+                sdv = a.s_down[((int64_t)es * (H / GROUP) + m0 / GROUP) * IB + b];
+            }
+            const v4f d = mfma_fp8_k128(aw, bq);
+            const int js = min(js_lane + 8 * u, K - 1);
+            const float sc = shs[(t * K + js) * IB + b] * sdv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(sc, d[i], acc[u][i]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int js = js_lane + 8 * u;
+        // D rows 4 kq + i are slot 2 tau + (kq >> 1), rows m0 + 4 (kq & 1) + i;
+        // the lane whose column is that slot holds the product wanted
+        if (js < K && l16 == js)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ej[js * MB + 4 * (kq & 1) + i] = acc[u][i];
+    }
+    __syncthreads();
+
+    // combine: slots in order, then the shared term; 8 copies for a stack
+    if (tid < MB * REPL) {
+        const int mm = tid & (MB - 1);
+        float yacc = 0.0f;
+        for (int j = 0; j < K; ++j) yacc = fmaf(wts[t * K + j], ej[j * MB + mm], yacc);
+        if (Is > 0) yacc += gsl[mm];
+        const uint32_t yb = f32_to_bf16(yacc);
+        if (tid < MB && a.y) a.y[(int64_t)t * H + m0 + mm] = (uint16_t)yb;
+        if (a.ytag) st_dev(a.ytag + ((int64_t)(tid / MB) * a.T + t) * H + m0 + mm, tagged(yb, epoch));
+    }
+    __syncthreads();  // ej and gsl are reused by the next unit
 }
 
 // ---------------------------------------------------------------- kernel
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, hs, gam, xs, red, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, ej, gsl, xs, red, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
 __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is,
@@ -502,7 +572,9 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is,
     L.wts = L.ids + al16i(P * 4);
     L.hs = L.wts + al16i(P * 4);
     L.gam = L.hs + al16i(T * Is * 2);
-    L.xs = L.gam + al16i(T * 4);                     // stacks: the renormalised rows
+    L.ej = L.gam + al16i(T * 4);                     // phase-C unit: e_j of its rows
+    L.gsl = L.ej + al16i(K * MB * 4);                // phase-C unit: gated shared rows
+    L.xs = L.gsl + al16i(MB * 4);                    // stacks: the renormalised rows
     L.red = L.xs + (stack ? al16i(T * H * 2) : 0);   // stacks: 4 fp64 partial sums
     L.total = L.red + (stack ? 32 : 0);
     return L;
@@ -587,61 +659,86 @@ __device__ __forceinline__ void quant8_strided_to_lds(const float (&f)[8], int g
 
 // Phase C inputs from this workgroup's copy, waiting for each word's epoch:
 // h (fp32, re-quantised 1x128 into LDS codes and scales), hs (bf16) and
-// gamma into LDS. The first loads of hs and gamma and of the first round of
-// h all go out before any is waited for, so a workgroup pays one handoff
-// round trip here, not one per kind of value.
-__device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint64_t *gamma,
-                              int T, int P, int I, int Is, uint32_t epoch, uint32_t *err,
-                              uint8_t *qh, float *shs, uint16_t *hs_l, float *gam_l) {
-    const int rp = blockIdx.x % REPL;
-    const int tid = threadIdx.x, nth = blockDim.x, teams = nth >> 4, team = tid >> 4;
-    const int sub = tid & 15;
+// gamma into LDS. stage_c_issue sends the first loads of hs, gamma and of the
+// first round of h; the caller can issue other loads (the routed down rows)
+// before stage_c_finish waits on them: loads return in issue order, so the
+// handoff words come back first and a workgroup pays one handoff round trip
+// here, not one per kind of value.
+struct StageC {
+    int sidx[8], gidx[1], hidx[8 * STAGE_HG];
+    int n_s0, n_g, nk0;
+    uint64_t sw[8], gw[1], hw[8 * STAGE_HG];
+};
+
+// h: team j of a round stages groups base + team + teams * k, k < STAGE_HG;
+// lane `sub` of a team takes the words sub + 16 i of a group, so every load
+// instruction of a team reads one whole 128-byte line
+__device__ __forceinline__ int stage_h_round(int base, int n_groups, int (&idx)[8 * STAGE_HG]) {
+    const int teams = blockDim.x >> 4, team = threadIdx.x >> 4, sub = threadIdx.x & 15;
+#pragma unroll
+    for (int k = 0; k < STAGE_HG; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) idx[8 * k + i] = (base + team + teams * k) * GROUP + 16 * i + sub;
+    return min(STAGE_HG, max(0, (n_groups - base - team + teams - 1) / teams));
+}
+
+__device__ __forceinline__ void stage_h_quant(int base, int nk, const uint32_t (&bits)[8 * STAGE_HG],
+                                              uint8_t *qh, float *shs) {
+    const int teams = blockDim.x >> 4, team = threadIdx.x >> 4, sub = threadIdx.x & 15;
+#pragma unroll
+    for (int k = 0; k < STAGE_HG; ++k)
+        if (k < nk) {
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[8 * k + i]);
+            quant8_strided_to_lds(f, base + team + teams * k, sub, qh, shs);
+        }
+}
+
+__device__ __forceinline__ void stage_c_issue(const uint64_t *h, const uint64_t *hs,
+                                              const uint64_t *gamma, int T, int P, int I, int Is,
+                                              uint32_t epoch, StageC &c) {
+    const int rp = blockIdx.x % REPL, tid = threadIdx.x, nth = blockDim.x;
+    const int n_hs = T * Is;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c.sidx[i] = tid + nth * i;
+    c.n_s0 = min(8, max(0, (n_hs - tid + nth - 1) / nth));
+    c.gidx[0] = rp * T + tid;
+    c.n_g = Is > 0 && tid < T ? 1 : 0;
+    c.nk0 = stage_h_round(0, P * (I / GROUP), c.hidx);
+    poll_issue<8 * STAGE_HG>(h + (int64_t)rp * P * I, c.hidx, 8 * c.nk0, epoch, c.hw);
+    poll_issue<8>(hs + (int64_t)rp * T * Is, c.sidx, c.n_s0, epoch, c.sw);
+    poll_issue<1>(gamma, c.gidx, c.n_g, epoch, c.gw);
+}
+
+__device__ __forceinline__ void stage_c_finish(const uint64_t *h, const uint64_t *hs,
+                                               const uint64_t *gamma, int T, int P, int I, int Is,
+                                               uint32_t epoch, uint32_t *err, StageC &c,
+                                               uint8_t *qh, float *shs, uint16_t *hs_l,
+                                               float *gam_l) {
+    const int rp = blockIdx.x % REPL, tid = threadIdx.x, nth = blockDim.x, teams = nth >> 4;
     const uint64_t *hsrc = h + (int64_t)rp * P * I;
     const uint64_t *ssrc = hs + (int64_t)rp * T * Is;
     const int n_groups = P * (I / GROUP), n_hs = T * Is;
-
-    // hs: up to 8 words per thread per round; the first round issued now
-    int sidx[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sidx[i] = tid + nth * i;
-    const int n_s0 = min(8, max(0, (n_hs - tid + nth - 1) / nth));
-    uint64_t sw[8];
-    poll_issue<8>(ssrc, sidx, n_s0, epoch, sw);
-    const int gidx[1] = {rp * T + tid};
-    const int n_g = Is > 0 && tid < T ? 1 : 0;
-    uint64_t gw[1];
-    poll_issue<1>(gamma, gidx, n_g, epoch, gw);
-
-    // h: team j of a round stages groups base + team + teams * k, k < STAGE_HG;
-    // lane `sub` of a team takes the words sub + 16 i of a group, so every
-    // load instruction of a team reads one whole 128-byte line
-    for (int base = 0; base < n_groups; base += STAGE_HG * teams) {
+    {
+        uint32_t bits[8 * STAGE_HG];
+        poll_finish<8 * STAGE_HG>(err, hsrc, c.hidx, 8 * c.nk0, epoch, c.hw, bits);
+        stage_h_quant(0, c.nk0, bits, qh, shs);
+    }
+    for (int base = STAGE_HG * teams; base < n_groups; base += STAGE_HG * teams) {
         int idx[8 * STAGE_HG];
-#pragma unroll
-        for (int k = 0; k < STAGE_HG; ++k)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                idx[8 * k + i] = (base + team + teams * k) * GROUP + 16 * i + sub;
-        const int nk = min(STAGE_HG, max(0, (n_groups - base - team + teams - 1) / teams));
+        const int nk = stage_h_round(base, n_groups, idx);
         uint32_t bits[8 * STAGE_HG];
         poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
-#pragma unroll
-        for (int k = 0; k < STAGE_HG; ++k)
-            if (k < nk) {
-                float f[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[8 * k + i]);
-                quant8_strided_to_lds(f, base + team + teams * k, sub, qh, shs);
-            }
+        stage_h_quant(base, nk, bits, qh, shs);
     }
-
-    // hs: finish the first round, then any further rounds
+    // hs: the first round, then any further rounds
     {
         uint32_t bits[8];
-        poll_finish<8>(err, ssrc, sidx, n_s0, epoch, sw, bits);
+        poll_finish<8>(err, ssrc, c.sidx, c.n_s0, epoch, c.sw, bits);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (i < n_s0) hs_l[sidx[i]] = (uint16_t)bits[i];
+            if (i < c.n_s0) hs_l[c.sidx[i]] = (uint16_t)bits[i];
     }
     for (int b = nth * 8; b < n_hs; b += nth * 8) {
         int idx[8];
@@ -654,9 +751,9 @@ __device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint6
         for (int i = 0; i < 8; ++i)
             if (i < n) hs_l[idx[i]] = (uint16_t)bits[i];
     }
-    if (n_g) {
+    if (c.n_g) {
         uint32_t bits[1];
-        poll_finish<1>(err, gamma, gidx, 1, epoch, gw, bits);
+        poll_finish<1>(err, gamma, c.gidx, 1, epoch, c.gw, bits);
         gam_l[tid] = __uint_as_float(bits[0]);
     }
 }
@@ -664,7 +761,7 @@ __device__ void stage_phase_c(const uint64_t *h, const uint64_t *hs, const uint6
 // Layer stacks: x_l = renorm(y_{l-1}) for every row, from this workgroup's
 // copy of the tagged y words, into LDS (bf16), with the arithmetic of the
 // stand-alone renormalisation kernel (same thread mapping and sum order).
-__device__ void renorm_rows_to_lds(const uint64_t *ytag, int T, int H, float eps,
+__device__ __forceinline__ void renorm_rows_to_lds(const uint64_t *ytag, int T, int H, float eps,
                                    uint32_t epoch, uint32_t *err, uint16_t *xs, double *red) {
     const int rp = blockIdx.x % REPL, tid = threadIdx.x, nc = H / 8;
     for (int t = 0; t < T; ++t) {
@@ -704,7 +801,7 @@ __device__ void renorm_rows_to_lds(const uint64_t *ytag, int T, int H, float eps
 }
 
 // STACK: a0.n_layers layers in sequence, one launch; otherwise one layer
-template <int NC, int KMAX, int CPL, int LPR, bool STACK>
+template <int NC, int KBR, int TPW, bool STACK>
 __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a0.T, H = a0.H, K = a0.K, I = a0.I, E = a0.E, P = T * K;
@@ -717,6 +814,8 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     float *wts = reinterpret_cast<float *>(lds + L.wts);      // [P]
     uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Is]
     float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
+    float *ej = reinterpret_cast<float *>(lds + L.ej);          // [K][MB]
+    float *gsl = reinterpret_cast<float *>(lds + L.gsl);        // [MB]
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nw = a0.nwg * 4;
@@ -728,10 +827,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     uint32_t *counter = a0.sync + SYNC_FLAGS + blockIdx.x;
     const uint32_t cnt = ld_dev(counter);
 
-    constexpr int RPP = WAVE / LPR;
-    const int sub = lane % LPR, rsel = lane / LPR;
-    const int items = T * (H / RPP);  // phase-C output row blocks
-    const int t_first = gw / (H / RPP), m_first = (gw % (H / RPP)) * RPP + rsel;
+    // phase-C units (t, MB-row block), workgroup-major; a workgroup past the
+    // last unit loads the last unit's rows (unused), so its loads need no
+    // branch
+    const int units = T * (H / MB);
+    const int u_first = min((int)blockIdx.x, units - 1);
+    const int t_first = u_first / (H / MB), m_first = (u_first % (H / MB)) * MB;
     const int n_layers = STACK ? a0.n_layers : 1;
 
     for (int l = 0; l < n_layers; ++l) {
@@ -760,14 +861,14 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
             a.ytag = l < n_layers - 1 ? a0.ytag + par * REPL * T * H : nullptr;
             if (l > 0) a.x = reinterpret_cast<const uint16_t *>(lds + L.xs);
         }
-        DownRegs<KMAX, CPL> dr;
+        DownRegs<KBR, TPW> dr;
 
         // A: router logits, shared-expert gate/up rows and the shared gate.
         // Every load that does not depend on the routing is issued here,
-        // including this wave's first shared down row (kept in registers
+        // including the first unit's shared down rows (kept in registers
         // until phase C); in a stack, before the previous layer's output is
         // awaited.
-        if (gw < items && a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m_first, sub, dr);
+        if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         const int n_items = T * E + (a.Is > 0 ? T * a.Is + T : 0);
         XRegs xr;
         uint32_t epoch;
@@ -798,8 +899,8 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
             itemA_compute<NB>(a, it, lane, ir, epoch);
         }
 
-        // B: top-K per row (one wave per row) once its logits exist; issue this
-        // wave's first block of routed down rows; then the routed gate/up rows
+        // B: top-K per row (one wave per row) once its logits exist, then the
+        // routed gate/up rows
         for (int t = wave; t < T; t += 4)
             topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch,
                         a.sync + ERR_WORD, lane, ids + t * K, wts + t * K,
@@ -807,7 +908,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         __syncthreads();
         // the routed down rows are loaded only once this wave's gate/up rows
         // are in: phase B is bandwidth-bound and h is on the critical path,
-        // while the down rows arrive during the h handoff
+        // while the down rows can arrive during the h handoff
         const int per_pair = I / GU_ROWS;
         for (int it = gw; it < P * per_pair; it += nw) {
             const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
@@ -816,22 +917,26 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
             gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr,
                                epoch);
         }
-        if (gw < items) down_load_routed<KMAX, CPL, LPR>(a, t_first, m_first, sub, ids, dr);
 
         // C: h (re-quantised), hs and gamma into LDS once they exist, then
-        // whole output rows with the combine
-        stage_phase_c(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, a.sync + ERR_WORD, qh, shs,
-                      hs_l, gam_l);
+        // whole output rows with the combine. The routed down rows go out
+        // first: loads return in order, and h is not complete before they
+        // are in, so a handoff load sent earlier would come back stale and
+        // its second try would queue behind them anyway.
+        down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
+        StageC sc;
+        stage_c_issue(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_c_finish(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, a.sync + ERR_WORD, sc, qh, shs,
+                       hs_l, gam_l);
         __syncthreads();
-        for (int it = gw; it < items; it += nw) {
-            const int t = it / (H / RPP);
-            const int m = (it % (H / RPP)) * RPP + rsel;
-            if (it != gw) {
-                if (a.Is > 0) down_load_shared<KMAX, CPL, LPR>(a, m, sub, dr);
-                down_load_routed<KMAX, CPL, LPR>(a, t, m, sub, ids, dr);
+        for (int u = blockIdx.x; u < units; u += a0.nwg) {
+            const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
+            if (u != (int)blockIdx.x) {
+                if (a.Is > 0) down_load_shared<KBR, TPW>(a, m0, dr);
+                down_load_routed<KBR, TPW>(a, t, m0, ids, dr);
             }
-            const float gsv = shared_down<KMAX, CPL, LPR>(a, t, m, sub, dr, hs_l, gam_l);
-            down_compute<KMAX, CPL, LPR>(a, t, m, sub, qh, shs, ids, wts, dr, gsv, epoch);
+            down_unit<KBR, TPW>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, gsl, epoch);
         }
         __syncthreads();  // LDS is reused by the next layer
     }
@@ -839,51 +944,47 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 4u * (uint32_t)(n_layers - 1) + 1u);
 }
 
-template <int NC, int KMAX, bool STACK>
-static hipError_t launch_k(const FusedArgs &a, size_t lds, hipStream_t st) {
+// KBR: K blocks of a down row held in registers (I / 128 up to 8); TPW:
+// MFMA tiles (slot pairs) per wave (K up to 8: one, up to 16: two)
+template <int NC, int TPW, bool STACK>
+static hipError_t launch_t(const FusedArgs &a, size_t lds, hipStream_t st) {
     const dim3 grid(a.nwg), block(256);
-    const int chunks = a.I / 16;
-#define MOE_DECODE(CPLV, LPRV) \
-    hipLaunchKernelGGL((decode_fused_kernel<NC, KMAX, CPLV, LPRV, STACK>), grid, block, lds, st, a)
-    if (chunks <= 8) MOE_DECODE(1, 8);
-    else if (chunks <= 16) MOE_DECODE(1, 16);
-    else if (chunks <= 32) MOE_DECODE(1, 32);
-    else if (chunks <= 64) MOE_DECODE(1, 64);
-    else if (chunks <= 128) MOE_DECODE(2, 64);
-    else MOE_DECODE(4, 64);
+    const int ib = a.I / GROUP;
+#define MOE_DECODE(KBRV) \
+    hipLaunchKernelGGL((decode_fused_kernel<NC, KBRV, TPW, STACK>), grid, block, lds, st, a)
+    if (ib <= 1) MOE_DECODE(1);
+    else if (ib <= 2) MOE_DECODE(2);
+    else if (ib <= 4) MOE_DECODE(4);
+    else MOE_DECODE(8);
 #undef MOE_DECODE
     return hipGetLastError();
 }
 
 template <int NC, bool STACK>
 static hipError_t launch_nc(const FusedArgs &a, size_t lds, hipStream_t st) {
-    if (a.K <= 4) return launch_k<NC, 4, STACK>(a, lds, st);
-    if (a.K <= 8) return launch_k<NC, 8, STACK>(a, lds, st);
-    return launch_k<NC, 16, STACK>(a, lds, st);
+    if (a.K <= 8) return launch_t<NC, 1, STACK>(a, lds, st);
+    return launch_t<NC, 2, STACK>(a, lds, st);
 }
 
-template <int NC, int KMAX, int CPL, int LPR, bool STACK>
+template <int NC, int KBR, int TPW, bool STACK>
 static void set_lds_limit() {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_fused_kernel<NC, KMAX, CPL, LPR, STACK>),
+        reinterpret_cast<const void *>(&decode_fused_kernel<NC, KBR, TPW, STACK>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
-template <int NC, int KMAX, bool STACK>
-static void set_lds_limits_k() {
-    set_lds_limit<NC, KMAX, 1, 8, STACK>();
-    set_lds_limit<NC, KMAX, 1, 16, STACK>();
-    set_lds_limit<NC, KMAX, 1, 32, STACK>();
-    set_lds_limit<NC, KMAX, 1, 64, STACK>();
-    set_lds_limit<NC, KMAX, 2, 64, STACK>();
-    set_lds_limit<NC, KMAX, 4, 64, STACK>();
+template <int NC, int TPW, bool STACK>
+static void set_lds_limits_t() {
+    set_lds_limit<NC, 1, TPW, STACK>();
+    set_lds_limit<NC, 2, TPW, STACK>();
+    set_lds_limit<NC, 4, TPW, STACK>();
+    set_lds_limit<NC, 8, TPW, STACK>();
 }
 
 template <int NC, bool STACK>
 static void set_lds_limits() {
-    set_lds_limits_k<NC, 4, STACK>();
-    set_lds_limits_k<NC, 8, STACK>();
-    set_lds_limits_k<NC, 16, STACK>();
+    set_lds_limits_t<NC, 1, STACK>();
+    set_lds_limits_t<NC, 2, STACK>();
 }
 
 template <bool STACK>
