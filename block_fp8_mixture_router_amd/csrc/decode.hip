@@ -164,10 +164,69 @@ __device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
 
 // ------------------------------------------------------------- phase A
 
+// Router logits come first and alone: each workgroup's four waves share one
+// logit at a time (a quarter of the row each), so the 1 MiB of router rows
+// is requested before anything else, arrives in about one memory round trip,
+// and the routing decision that everything after it waits for is taken as
+// early as possible. NQ = 16-byte chunks of a bf16 H-row per lane per wave
+// quarter (H / 2048, rounded up).
+template <int NQ>
+struct RouterRegs {
+    uint4 x[NQ], w[NQ];
+};
+
+// chunk c = lane + 64 (wave + 4 i) of row e of the router and of row t of x
+template <int NQ>
+__device__ __forceinline__ void router_load(const FusedArgs &a, int r, RouterRegs<NQ> &rr) {
+    const int t = r / a.E, e = r % a.E, nc8 = a.H / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t *wr = a.router_w + (int64_t)e * a.H, *xr = a.x + (int64_t)t * a.H;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int c = lane + WAVE * (wave + 4 * i);
+        const bool ok = c < nc8;
+        rr.w[i] = ok ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
+        rr.x[i] = ok ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Logit r = (t, e): exact fp64 sum of bf16 products (each wave's partial in
+// two chains and a lane tree, the four partials in wave order), rounded once
+// to fp32, then to bf16, then the bias; handed off in every copy. Every
+// thread of the workgroup calls this (it has a barrier); red is 4 doubles of
+// LDS, not reused by the next call before that call's barrier.
+template <int NQ>
+__device__ __forceinline__ void router_logit(const FusedArgs &a, int r, const RouterRegs<NQ> &rr,
+                                             double *red, uint32_t epoch) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const uint32_t xs[4] = {rr.x[i].x, rr.x[i].y, rr.x[i].z, rr.x[i].w};
+        const uint32_t ws[4] = {rr.w[i].x, rr.w[i].y, rr.w[i].z, rr.w[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
+            acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
+        }
+    }
+    const double part = wave_allsum_d(acc0 + acc1);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (wave == 0 && lane < REPL) {
+        const int t = r / a.E, e = r % a.E;
+        const double acc = ((red[0] + red[1]) + red[2]) + red[3];
+        float l = (float)acc;
+        if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
+        if (a.bias) l = l + a.bias[e];
+        st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e, tagged(__float_as_uint(l), epoch));
+    }
+}
+
 // NB = 16-byte chunks of a bf16 H-row per lane (H / 512, rounded up). An
-// item is one router logit, one shared-expert row or the shared gate of one
-// row of x; all of an item's loads are issued before any of its arithmetic,
-// and the kernel can do other work between the two.
+// item is one shared-expert row or the shared gate of one row of x; all of
+// an item's loads are issued before any of its arithmetic, and the kernel
+// can do other work between the two.
 template <int NB>
 struct ItemARegs {
     uint4 x[NB], w0[NB], w1[NB];
@@ -183,18 +242,15 @@ __device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
     return acc;
 }
 
-// item `it`: [0, T*E) router logits (t, e); [T*E, T*E + T*Is) shared rows
-// (t, n); then T shared gates
+// item `it`: [0, T*Is) shared rows (t, n); then T shared gates
 // the item's weight rows (they do not depend on x)
 template <int NB>
 __device__ __forceinline__ void itemA_load_w(const FusedArgs &a, int it, int lane,
                                              ItemARegs<NB> &r) {
-    const int n_router = a.T * a.E, n_sh = a.T * a.Is, nc8 = a.H / 8;
+    const int n_sh = a.T * a.Is, nc8 = a.H / 8;
     const uint16_t *w0, *w1 = nullptr;
-    if (it < n_router) {
-        w0 = a.router_w + (int64_t)(it % a.E) * a.H;
-    } else if (it < n_router + n_sh) {
-        const int n = (it - n_router) % a.Is;
+    if (it < n_sh) {
+        const int n = it % a.Is;
         w0 = a.sh_gate + (int64_t)n * a.H;
         w1 = a.sh_up + (int64_t)n * a.H;
     } else {
@@ -213,10 +269,8 @@ __device__ __forceinline__ void itemA_load_w(const FusedArgs &a, int it, int lan
 template <int NB>
 __device__ __forceinline__ void itemA_load_x(const FusedArgs &a, int it, int lane,
                                              ItemARegs<NB> &r) {
-    const int n_router = a.T * a.E, n_sh = a.T * a.Is, nc8 = a.H / 8;
-    const int t = it < n_router ? it / a.E
-                  : it < n_router + n_sh ? (it - n_router) / a.Is
-                                         : it - n_router - n_sh;
+    const int n_sh = a.T * a.Is, nc8 = a.H / 8;
+    const int t = it < n_sh ? it / a.Is : it - n_sh;
     const uint16_t *xr = a.x + (int64_t)t * a.H;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -228,32 +282,10 @@ __device__ __forceinline__ void itemA_load_x(const FusedArgs &a, int it, int lan
 template <int NB>
 __device__ __forceinline__ void itemA_compute(const FusedArgs &a, int it, int lane,
                                               const ItemARegs<NB> &r, uint32_t epoch) {
-    const int n_router = a.T * a.E, n_sh = a.T * a.Is;
-    if (it < n_router) {
-        // logit of (t, e): exact fp64 sum of bf16 products, one rounding
-        const int t = it / a.E, e = it % a.E;
-        double acc0 = 0.0, acc1 = 0.0;  // two independent chains
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const uint32_t xs[4] = {r.x[i].x, r.x[i].y, r.x[i].z, r.x[i].w};
-            const uint32_t ws[4] = {r.w0[i].x, r.w0[i].y, r.w0[i].z, r.w0[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc0 = fma((double)bf16_lo(xs[k]), (double)bf16_lo(ws[k]), acc0);
-                acc1 = fma((double)bf16_hi(xs[k]), (double)bf16_hi(ws[k]), acc1);
-            }
-        }
-        const double acc = wave_allsum_d(acc0 + acc1);
-        if (lane < REPL) {
-            float l = (float)acc;
-            if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
-            if (a.bias) l = l + a.bias[e];
-            st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e,
-                   tagged(__float_as_uint(l), epoch));
-        }
-    } else if (it < n_router + n_sh) {
+    const int n_sh = a.T * a.Is;
+    if (it < n_sh) {
         // shared-expert row n of row t: hs = bf16(silu(g) * u)
-        const int t = (it - n_router) / a.Is, n = (it - n_router) % a.Is;
+        const int t = it / a.Is, n = it % a.Is;
         float g = 0.0f, u = 0.0f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -267,7 +299,7 @@ __device__ __forceinline__ void itemA_compute(const FusedArgs &a, int it, int la
                    tagged(f32_to_bf16(silu(g) * u), epoch));
     } else {
         // shared gate of row t
-        const int t = it - n_router - n_sh;
+        const int t = it - n_sh;
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) z = dot8_bf16_regs(r.x[i], r.w0[i], z);
@@ -557,7 +589,7 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, hs, gam, ej, gsl, xs, red, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, ej, gsl, rl, xs, red, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
 __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is,
@@ -574,7 +606,8 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is,
     L.gam = L.hs + al16i(T * Is * 2);
     L.ej = L.gam + al16i(T * 4);                     // phase-C unit: e_j of its rows
     L.gsl = L.ej + al16i(K * MB * 4);                // phase-C unit: gated shared rows
-    L.xs = L.gsl + al16i(MB * 4);                    // stacks: the renormalised rows
+    L.rl = L.gsl + al16i(MB * 4);                    // router: 2 x 4 fp64 wave partials
+    L.xs = L.rl + 64;                                // stacks: the renormalised rows
     L.red = L.xs + (stack ? al16i(T * H * 2) : 0);   // stacks: 4 fp64 partial sums
     L.total = L.red + (stack ? 32 : 0);
     return L;
@@ -620,6 +653,19 @@ __device__ __forceinline__ void quant_chunk_to_lds(uint4 v, int c, uint8_t *q, f
     const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
     quant8_to_lds(f, c >> 4, c & 15, q, s);
+}
+
+// x from a workgroup's router loads (one row): lane chunk c = lane + 64
+// (wave + 4 i), 16 lanes per 128-group
+template <int NQ>
+__device__ __forceinline__ void x_quant_router(const RouterRegs<NQ> &rr, int H, uint8_t *q,
+                                               float *s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int c = lane + WAVE * (wave + 4 * i);
+        if (c < H / 8) quant_chunk_to_lds(rr.x[i], c, q, s);  // whole 16-lane groups
+    }
 }
 
 // chunks beyond the register copy (more than XQ per thread) are loaded here
@@ -816,10 +862,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
     float *ej = reinterpret_cast<float *>(lds + L.ej);          // [K][MB]
     float *gsl = reinterpret_cast<float *>(lds + L.gsl);        // [MB]
+    double *rl = reinterpret_cast<double *>(lds + L.rl);        // [2][4]
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nw = a0.nwg * 4;
-    constexpr int NB = 2 * NC;  // bf16 H-row chunks per lane
+    constexpr int NB = 2 * NC;        // bf16 H-row chunks per lane
+    constexpr int NQ = (NB + 3) / 4;  // the same per lane of a wave quarter
     const int gw = wave * a0.nwg + blockIdx.x;  // workgroup-major wave index
     // The counter's load goes out first but is waited for only after the
     // first weight loads have been issued: it is a full device-coherent round
@@ -863,18 +911,13 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         }
         DownRegs<KBR, TPW> dr;
 
-        // A: router logits, shared-expert gate/up rows and the shared gate.
-        // Every load that does not depend on the routing is issued here,
-        // including the first unit's shared down rows (kept in registers
-        // until phase C); in a stack, before the previous layer's output is
-        // awaited.
-        if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
-        const int n_items = T * E + (a.Is > 0 ? T * a.Is + T : 0);
-        XRegs xr;
+        // A1: router logits, one per workgroup at a time (four waves each),
+        // before any other load; in a stack, once the previous layer's output
+        // is in and renormalised.
+        const int n_logits = T * E;
         uint32_t epoch;
         {
-            ItemARegs<NB> ir;
-            if (gw < n_items) itemA_load_w<NB>(a, gw, lane, ir);
+            RouterRegs<NQ> rr;
             if constexpr (STACK) {
                 epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt)) + 4u * (uint32_t)l;
                 if (l > 0) {
@@ -884,15 +927,37 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
                                        reinterpret_cast<double *>(lds + L.red));
                 }
             }
-            if (gw < n_items) itemA_load_x<NB>(a, gw, lane, ir);
-            x_load(a.x, T * H / 8, xr);
+            if ((int)blockIdx.x < n_logits) router_load<NQ>(a, blockIdx.x, rr);
             if constexpr (!STACK) epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt));
-            // the lowest-numbered items are the router logits, the critical
-            // path: each wave hands its first item off before x is quantised
-            if (gw < n_items) itemA_compute<NB>(a, gw, lane, ir, epoch);
+            int round = 0;
+            for (int r = blockIdx.x; r < n_logits; r += a0.nwg, ++round) {
+                if (round > 0) router_load<NQ>(a, r, rr);
+                router_logit<NQ>(a, r, rr, rl + 4 * (round & 1), epoch);
+            }
+            // one row: the workgroup's router loads hold all of x, which is
+            // quantised (1x128) into LDS from them, needed from phase B on
+            if (T == 1 && (int)blockIdx.x < n_logits) x_quant_router<NQ>(rr, H, qx, sx);
         }
-        x_quant(a.x, T * H / 8, xr, qx, sx);  // needed from phase B on
-        for (int it = gw + nw; it < n_items; it += nw) {
+
+        // A2: shared-expert gate/up rows and the shared gate, one item per
+        // wave (waves 1-3 first: wave 0 runs the top-K next, and a wave with
+        // loads in flight would wait for them before its first poll).
+        const int n_items = a.Is > 0 ? T * a.Is + T : 0;
+        const int ia = (gw + nw - a0.nwg) % nw;  // this wave's first item
+        {
+            ItemARegs<NB> ir;
+            if (ia < n_items) {
+                itemA_load_w<NB>(a, ia, lane, ir);
+                itemA_load_x<NB>(a, ia, lane, ir);
+                itemA_compute<NB>(a, ia, lane, ir, epoch);
+            }
+        }
+        if (T > 1 || (int)blockIdx.x >= n_logits) {
+            XRegs xr;
+            x_load(a.x, T * H / 8, xr);
+            x_quant(a.x, T * H / 8, xr, qx, sx);  // needed from phase B on
+        }
+        for (int it = ia + nw; it < n_items; it += nw) {
             ItemARegs<NB> ir;
             itemA_load_w<NB>(a, it, lane, ir);
             itemA_load_x<NB>(a, it, lane, ir);
@@ -919,10 +984,11 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         }
 
         // C: h (re-quantised), hs and gamma into LDS once they exist, then
-        // whole output rows with the combine. The routed down rows go out
-        // first: loads return in order, and h is not complete before they
-        // are in, so a handoff load sent earlier would come back stale and
-        // its second try would queue behind them anyway.
+        // whole output rows with the combine. The first unit's shared and
+        // routed down rows go out first: loads return in order, and h is not
+        // complete before they are in, so a handoff load sent earlier would
+        // come back stale and its second try would queue behind them anyway.
+        if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
         StageC sc;
         stage_c_issue(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, sc);
