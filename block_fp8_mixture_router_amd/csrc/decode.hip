@@ -85,6 +85,14 @@ template <typename T>
 __device__ __forceinline__ T ld_dev(const T *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Handoff words live in the workspace (global memory). Loading them through
+// a global-address-space pointer keeps them global loads in functions the
+// compiler does not inline: a flat load is also counted as an LDS access,
+// and every wait on it becomes a wait for all outstanding memory operations.
+typedef __attribute__((address_space(1))) const uint64_t gword;
+__device__ __forceinline__ uint64_t ld_word(const uint64_t *p) {
+    return __hip_atomic_load((gword *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 template <typename T>
 __device__ __forceinline__ void st_dev(T *p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -115,7 +123,11 @@ template <int N>
 __device__ __forceinline__ void poll_issue(const uint64_t *p, const int (&idx)[N], int n,
                                            uint32_t epoch, uint64_t (&w)[N]) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) w[i] = i < n ? ld_dev(p + idx[i]) : tagged(0u, epoch);
+    for (int i = 0; i < N; ++i) {
+        // branch-free: entries past n load word 0 and are then marked done
+        const uint64_t x = ld_word(p + (i < n ? idx[i] : 0));
+        w[i] = i < n ? x : tagged(0u, epoch);
+    }
 }
 
 // Polls the words of an earlier poll_issue that do not yet carry `epoch`
@@ -147,10 +159,32 @@ __device__ __forceinline__ void poll_finish(uint32_t *err, const uint64_t *p,
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int i = 0; i < N; ++i)
-            if (i < n && !has_epoch(w[i], epoch)) w[i] = ld_dev(p + idx[i]);
+            if (i < n && !has_epoch(w[i], epoch)) w[i] = ld_word(p + idx[i]);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) v[i] = (uint32_t)w[i];
+}
+
+// Two first loads of the words, a short sleep apart: when the first comes
+// back a little too early, the second (already on its way) usually has them,
+// instead of a new round trip.
+template <int N>
+__device__ __forceinline__ void poll_words_staggered(uint32_t *err, const uint64_t *p,
+                                                     const int (&idx)[N], int n, uint32_t epoch,
+                                                     uint32_t (&v)[N]) {
+    uint64_t w0[N], w1[N];
+    poll_issue<N>(p, idx, n, epoch, w0);
+    __builtin_amdgcn_s_sleep(6);
+    poll_issue<N>(p, idx, n, epoch, w1);
+    if (all_have_epoch<N>(w0, epoch)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = (uint32_t)w0[i];
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (!has_epoch(w0[i], epoch)) w0[i] = w1[i];
+    poll_finish<N>(err, p, idx, n, epoch, w0, v);
 }
 
 template <int N>
@@ -213,7 +247,10 @@ __device__ __forceinline__ void router_logit(const FusedArgs &a, int r, const Ro
     const double part = wave_allsum_d(acc0 + acc1);
     if (lane == 0) red[wave] = part;
     __syncthreads();
-    if (wave == 0 && lane < REPL) {
+    // the last wave stores: wave 0 runs the first top-K, and a store still
+    // in flight would hold back the results of its polls (the wave's memory
+    // operations complete in order)
+    if (wave == 3 && lane < REPL) {
         const int t = r / a.E, e = r % a.E;
         const double acc = ((red[0] + red[1]) + red[2]) + red[3];
         float l = (float)acc;
@@ -321,7 +358,7 @@ __device__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, 
     for (int i = 0; i < NL; ++i) idx[i] = lane + WAVE * i;
     const int n = min(NL, max(0, (E - lane + WAVE - 1) / WAVE));
     uint32_t bits[NL];
-    poll_words<NL>(err, lr, idx, n, epoch, bits);
+    poll_words_staggered<NL>(err, lr, idx, n, epoch, bits);
     if (packed) {
         uint32_t k[NL];
 #pragma unroll
