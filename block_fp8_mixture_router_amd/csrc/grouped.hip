@@ -157,8 +157,112 @@ __global__ __launch_bounds__(SORT_THREADS) void group_sort_kernel(GroupedArgs a)
     }
 }
 
+// The same stable counting sort for up to SORT_CAP pairs in one pass over
+// the ids: each wave loads its whole segment at once (one memory round trip)
+// and ranks equal experts within each 64-pair step with ballots over the key
+// bits, so it has every pair's rank within the wave before the scan; the
+// scans over experts are wave prefix sums plus one pass over the 16 wave
+// totals. Same output (offsets, perm, tiles) as group_sort_kernel.
+constexpr int SORT_CAP = 16384;
+constexpr int SORT_STEPS = SORT_CAP / SORT_THREADS;  // 64-pair steps per wave segment
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void group_sort_small_kernel(GroupedArgs a) {
+    __shared__ int cnt[SORT_WAVES][SORT_E];  // per-wave counts, then per-wave bases
+    __shared__ int offs[SORT_E];
+    __shared__ int wtot_c[SORT_WAVES], wtot_t[SORT_WAVES];
+    const int P = a.T * a.K, E = a.E;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int seg = (P + SORT_WAVES - 1) / SORT_WAVES;
+    const int p_begin = wave * seg, p_end = min(P, p_begin + seg);
+    int ev[SORT_STEPS];
+#pragma unroll
+    for (int u = 0; u < SORT_STEPS; ++u) {
+        const int p = p_begin + 64 * u + lane;
+        ev[u] = p < p_end ? a.ids[p] : -1;
+    }
+    for (int i = tid; i < SORT_WAVES * SORT_E; i += SORT_THREADS) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    int kbits = 0;
+    while ((1 << kbits) < E) ++kbits;
+    // ranks within the wave: pairs in order, equal experts ranked by lane
+    int rk[SORT_STEPS];
+#pragma unroll
+    for (int u = 0; u < SORT_STEPS; ++u) {
+        rk[u] = 0;
+        if (64 * u < seg) {  // uniform
+            const bool valid = ev[u] >= 0;
+            const int e = valid ? ev[u] : 0;
+            uint64_t mask = __ballot(valid);
+            for (int b = 0; b < kbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t bal = __ballot(valid && bit);
+                mask &= bit ? bal : ~bal;
+            }
+            const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+            const int base = valid ? cnt[wave][e] : 0;
+            rk[u] = base + rank;
+            if (valid && rank == 0) cnt[wave][e] = base + __popcll(mask);
+        }
+    }
+    __syncthreads();
+    // thread e: per-wave bases of expert e, its total and tiles
+    const int e = tid;
+    int total = 0;
+    if (e < E)
+        for (int w = 0; w < SORT_WAVES; ++w) {
+            const int c = cnt[w][e];
+            cnt[w][e] = total;
+            total += c;
+        }
+    const int nt = (total + GR - 1) / GR;
+    // exclusive scans of total and nt over experts
+    const int ic = wave_incl_scan(total, lane), it = wave_incl_scan(nt, lane);
+    if (lane == 63) {
+        wtot_c[wave] = ic;
+        wtot_t[wave] = it;
+    }
+    __syncthreads();
+    int bc = 0, bt = 0;
+    for (int w = 0; w < wave; ++w) {
+        bc += wtot_c[w];
+        bt += wtot_t[w];
+    }
+    const int off = bc + ic - total, tb = bt + it - nt;
+    if (e < E) {
+        offs[e] = off;
+        a.offsets[e] = off;
+        for (int i = 0; i < nt; ++i) {
+            int32_t *tl = a.tiles + 4 * (tb + i);
+            tl[0] = e;
+            tl[1] = off + i * GR;
+            tl[2] = min(GR, total - i * GR);
+            tl[3] = 0;
+        }
+        if (e == E - 1) {
+            a.offsets[E] = off + total;
+            *a.n_tiles = tb + nt;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < SORT_STEPS; ++u)
+        if (ev[u] >= 0) a.perm[offs[ev[u]] + cnt[wave][ev[u]] + rk[u]] = p_begin + 64 * u + lane;
+}
+
 hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(group_sort_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a);
+    if (a.T * a.K <= SORT_CAP)
+        hipLaunchKernelGGL(group_sort_small_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a);
+    else
+        hipLaunchKernelGGL(group_sort_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a);
     return hipGetLastError();
 }
 
