@@ -401,19 +401,17 @@ __device__ __forceinline__ void gateup_load(const FusedArgs &a, int n0, int e, i
     const int KB = H / GROUP;
     const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
     const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+    // branch-free: chunks past the row reload its last chunk (the compute
+    // skips them), so the loads form one straight run
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int c = lane + WAVE * i;
-        r.sg[i] = c < nchunk ? sg[c / 8] : 0.0f;
-        r.su[i] = c < nchunk ? su[c / 8] : 0.0f;
+        const int c = min(lane + WAVE * i, nchunk - 1);
+        r.sg[i] = sg[c / 8];
+        r.su[i] = su[c / 8];
 #pragma unroll
         for (int q = 0; q < GU_ROWS; ++q) {
-            if (c < nchunk) {
-                r.g[i][q] = ld16(wg + (int64_t)q * H + c * 16);
-                r.u[i][q] = ld16(wu + (int64_t)q * H + c * 16);
-            } else {
-                r.g[i][q] = r.u[i][q] = make_uint4(0, 0, 0, 0);
-            }
+            r.g[i][q] = ld16(wg + (int64_t)q * H + c * 16);
+            r.u[i][q] = ld16(wu + (int64_t)q * H + c * 16);
         }
     }
 }
@@ -498,10 +496,8 @@ __device__ __forceinline__ void down_load_shared(const FusedArgs &a, int m0,
     const int l32 = threadIdx.x & 31, nch = a.Is / 8;
     const uint16_t *srow = a.sh_down + (int64_t)(m0 + (threadIdx.x >> 5)) * a.Is;
 #pragma unroll
-    for (int i = 0; i < SD_CH; ++i) {
-        const int c = l32 + 32 * i;
-        r.s[i] = c < nch ? ld16(srow + c * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < SD_CH; ++i)  // branch-free (chunks past the row are skipped later)
+        r.s[i] = ld16(srow + min(l32 + 32 * i, nch - 1) * 8);
 }
 
 // Routed A operands and block scales of unit (t, m0) for this wave's tiles,
@@ -1008,11 +1004,24 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
                         a.sync + ERR_WORD, lane, ids + t * K, wts + t * K,
                         !a.bias && !(a.flags & K_LOGITS_FP32));
         __syncthreads();
-        // the routed down rows are loaded only once this wave's gate/up rows
-        // are in: phase B is bandwidth-bound and h is on the critical path,
-        // while the down rows can arrive during the h handoff
+        // The first unit's shared and routed down rows are issued right after
+        // this wave's first gate/up rows: they stream in behind them while the
+        // gate/up arithmetic and the h handoff run, and the gate/up wait is
+        // for its own rows only (straight-line loads, scheduling barrier).
         const int per_pair = I / GU_ROWS;
-        for (int it = gw; it < P * per_pair; it += nw) {
+        {
+            const int it = min(gw, P * per_pair - 1);  // waves past the last item load it (unused)
+            const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
+            GateUpRegs<NC> gr;
+            gateup_load<NC>(a, n0, ids[p], lane, gr);
+            if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
+            down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
+            __builtin_amdgcn_sched_barrier(0);
+            if (gw < P * per_pair)
+                gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr,
+                                   epoch);
+        }
+        for (int it = gw + nw; it < P * per_pair; it += nw) {
             const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
             GateUpRegs<NC> gr;
             gateup_load<NC>(a, n0, ids[p], lane, gr);
@@ -1021,12 +1030,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
         }
 
         // C: h (re-quantised), hs and gamma into LDS once they exist, then
-        // whole output rows with the combine. The first unit's shared and
-        // routed down rows go out first: loads return in order, and h is not
-        // complete before they are in, so a handoff load sent earlier would
-        // come back stale and its second try would queue behind them anyway.
-        if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
-        down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
+        // whole output rows with the combine.
         StageC sc;
         stage_c_issue(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, sc);
         __builtin_amdgcn_sched_barrier(0);
