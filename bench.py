@@ -178,6 +178,7 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-addnorm", action="store_true")
     ap.add_argument("--live-launches", type=int, default=200)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -303,6 +304,36 @@ def main():
                         "hbm_tbs_algorithmic": round(L * nbytes / (sus * 1e-6) / 1e12, 4),
                         "launches_per_pass": 2 * L,
                         "passes_timed": args.stack_passes}
+    if not args.no_addnorm:
+        # the step in front of the layer: residual add + RMS norm + 1x128 FP8
+        # groups of the normed rows, one row and a 1024-row chunk, 8 rotated
+        # buffer sets (HBM-bound: bytes per launch below)
+        an = {}
+        H = shape.hidden
+        for rows in (1, 1024):
+            sets = []
+            for k in range(8):
+                g = torch.Generator(device="cuda").manual_seed(500 + k)
+                hs = torch.randn(rows, H, device="cuda", generator=g).to(torch.bfloat16)
+                rs = torch.randn(rows, H, device="cuda", generator=g).to(torch.bfloat16)
+                outs = (torch.empty_like(rs), torch.empty_like(hs),
+                        torch.empty(rows, H, dtype=torch.uint8, device="cuda"),
+                        torch.empty(rows, H // 128, dtype=torch.float32, device="cuda"))
+                sets.append((hs, rs, outs))
+            nw = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+
+            def astep(i, sets=sets, nw=nw):
+                hs, rs, (ro, xo, qo, so) = sets[i % len(sets)]
+                moe.add_rmsnorm_quant(hs, rs, nw, eps=1e-6, residual_out=ro, x=xo, q=qo,
+                                      scales=so, stream=stream)
+
+            n = 800 if rows == 1 else 200
+            asecs, _ = graph_time(astep, n, 8, stream)
+            aus = asecs / n * 1e6
+            abytes = rows * (4 * H + 4 * H + H + (H // 128) * 4) + 2 * H
+            an[f"rows{rows}"] = {"us": round(aus, 3), "bytes": abytes,
+                                 "hbm_tbs": round(abytes / (aus * 1e-6) / 1e12, 3)}
+        rec["add_rmsnorm_quant"] = an
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))

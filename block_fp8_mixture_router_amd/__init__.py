@@ -22,7 +22,7 @@ FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
-           "moe_forward", "moe_rms_renorm", "moe_forward_stack")
+           "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,9 @@ def lib():
         L.moe_forward.restype = ctypes.c_int
         L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_rms_renorm.restype = ctypes.c_int
+        L.moe_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
+                                            vp, vp]
+        L.moe_add_rmsnorm_quant.restype = ctypes.c_int
         L.moe_forward_stack.argtypes = [vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.moe_forward_stack.restype = ctypes.c_int
         _lib = L
@@ -144,6 +147,27 @@ def rms_renorm(y, x=None, eps: float = 1e-6, stream=None):
         x = torch.empty_like(y)
     _check("moe_rms_renorm", lib().moe_rms_renorm(_ptr(y), T, H, eps, _ptr(x), _stream(stream)))
     return x
+
+
+def add_rmsnorm_quant(hidden, residual, norm_w, eps: float = 1e-6, residual_out=None, x=None,
+                      q=None, scales=None, stream=None):
+    """Residual add, RMS norm and 1x128 quantisation of the normed rows.
+    Returns (residual_out, x, q, scales); residual_out may be `residual`
+    (in place)."""
+    import torch
+    T, H = hidden.shape
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if x is None:
+        x = torch.empty_like(hidden)
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=hidden.device)
+    if scales is None:
+        scales = torch.empty((T, H // 128), dtype=torch.float32, device=hidden.device)
+    _check("moe_add_rmsnorm_quant", lib().moe_add_rmsnorm_quant(
+        _ptr(hidden), _ptr(residual), _ptr(residual_out), _ptr(norm_w), T, H, eps, _ptr(x),
+        _ptr(q), _ptr(scales), _stream(stream)))
+    return residual_out, x, q, scales
 
 
 def quant_act(x, q=None, scales=None, stream=None):

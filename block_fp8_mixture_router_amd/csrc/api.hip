@@ -178,6 +178,28 @@ moe_status moe_rms_renorm(const void *y, int32_t T, int32_t H, float eps, void *
     return MOE_OK;
 }
 
+moe_status moe_add_rmsnorm_quant(const void *hidden, const void *residual_in,
+                                 void *residual_out, const void *norm_w, int32_t T, int32_t H,
+                                 float eps, void *x, uint8_t *q, float *scales, void *stream) {
+    if (T < 0 || T > MAX_ROWS || H < 128 || H > 8192 || H % 128) return MOE_E_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!hidden || !residual_in || !residual_out || !norm_w || !x || !q || !scales)
+        return MOE_E_NULL;
+    const void *a16[] = {hidden, residual_in, residual_out, norm_w, x, q};
+    for (const void *p : a16)
+        if (!al16(p)) return MOE_E_ALIGN;
+    if (reinterpret_cast<uintptr_t>(scales) & 3u) return MOE_E_ALIGN;
+    if (x == hidden || x == residual_in || x == residual_out || residual_out == hidden)
+        return MOE_E_UNSUPPORTED;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    MOE_TRY(launch_add_rmsnorm_quant(
+        static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(residual_in),
+        static_cast<const uint16_t *>(norm_w), T, H, eps, static_cast<uint16_t *>(residual_out),
+        static_cast<uint16_t *>(x), q, scales, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void *router_w,
                      const float *router_bias, int32_t *ids, float *weights, float *logits,
                      void *workspace, size_t workspace_bytes, void *stream) {

@@ -19,6 +19,12 @@ constexpr int RENORM_CHUNKS = 4;  // 16-byte chunks per thread of 256: H <= 8192
 hipError_t launch_rms_renorm(const uint16_t *y, int T, int H, float eps, uint16_t *x,
                              hipStream_t st);
 
+// ---- addnorm.hip (residual add + RMS norm + 1x128 quantisation, before the layer)
+hipError_t launch_add_rmsnorm_quant(const uint16_t *hidden, const uint16_t *res_in,
+                                    const uint16_t *norm_w, int T, int H, float eps,
+                                    uint16_t *res_out, uint16_t *x, uint8_t *q, float *s,
+                                    hipStream_t st);
+
 // ---- route.hip
 hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_w,
                                const float *bias, int H, int E, uint32_t flags, float *logits,

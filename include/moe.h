@@ -201,6 +201,28 @@ moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, i
 moe_status moe_rms_renorm(const void *y, int32_t T, int32_t H, float eps, void *x,
                           void *stream);
 
+/*
+ * Residual add, RMS norm and 1x128 activation quantisation: the step in front
+ * of the layer, whose FP8 groups come out of the norm with the order and
+ * rounding of the separate quantisation they replace (PR #925 "drama: load
+ * the checkpoint with direct I/O in file order and build the codec on its own
+ * thread", commit summaries of the Drama 3 backbone: the add-norm before the
+ * MoE writes the normed rows' FP8 groups). For each row t:
+ *   r[t,h]   = bf16(fp32(hidden[t,h]) + fp32(residual_in[t,h]))  -> residual_out
+ *   ms       = fp32(sum_h r[t,h]^2 / H), the squares exact and summed in fp64;
+ *   rs       = 1 / sqrt(ms + eps), fp32 with correctly rounded sqrt and division;
+ *   x[t,h]   = bf16(fp32(fp32(r[t,h] * rs) * norm_w[h]));
+ *   q, scales = moe_quant_act of x (bit for bit).
+ * hidden, residual_in, residual_out, x: bf16 [T, H]; norm_w: bf16 [H];
+ * q: uint8 [T, H] e4m3 codes; scales: fp32 [T, H/128]. H is a multiple of 128
+ * up to 8192; 0 <= eps <= 1. residual_out may equal residual_in (in place);
+ * x must not alias any other row tensor, nor residual_out hidden
+ * (MOE_E_UNSUPPORTED).
+ */
+moe_status moe_add_rmsnorm_quant(const void *hidden, const void *residual_in,
+                                 void *residual_out, const void *norm_w, int32_t T, int32_t H,
+                                 float eps, void *x, uint8_t *q, float *scales, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -73,6 +73,8 @@ def lib():
         L.oracle_route.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp]
         L.oracle_rms_renorm.argtypes = [vp, i64, i64, ctypes.c_float, vp]
+        L.oracle_add_rmsnorm_quant.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp, vp,
+                                               vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -150,6 +152,23 @@ def rms_renorm(y, eps: float = 1e-6):
     x = np.empty((T, H), dtype=np.uint16)
     lib().oracle_rms_renorm(_p(ya), T, H, eps, _p(x))
     return x
+
+
+def add_rmsnorm_quant(hidden, residual, norm_w, eps: float = 1e-6):
+    """Residual add, RMS norm and 1x128 quantisation of rows (bf16 [T, H]
+    inputs, norm_w bf16 [H]) -> (new residual bf16 bits, normed x bf16 bits,
+    codes uint8 [T, H], scales fp32 [T, H/128])."""
+    ha = _np(hidden, np.uint16)
+    ra = _np(residual, np.uint16)
+    wa = _np(norm_w, np.uint16)
+    T, H = ha.shape
+    assert ra.shape == (T, H) and wa.shape == (H,)
+    ro = np.empty((T, H), dtype=np.uint16)
+    x = np.empty((T, H), dtype=np.uint16)
+    q = np.empty((T, H), dtype=np.uint8)
+    s = np.empty((T, H // 128), dtype=np.float32)
+    lib().oracle_add_rmsnorm_quant(_p(ha), _p(ra), _p(wa), T, H, eps, _p(ro), _p(x), _p(q), _p(s))
+    return ro, x, q, s
 
 
 def route(shape, x, router_w, router_bias=None, flags: int = 0):

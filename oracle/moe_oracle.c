@@ -187,6 +187,37 @@ void oracle_rms_renorm(const uint16_t *y, int64_t T, int64_t H, float eps, uint1
     }
 }
 
+/* ------------------------------- residual add, RMS norm and quantisation */
+
+/* The step before the layer (PR #925 commit summaries: the add-norm before the
+ * MoE also writes the normed rows' FP8 groups, with the order and rounding of
+ * the quantisation launch it replaces). Row by row: the residual stream is
+ * updated first and rounded to bf16; the norm reads those bf16 values; the
+ * normed row is rounded to bf16; its groups are quantised exactly as
+ * oracle_quant_act quantises a bf16 row. */
+void oracle_add_rmsnorm_quant(const uint16_t *hidden, const uint16_t *res_in,
+                              const uint16_t *norm_w, int64_t T, int64_t H, float eps,
+                              uint16_t *res_out, uint16_t *x, uint8_t *q, float *s) {
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *hr = hidden + t * H, *rr = res_in + t * H;
+        uint16_t *ro = res_out + t * H, *xr = x + t * H;
+        for (int64_t h = 0; h < H; ++h) ro[h] = oracle_bf16_round(bf16_to_f32(hr[h]) + bf16_to_f32(rr[h]));
+        double sum = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double v = (double)bf16_to_f32(ro[h]);
+            sum += v * v;
+        }
+        float ms = (float)(sum / (double)H);
+        float r = 1.0f / sqrtf(ms + eps);
+        for (int64_t h = 0; h < H; ++h) {
+            float v = bf16_to_f32(ro[h]) * r;
+            v = v * bf16_to_f32(norm_w[h]);
+            xr[h] = oracle_bf16_round(v);
+        }
+        oracle_quant_act(xr, 1, H, q + t * H, s + t * (H / GRP));
+    }
+}
+
 /* ----------------------------------------------------------------- router */
 
 static void route_row(const oracle_cfg *cfg, const uint16_t *xr, const uint16_t *rw,

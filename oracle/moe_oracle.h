@@ -73,6 +73,18 @@ void oracle_forward(const oracle_cfg *cfg, const oracle_weights *w,
  * y, x: bf16 [T, H]; x may equal y. */
 void oracle_rms_renorm(const uint16_t *y, int64_t T, int64_t H, float eps, uint16_t *x);
 
+/* Residual add, RMS norm and 1x128 quantisation, the step before the layer:
+ *   r[h]  = bf16(fp32(hidden[h]) + fp32(res_in[h]))     (res_out, new stream);
+ *   ms    = fp32(sum_h r[h]^2 / H), the sum of exact squares taken in fp64;
+ *   rs    = 1 / sqrt(ms + eps) in fp32;
+ *   x[h]  = bf16(fp32(fp32(r[h] * rs) * norm_w[h]));
+ *   (q, s) = oracle_quant_act of x.
+ * hidden, res_in, res_out, x: bf16 [T, H]; norm_w: bf16 [H]; q: [T, H];
+ * s: fp32 [T, H/128]; H a multiple of 128. */
+void oracle_add_rmsnorm_quant(const uint16_t *hidden, const uint16_t *res_in,
+                              const uint16_t *norm_w, int64_t T, int64_t H, float eps,
+                              uint16_t *res_out, uint16_t *x, uint8_t *q, float *s);
+
 /* Threads the OpenMP runtime will use (for the baseline record). */
 int oracle_num_threads(void);
 

@@ -161,3 +161,27 @@ def test_workspace_is_monotonic_in_rows():
         c = moe.config(shape)
         sizes = [moe.workspace_bytes(c, T) for T in range(1, 1100)]
         assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+
+
+def test_add_rmsnorm_quant_refusals():
+    L = moe.lib()
+    H, R, O, W, X, Q, S = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, \
+        0x60000000, 0x70000000
+    eps = ctypes.c_float(1e-6)
+    f = lambda *a: L.moe_add_rmsnorm_quant(*a)  # noqa: E731
+    assert f(H, R, O, W, 4, 2048, eps, X, Q, S, None) == -5            # no device
+    assert f(H, R, R, W, 4, 2048, eps, X, Q, S, None) == -5            # in place: no device
+    assert f(H, R, O, W, 0, 2048, eps, X, Q, S, None) == 0             # no rows: no-op
+    assert f(H, R, O, W, 4, 2000, eps, X, Q, S, None) == -2
+    assert f(H, R, O, W, 4, 16384, eps, X, Q, S, None) == -2
+    assert f(H, R, O, W, -1, 2048, eps, X, Q, S, None) == -2
+    assert f(H, R, O, W, 4, 2048, ctypes.c_float(-1.0), X, Q, S, None) == -2
+    assert f(H, R, O, W, 4, 2048, ctypes.c_float(float("nan")), X, Q, S, None) == -2
+    assert f(None, R, O, W, 4, 2048, eps, X, Q, S, None) == -1
+    assert f(H, R, O, None, 4, 2048, eps, X, Q, S, None) == -1
+    assert f(H, R, O, W, 4, 2048, eps, X, Q, None, None) == -1
+    assert f(H + 2, R, O, W, 4, 2048, eps, X, Q, S, None) == -3
+    assert f(H, R, O, W, 4, 2048, eps, X, Q + 8, S, None) == -3
+    assert f(H, R, O, W, 4, 2048, eps, X, Q, S + 2, None) == -3
+    assert f(H, R, O, W, 4, 2048, eps, R, Q, S, None) == -5            # x aliases the residual
+    assert f(H, R, H, W, 4, 2048, eps, X, Q, S, None) == -5            # residual_out aliases hidden

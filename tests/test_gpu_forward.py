@@ -182,3 +182,20 @@ def test_no_shared_expert_matches_oracle():
         x, xh = x_rows(shape, T, seed=10)
         y = run_forward(shape, dev, x, shared=False)
         _check(shape, host, xh, y, shared=False)
+
+
+@pytest.mark.parametrize("T", [2048, 2500])
+def test_forward_sort_capacity_edges(T):
+    """Chunks at and past the one-pass sort's capacity (16,384 pairs: T = 2048
+    at top-8; T = 2500 takes the segmented sort): sampled rows against the
+    oracle, and the first 300 rows bit-identical to the same rows run as a
+    chunk of their own (rows are independent of the sort that placed them)."""
+    say(f"forward sort capacity T={T}")
+    shape, dev, host = layer("DECODE", 0, False)
+    x, xh = x_rows(shape, T, seed=T)
+    y = run_forward(shape, dev, x)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(T - 4, T),
+                                     np.random.default_rng(T).choice(T, 24, replace=False)]))
+    _check(shape, host, xh, y, rows=rows)
+    y300 = run_forward(shape, dev, x[:300].contiguous())
+    assert torch.equal(y[:300].view(torch.int16), y300.view(torch.int16))
