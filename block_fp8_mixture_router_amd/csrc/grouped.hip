@@ -577,8 +577,8 @@ __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
 }
 
 // ---------------------------------------------------- shared gate / up
-// Tile: 32 rows x 64 columns of Is. Wave w owns 16 columns of gate and up.
-// All 32 row tiles of a column block read the same weight rows; walking K in
+// Tile: 64 rows x 64 columns of Is. Wave w owns 16 columns of gate and up.
+// All 16 row tiles of a column block read the same weight rows; walking K in
 // the same order they would request the same lines at the same moment, which
 // measured over 2x slower. So tile r walks the K steps starting at step
 // 2r (mod KB). Each K step's partial product (four chained MFMAs from zero,
@@ -589,34 +589,43 @@ __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
 // the LDS activation fragments follow the same column split. Loads run two
 // K steps ahead, unconditionally (see the routed kernels).
 
-constexpr int SR = 32;  // rows per shared-expert tile
+constexpr int SR = 32;  // rows per combine tile
 
+constexpr int SRG = 64;  // rows per shared gate/up tile (32: +6 us on the skewed chunk, +11 us
+                         // on the concentrated one, -1.5 us on the uniform one; 128: +60 us)
 template <int PD>
 __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
-    __shared__ __align__(16) uint8_t Ash[2][SR][GROUP * 2 + APAD];
+    constexpr int NRT = SRG / 16, ARR = SRG / 32;
+    __shared__ __align__(16) uint8_t Ash[2][SRG][GROUP * 2 + APAD];
     const int H = a.H, Is = a.Is, KB = H / GROUP;
     const int snb = Is / 64;
-    const int t0 = (blk / snb) * SR, nb = blk % snb;
+    const int t0 = (blk / snb) * SRG, nb = blk % snb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, kq = lane >> 4;
     const int arow = tid >> 3, acol = (tid & 7) * 32;  // bytes
-    const int at = min(t0 + arow, a.T - 1);            // rows past T read a valid row
-    const uint8_t *aptr = reinterpret_cast<const uint8_t *>(a.x + (int64_t)at * H) + acol;
+    const uint8_t *aptr[ARR];
+    for (int r = 0; r < ARR; ++r) {
+        const int at = min(t0 + arow + 32 * r, a.T - 1);  // rows past T read a valid row
+        aptr[r] = reinterpret_cast<const uint8_t *>(a.x + (int64_t)at * H) + acol;
+    }
     const int n = nb * 64 + 16 * wave + l16;
     const uint8_t *gp = reinterpret_cast<const uint8_t *>(a.sh_gate + (int64_t)n * H) + 64 * kq;
     const uint8_t *up = reinterpret_cast<const uint8_t *>(a.sh_up + (int64_t)n * H) + 64 * kq;
-    double dg[2][4] = {}, du[2][4] = {};
+    double dg[NRT][4] = {}, du[NRT][4] = {};
     const int krot = (2 * (blk / snb)) % KB;
-    uint4 bg[PD][4], bu[PD][4], av[PD][2];
-    auto load = [&](int kb, uint4 (&g)[4], uint4 (&u)[4], uint4 (&x)[2]) {
+    uint4 bg[PD][4], bu[PD][4], av[PD][ARR][2];
+    auto load = [&](int kb, uint4 (&g)[4], uint4 (&u)[4], uint4 (&x)[ARR][2]) {
         const int off = ((kb + krot) % KB) * GROUP * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             g[i] = ld16(gp + off + 16 * i);
             u[i] = ld16(up + off + 16 * i);
         }
-        x[0] = ld16(aptr + off);
-        x[1] = ld16(aptr + off + 16);
+#pragma unroll
+        for (int r = 0; r < ARR; ++r) {
+            x[r][0] = ld16(aptr[r] + off);
+            x[r][1] = ld16(aptr[r] + off + 16);
+        }
     };
 #pragma unroll
     for (int d = 0; d < PD; ++d) load(d, bg[d], bu[d], av[d]);
@@ -627,11 +636,14 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
             const int kb = kb0 + d;
             {
                 uint8_t(*Ab)[GROUP * 2 + APAD] = Ash[kb & 1];
-                *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
-                *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+#pragma unroll
+                for (int r = 0; r < ARR; ++r) {
+                    *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol]) = av[d][r][0];
+                    *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol + 16]) = av[d][r][1];
+                }
                 __syncthreads();
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < NRT; ++rt) {
                     const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
                     v4f pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -651,7 +663,7 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
         }
     }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + rt * 16 + 4 * kq + i;
@@ -674,7 +686,7 @@ __global__ __launch_bounds__(256, 2) void expert_gateup_kernel(GroupedArgs a, in
 }
 
 hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st) {
-    const int n_shared = a.Is > 0 ? ((a.T + SR - 1) / SR) * (a.Is / 64) : 0;
+    const int n_shared = a.Is > 0 ? ((a.T + SRG - 1) / SRG) * (a.Is / 64) : 0;
     const dim3 grid((unsigned)(n_shared + a.max_tiles * (a.I / GROUP)));
     if ((a.H / GROUP) % 2 == 0)
         hipLaunchKernelGGL(expert_gateup_kernel<2>, grid, dim3(256), 0, st, a, n_shared);
