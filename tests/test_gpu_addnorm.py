@@ -52,3 +52,54 @@ def test_add_rmsnorm_quant_bit_exact(T, H, in_place):
     q2, s2 = moe.quant_act(x)
     torch.cuda.synchronize()
     assert torch.equal(q2, q) and torch.equal(s2.view(torch.int32), s.view(torch.int32))
+
+
+def test_add_rmsnorm_quant_in_a_graph():
+    """Captured in a graph and replayed (with eager work between replays),
+    every replay gives the eager bytes."""
+    T, H = 64, 2048
+    h, r, w = _inputs(T, H, seed=77)
+    hd, rd, wd = h.cuda(), r.cuda(), w.cuda()
+    ro, x, q, s = moe.add_rmsnorm_quant(hd, rd, wd)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (ro, x, q, s)]
+    stream = torch.cuda.Stream()
+    outs = [torch.empty_like(t) for t in want]
+    with torch.cuda.stream(stream):
+        moe.add_rmsnorm_quant(hd, rd, wd, residual_out=outs[0], x=outs[1], q=outs[2],
+                              scales=outs[3], stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        moe.add_rmsnorm_quant(hd, rd, wd, residual_out=outs[0], x=outs[1], q=outs[2],
+                              scales=outs[3], stream=stream)
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+
+
+def test_add_norm_then_layer_matches_the_oracle_chain():
+    """The step in front of the layer feeding the layer: the layer's output on
+    the GPU's normed rows is within tolerance of the oracle layer on the
+    oracle's normed rows (which are bit-identical to the GPU's)."""
+    from tests.gpu_common import OUT_TOL, layer, rel_rows
+    shape, dev, host = layer("DECODE", 0, False)
+    for T in (1, 300):
+        say(f"add-norm then layer T={T}")
+        h, r, w = _inputs(T, shape.hidden, seed=90 + T)
+        _, x_o, _, _ = oracle.add_rmsnorm_quant(h, r, w)
+        _, x_d, _, _ = moe.add_rmsnorm_quant(h.cuda(), r.cuda(), w.cuda())
+        assert np.array_equal(bits(x_d.cpu()), x_o)
+        cfg = moe.config(shape)
+        y = moe.forward(cfg, dev, x_d)
+        torch.cuda.synchronize()
+        xt = torch.from_numpy(x_o.view(np.int16)).view(torch.bfloat16)
+        _, acc, _, _ = oracle.forward(shape, host, xt)
+        rel, worst = rel_rows(bits(y.cpu()), acc)
+        say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
+        assert rel <= OUT_TOL
