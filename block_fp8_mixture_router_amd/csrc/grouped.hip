@@ -157,14 +157,18 @@ __global__ __launch_bounds__(SORT_THREADS) void group_sort_kernel(GroupedArgs a)
     }
 }
 
-// The same stable counting sort for up to SORT_CAP pairs in one pass over
-// the ids: each wave loads its whole segment at once (one memory round trip)
-// and ranks equal experts within each 64-pair step with ballots over the key
-// bits, so it has every pair's rank within the wave before the scan; the
-// scans over experts are wave prefix sums plus one pass over the 16 wave
-// totals. Same output (offsets, perm, tiles) as group_sort_kernel.
+// Counting sort for up to SORT_CAP pairs in one pass over the ids. A pair's
+// rank within its expert comes from an LDS atomic add on that expert's
+// counter, so the order of equal experts is not fixed. Nothing computed
+// depends on it: a pair's row of the gate/up and down products, and the
+// requantisation of its h, use that pair's row alone, and the combine reads
+// the slots in slot order. (The ballot ranks of group_sort_kernel cost about
+// 100 vector instructions per 64 pairs; for 8192 pairs on one CU that was
+// 11 us of issue time.) Same kind of output (offsets, perm, tiles) as
+// group_sort_kernel.
 constexpr int SORT_CAP = 16384;
-constexpr int SORT_STEPS = SORT_CAP / SORT_THREADS;  // 64-pair steps per wave segment
+constexpr int SORT_STEPS = SORT_CAP / SORT_THREADS;  // pairs per thread
+static_assert(SORT_E == SORT_THREADS, "one expert counter per thread");
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -176,55 +180,28 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 __global__ __launch_bounds__(SORT_THREADS) void group_sort_small_kernel(GroupedArgs a) {
-    __shared__ int cnt[SORT_WAVES][SORT_E];  // per-wave counts, then per-wave bases
-    __shared__ int offs[SORT_E];
+    __shared__ int cnt[SORT_E];   // pairs per expert
+    __shared__ int offs[SORT_E];  // first sorted position of each expert
     __shared__ int wtot_c[SORT_WAVES], wtot_t[SORT_WAVES];
     const int P = a.T * a.K, E = a.E;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int seg = (P + SORT_WAVES - 1) / SORT_WAVES;
-    const int p_begin = wave * seg, p_end = min(P, p_begin + seg);
+    // pair p = tid + SORT_THREADS * u: each load step is one coalesced row
     int ev[SORT_STEPS];
 #pragma unroll
     for (int u = 0; u < SORT_STEPS; ++u) {
-        const int p = p_begin + 64 * u + lane;
-        ev[u] = p < p_end ? a.ids[p] : -1;
+        const int p = tid + SORT_THREADS * u;
+        ev[u] = p < P ? a.ids[p] : -1;
     }
-    for (int i = tid; i < SORT_WAVES * SORT_E; i += SORT_THREADS) (&cnt[0][0])[i] = 0;
+    cnt[tid] = 0;
     __syncthreads();
-    int kbits = 0;
-    while ((1 << kbits) < E) ++kbits;
-    // ranks within the wave: pairs in order, equal experts ranked by lane
     int rk[SORT_STEPS];
 #pragma unroll
-    for (int u = 0; u < SORT_STEPS; ++u) {
-        rk[u] = 0;
-        if (64 * u < seg) {  // uniform
-            const bool valid = ev[u] >= 0;
-            const int e = valid ? ev[u] : 0;
-            uint64_t mask = __ballot(valid);
-            for (int b = 0; b < kbits; ++b) {
-                const bool bit = (e >> b) & 1;
-                const uint64_t bal = __ballot(valid && bit);
-                mask &= bit ? bal : ~bal;
-            }
-            const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-            const int base = valid ? cnt[wave][e] : 0;
-            rk[u] = base + rank;
-            if (valid && rank == 0) cnt[wave][e] = base + __popcll(mask);
-        }
-    }
+    for (int u = 0; u < SORT_STEPS; ++u) rk[u] = ev[u] >= 0 ? atomicAdd(&cnt[ev[u]], 1) : 0;
     __syncthreads();
-    // thread e: per-wave bases of expert e, its total and tiles
+    // thread e: expert e's total and tiles; exclusive scans over experts
     const int e = tid;
-    int total = 0;
-    if (e < E)
-        for (int w = 0; w < SORT_WAVES; ++w) {
-            const int c = cnt[w][e];
-            cnt[w][e] = total;
-            total += c;
-        }
+    const int total = e < E ? cnt[e] : 0;
     const int nt = (total + GR - 1) / GR;
-    // exclusive scans of total and nt over experts
     const int ic = wave_incl_scan(total, lane), it = wave_incl_scan(nt, lane);
     if (lane == 63) {
         wtot_c[wave] = ic;
@@ -255,7 +232,7 @@ __global__ __launch_bounds__(SORT_THREADS) void group_sort_small_kernel(GroupedA
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < SORT_STEPS; ++u)
-        if (ev[u] >= 0) a.perm[offs[ev[u]] + cnt[wave][ev[u]] + rk[u]] = p_begin + 64 * u + lane;
+        if (ev[u] >= 0) a.perm[offs[ev[u]] + rk[u]] = tid + SORT_THREADS * u;
 }
 
 hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
