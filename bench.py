@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-addnorm", action="store_true")
+    ap.add_argument("--no-control", action="store_true",
+                    help="skip the no-activation-quantisation control chunk")
     ap.add_argument("--live-launches", type=int, default=200)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -280,6 +282,23 @@ def main():
                            "pct_of_attainable": round(100 * tflops / attain, 1),
                            "hbm_tbs_algorithmic": round(cb / (cus * 1e-6) / 1e12, 3),
                            "experts_touched": touched, "algorithmic_bytes": cb}
+        if not args.no_control:
+            # the no-activation-quantisation control on the uniform chunk
+            # (bf16 x and h times decoded e4m3 weights; untuned kernels)
+            cfg_nq = moe.config(shape, moe.NO_ACT_QUANT)
+            ws_nq = moe.alloc_workspace(cfg_nq, 1024)
+            lsu = [(layers[l], moe.weights_struct(layers[l])) for l in range(nrot)]
+
+            def nstep(i):
+                lw, wsr = lsu[i % nrot]
+                moe.forward(cfg_nq, lw, xc, y=yc, workspace=ws_nq, wstruct=wsr, stream=stream)
+
+            print(f"[bench] control: {args.chunk_steps} steps", file=sys.stderr, flush=True)
+            nsecs, _ = graph_time(nstep, args.chunk_steps, 2, stream)
+            chunk["chunk1024_uniform_no_act_quant"] = {
+                "us_per_chunk": round(nsecs / args.chunk_steps * 1e6, 2),
+                "note": "fidelity control: bf16 activations, decoded e4m3 weights"}
+            del ws_nq
         rec["chunk"] = chunk
     if not args.no_stack and L >= 2:
         # the per-frame stack: L independent decode layers chained on one row,

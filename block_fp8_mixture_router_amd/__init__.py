@@ -18,6 +18,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
           -4: "MOE_E_WORKSPACE", -5: "MOE_E_UNSUPPORTED", -6: "MOE_E_LAUNCH"}
 LOGITS_FP32 = 1 << 1
+NO_ACT_QUANT = 1 << 2  # fidelity control: no activation quantisation (grouped path)
 FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
 

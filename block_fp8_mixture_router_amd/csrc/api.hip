@@ -58,7 +58,7 @@ bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 moe_status check_cfg(const moe_config *c) {
     if (!c) return MOE_E_NULL;
-    const uint32_t known = MOE_LOGITS_FP32 | MOE_FORCE_GEMV | MOE_FORCE_GROUPED;
+    const uint32_t known = MOE_LOGITS_FP32 | MOE_NO_ACT_QUANT | MOE_FORCE_GEMV | MOE_FORCE_GROUPED;
     if (c->flags & ~known) return MOE_E_UNSUPPORTED;
     if ((c->flags & MOE_FORCE_GEMV) && (c->flags & MOE_FORCE_GROUPED)) return MOE_E_UNSUPPORTED;
     if (c->hidden < 128 || c->hidden > 8192 || c->hidden % 128) return MOE_E_SHAPE;
@@ -79,7 +79,7 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t sync, dlogits, dgamma, dhs, dh, dy, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
-        perm, tiles, n_tiles, qh, sh, stage;
+        perm, tiles, n_tiles, qh, sh, stage, hb;
     size_t total;
     int max_tiles;
 };
@@ -124,6 +124,8 @@ Layout layout_of(const moe_config *c, int T) {
     L.qh = take(t * K * I);
     L.sh = take(t * K * (I / 128) * 4);
     L.stage = take(t * K * H * 2);
+    // bf16 h of the no-activation-quantisation control
+    L.hb = take((c->flags & MOE_NO_ACT_QUANT) ? t * K * I * 2 : 0);
     L.total = off;
     return L;
 }
@@ -304,9 +306,10 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     float *wts = at<float>(workspace, L.wts);
     float *gamma = at<float>(workspace, L.gamma);
     const bool fits = decode_fits(T, H, K, cfg->inter, shared ? cfg->shared_inter : 0);
-    if ((cfg->flags & MOE_FORCE_GEMV) && !fits) return MOE_E_UNSUPPORTED;
+    const bool noq = (cfg->flags & MOE_NO_ACT_QUANT) != 0;
+    if ((cfg->flags & MOE_FORCE_GEMV) && (!fits || noq)) return MOE_E_UNSUPPORTED;
     const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
-                      (!(cfg->flags & MOE_FORCE_GROUPED) && T <= 4 && fits);
+                      (!(cfg->flags & MOE_FORCE_GROUPED) && !noq && T <= 4 && fits);
     if (gemv) {
         FusedArgs a{};
         fill_decode_args(a, cfg, w, x, T, y, workspace, L);
@@ -334,6 +337,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     g.sh = at<float>(workspace, L.sh);
     g.hs = at<uint16_t>(workspace, L.hs);
     g.stage = at<uint16_t>(workspace, L.stage);
+    g.hb = noq ? at<uint16_t>(workspace, L.hb) : nullptr;
     g.y = static_cast<uint16_t *>(y);
     const uint16_t *rw = static_cast<const uint16_t *>(w->router_w);
     const uint16_t *gw = shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr;
@@ -350,8 +354,17 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                                   at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
     }
     MOE_TRY(launch_group_sort(g, st));
-    MOE_TRY(launch_expert_gateup(g, st));
-    MOE_TRY(launch_grouped_down(g, st));
+    if (noq) {
+        // the shared expert's tiles alone (the launch holds no routed tiles
+        // when max_tiles is 0), then the control's routed products
+        GroupedArgs gs = g;
+        gs.max_tiles = 0;
+        MOE_TRY(launch_expert_gateup(gs, st));
+        MOE_TRY(launch_grouped_noq(g, st));
+    } else {
+        MOE_TRY(launch_expert_gateup(g, st));
+        MOE_TRY(launch_grouped_down(g, st));
+    }
     MOE_TRY(launch_shared_down_combine(g, st));
     return MOE_OK;
 }
@@ -362,7 +375,8 @@ moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, i
     static_assert(sizeof(LayerPtrs) == sizeof(moe_weights), "layer table layout");
     moe_status s = check_cfg(cfg);
     if (s != MOE_OK) return s;
-    if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_E_UNSUPPORTED;
+    if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_NO_ACT_QUANT))
+        return MOE_E_UNSUPPORTED;
     if (T < 0 || n_layers < 0 || n_layers > MAX_STACK_LAYERS) return MOE_E_SHAPE;
     if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;
     if (T == 0 || n_layers == 0) return MOE_OK;

@@ -665,6 +665,7 @@ __global__ __launch_bounds__(256, 2) void expert_gateup_kernel(GroupedArgs a, in
 hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st) {
     const int n_shared = a.Is > 0 ? ((a.T + SRG - 1) / SRG) * (a.Is / 64) : 0;
     const dim3 grid((unsigned)(n_shared + a.max_tiles * (a.I / GROUP)));
+    if (grid.x == 0) return hipSuccess;
     if ((a.H / GROUP) % 2 == 0)
         hipLaunchKernelGGL(expert_gateup_kernel<2>, grid, dim3(256), 0, st, a, n_shared);
     else

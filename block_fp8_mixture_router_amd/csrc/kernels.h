@@ -114,6 +114,7 @@ struct GroupedArgs {
     float *sh;           // [T*K, I/128]
     uint16_t *hs;        // [T, Is] bf16
     uint16_t *stage;     // [T*K, H] bf16 expert outputs e_j, pair order
+    uint16_t *hb;        // [T*K, I] bf16 h, sorted order (no-quantisation control only)
     uint16_t *y;         // [T, H]
 };
 constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
@@ -125,5 +126,8 @@ hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st);
 
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
+// the no-activation-quantisation control: routed gate/up and down on bf16
+// activations and decoded e4m3 weights (writes hb, then stage)
+hipError_t launch_grouped_noq(const GroupedArgs &a, hipStream_t st);
 
 }  // namespace moe

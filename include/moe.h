@@ -59,6 +59,9 @@ typedef enum {
 
 /* moe_config.flags */
 #define MOE_LOGITS_FP32   (1u << 1) /* decide on fp32 router logits (no bf16 rounding) */
+#define MOE_NO_ACT_QUANT  (1u << 2) /* fidelity control: the routed experts take bf16 x and
+                                       bf16 h times the decoded e4m3 weights (no activation
+                                       quantisation); moe_forward only, grouped path at any T */
 #define MOE_FORCE_GEMV    (1u << 8) /* run the row-at-a-time decode path (T <= 16; refused
                                        with MOE_E_UNSUPPORTED where its LDS plan does not fit) */
 #define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
@@ -144,6 +147,11 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
  *   s         = Wsd . bf16(silu(Wsg x) * (Wsu x))   (bf16 shared expert);
  *   gamma     = sigmoid(sh_gate_w . x);
  *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
+ * With MOE_NO_ACT_QUANT (a fidelity control, not a fast path): g_j and u_j
+ * take bf16 x unquantised, h_j is rounded to bf16 instead of re-quantised,
+ * and e_j takes that h; every product is with the decoded e4m3 weights times
+ * their block scales. It runs on the expert-grouped kernels at any T and is
+ * refused (MOE_E_UNSUPPORTED) together with MOE_FORCE_GEMV.
  * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
  * workspace: >= moe_workspace_bytes(cfg, T) bytes, zero-filled once before
  * the first moe_forward call that uses it (any single repeated byte value
@@ -175,7 +183,8 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
  * x: bf16 [T, H]; y: bf16 [T, H], the last layer's output (must not alias
  * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL;
  * T rows of the decode path only (MOE_E_UNSUPPORTED where its LDS plan does
- * not fit, e.g. beyond 16 rows); cfg->flags may not force a path;
+ * not fit, e.g. beyond 16 rows); cfg->flags may not force a path or set
+ * MOE_NO_ACT_QUANT;
  * 0 <= n_layers <= 4096; 0 <= eps <= 1; workspace as for moe_forward.
  * STATUS: switched off. The arguments are checked as above (T = 0 or
  * n_layers = 0 still returns MOE_OK); every other valid call returns

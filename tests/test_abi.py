@@ -185,3 +185,21 @@ def test_add_rmsnorm_quant_refusals():
     assert f(H, R, O, W, 4, 2048, eps, X, Q, S + 2, None) == -3
     assert f(H, R, O, W, 4, 2048, eps, R, Q, S, None) == -5            # x aliases the residual
     assert f(H, R, H, W, 4, 2048, eps, X, Q, S, None) == -5            # residual_out aliases hidden
+
+
+def test_no_act_quant_flag():
+    """The control flag is known, adds exactly one bf16 [T*K, I] region to the
+    workspace, and is refused with the decode path forced or in a stack."""
+    c, n = _cfg(), _cfg(flags=moe.NO_ACT_QUANT)
+    s = inputs.DECODE
+    for T in (1, 1024):
+        extra = (T * s.top_k * s.inter * 2 + 255) // 256 * 256
+        assert moe.workspace_bytes(n, T) == moe.workspace_bytes(c, T) + extra
+    L = moe.lib()
+    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    eps = ctypes.c_float(1e-6)
+    nb = moe.workspace_bytes(n, 1)
+    assert L.moe_forward_stack(ctypes.byref(n), TB, 40, X, 1, eps, Y, None, WS, nb, None) == -5
+    w = _fake_weights()
+    gemv = _cfg(flags=moe.NO_ACT_QUANT | moe.FORCE_GEMV)
+    assert _fwd(gemv, w, X, 1, Y, WS, moe.workspace_bytes(gemv, 1)) == -5
