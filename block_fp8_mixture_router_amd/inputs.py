@@ -155,12 +155,19 @@ class LayerWeights:
     sh_up: torch.Tensor               # bf16 [Is, H]
     sh_down: torch.Tensor             # bf16 [H, Is]
     sh_gate_w: torch.Tensor           # bf16 [H]
+    # block-FP8 shared expert (make_layer(shared_fp8=True)): sh_gate, sh_up
+    # and sh_down then hold e4m3 codes [Is, H], [Is, H], [H, Is] and these
+    # their fp32 scales [Is/128, H/128], [Is/128, H/128], [H/128, Is/128]
+    sh_s_gate: Optional[torch.Tensor] = None
+    sh_s_up: Optional[torch.Tensor] = None
+    sh_s_down: Optional[torch.Tensor] = None
     extra: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     def tensors(self) -> Dict[str, Optional[torch.Tensor]]:
         return {k: getattr(self, k) for k in (
             "router_w", "router_bias", "w_gate", "s_gate", "w_up", "s_up", "w_down",
-            "s_down", "sh_gate", "sh_up", "sh_down", "sh_gate_w")}
+            "s_down", "sh_gate", "sh_up", "sh_down", "sh_gate_w", "sh_s_gate", "sh_s_up",
+            "sh_s_down")}
 
     def to(self, device) -> "LayerWeights":
         kw = {k: (None if v is None else v.to(device)) for k, v in self.tensors().items()}
@@ -176,7 +183,8 @@ def make_router(shape: LayerShape, seed: int = 0, layer: int = 0, device="cpu",
 
 
 def make_layer(shape: LayerShape, seed: int = 0, layer: int = 0, device="cpu",
-               skewed: bool = False, std: float = 0.02) -> LayerWeights:
+               skewed: bool = False, std: float = 0.02,
+               shared_fp8: bool = False) -> LayerWeights:
     E, H, I, Is = shape.n_experts, shape.hidden, shape.inter, shape.shared_inter
     dev = torch.device(device)
     g = lambda t: _gen(seed, layer, t, dev)  # noqa: E731
@@ -189,6 +197,14 @@ def make_layer(shape: LayerShape, seed: int = 0, layer: int = 0, device="cpu",
     sh_down = _normal((H, Is), std, g(_T_SH_DOWN), dev).to(torch.bfloat16)
     sh_gate_w = _normal((H,), std, g(_T_SH_GW), dev).to(torch.bfloat16)
     bias = skew_bias(E).to(dev) if skewed else None
+    if shared_fp8:
+        # the same recipe as the routed experts, one expert, from the shared
+        # matrices' own streams
+        (sg, ssg), (su, ssu), (sd, ssd) = (
+            fp8_block_weights(1, r, c, std, g(t), dev)
+            for r, c, t in ((Is, H, _T_SH_GATE), (Is, H, _T_SH_UP), (H, Is, _T_SH_DOWN)))
+        return LayerWeights(shape, router_w, bias, w_gate, s_gate, w_up, s_up, w_down, s_down,
+                            sg[0], su[0], sd[0], sh_gate_w, ssg[0], ssu[0], ssd[0])
     return LayerWeights(shape, router_w, bias, w_gate, s_gate, w_up, s_up, w_down, s_down,
                         sh_gate, sh_up, sh_down, sh_gate_w)
 

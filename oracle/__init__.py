@@ -24,6 +24,7 @@ SOURCES = [os.path.join(_HERE, "moe_oracle.c")]
 
 NO_ACT_QUANT = 1 << 0
 LOGITS_FP32 = 1 << 1
+SHARED_FP8 = 1 << 2  # shared expert stored block-FP8, run as the routed experts
 
 
 def build(force: bool = True) -> str:
@@ -46,7 +47,7 @@ class _Cfg(ctypes.Structure):
 class _Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "router_bias", "w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down",
-        "sh_gate", "sh_up", "sh_down", "sh_gate_w")]
+        "sh_gate", "sh_up", "sh_down", "sh_gate_w", "sh_s_gate", "sh_s_up", "sh_s_down")]
 
 
 _lib = None
@@ -194,12 +195,16 @@ def forward(shape, weights, x, flags: int = 0, shared: Optional[bool] = None):
     xa = _np(x, np.uint16)
     T = xa.shape[0]
     arrs = {}
+    sh = np.uint8 if flags & SHARED_FP8 else np.uint16  # e4m3 codes or bf16
     dt = {"router_w": np.uint16, "router_bias": np.float32, "w_gate": np.uint8,
           "s_gate": np.float32, "w_up": np.uint8, "s_up": np.float32, "w_down": np.uint8,
-          "s_down": np.float32, "sh_gate": np.uint16, "sh_up": np.uint16,
-          "sh_down": np.uint16, "sh_gate_w": np.uint16}
+          "s_down": np.float32, "sh_gate": sh, "sh_up": sh, "sh_down": sh,
+          "sh_gate_w": np.uint16, "sh_s_gate": np.float32, "sh_s_up": np.float32,
+          "sh_s_down": np.float32}
     for name, d in dt.items():
-        a = getattr(weights, name)
+        a = getattr(weights, name, None)
+        if shared is False and name.startswith("sh_"):
+            a = None  # no shared expert: its matrices are never read
         arrs[name] = None if a is None else _np(a, d)
     W = _Weights(**{k: (None if v is None else v.ctypes.data) for k, v in arrs.items()})
     y = np.empty((T, shape.hidden), dtype=np.uint16)

@@ -296,26 +296,26 @@ static void block_fp8_matvec(const uint8_t *W, const float *S, int N, int Kd,
     }
 }
 
-/* Expert output e_j for one (row, slot) pair. */
-static void expert_pair(const oracle_cfg *cfg, const oracle_weights *w, int e,
-                        const uint8_t *qx, const float *sx, const float *xf, float *out) {
-    const int H = cfg->hidden, I = cfg->inter;
+/* One block-FP8 SwiGLU expert on one row: gate and up [I,H], down [H,I],
+ * e4m3 codes with fp32 scales per 128x128 block; x quantised 1x128 (or not,
+ * with ORACLE_NO_ACT_QUANT), h = silu(g) * u re-quantised 1x128 (or not). */
+static void fp8_expert(const oracle_cfg *cfg, int I, const uint8_t *wg, const float *sg,
+                       const uint8_t *wu, const float *su, const uint8_t *wd,
+                       const float *sd, const uint8_t *qx, const float *sx,
+                       const float *xf, float *out) {
+    const int H = cfg->hidden;
     const int noq = (cfg->flags & ORACLE_NO_ACT_QUANT) != 0;
-    const int64_t gsz = (int64_t)I * H, ssz = (int64_t)(I / GRP) * (H / GRP);
     float *g = (float *)malloc(sizeof(float) * (size_t)I);
     float *u = (float *)malloc(sizeof(float) * (size_t)I);
     float *h = (float *)malloc(sizeof(float) * (size_t)I);
     uint8_t *qh = (uint8_t *)malloc((size_t)I);
     float *sh = (float *)malloc(sizeof(float) * (size_t)(I / GRP));
-    block_fp8_matvec(w->w_gate + e * gsz, w->s_gate + e * ssz, I, H,
-                     noq ? NULL : qx, xf, sx, g);
-    block_fp8_matvec(w->w_up + e * gsz, w->s_up + e * ssz, I, H,
-                     noq ? NULL : qx, xf, sx, u);
+    block_fp8_matvec(wg, sg, I, H, noq ? NULL : qx, xf, sx, g);
+    block_fp8_matvec(wu, su, I, H, noq ? NULL : qx, xf, sx, u);
     for (int n = 0; n < I; ++n) h[n] = silu(g[n]) * u[n];
     if (!noq)
         for (int b = 0; b < I / GRP; ++b) quant_group(h + b * GRP, qh + b * GRP, sh + b);
-    block_fp8_matvec(w->w_down + e * gsz, w->s_down + e * ssz, H, I,
-                     noq ? NULL : qh, h, sh, out);
+    block_fp8_matvec(wd, sd, H, I, noq ? NULL : qh, h, sh, out);
     free(g);
     free(u);
     free(h);
@@ -323,14 +323,34 @@ static void expert_pair(const oracle_cfg *cfg, const oracle_weights *w, int e,
     free(sh);
 }
 
+/* Expert output e_j for one (row, slot) pair. */
+static void expert_pair(const oracle_cfg *cfg, const oracle_weights *w, int e,
+                        const uint8_t *qx, const float *sx, const float *xf, float *out) {
+    const int H = cfg->hidden, I = cfg->inter;
+    const int64_t gsz = (int64_t)I * H, ssz = (int64_t)(I / GRP) * (H / GRP);
+    fp8_expert(cfg, I, w->w_gate + e * gsz, w->s_gate + e * ssz, w->w_up + e * gsz,
+               w->s_up + e * ssz, w->w_down + e * gsz, w->s_down + e * ssz, qx, sx, xf, out);
+}
+
 /* Shared expert s = Wsd . bf16(silu(Wsg x) * (Wsu x)) and gate
- * gamma = sigmoid(wg . x), fp32 sums of exact bf16 products. */
-static void shared_row(const oracle_cfg *cfg, const oracle_weights *w, const float *xf,
-                       float *s, float *gamma) {
+ * gamma = sigmoid(wg . x), fp32 sums of exact bf16 products. With
+ * ORACLE_SHARED_FP8 (a variant: the pages keep the shared expert bf16) the
+ * shared matrices are block-FP8 and s is computed exactly as a routed
+ * expert's output. */
+static void shared_row(const oracle_cfg *cfg, const oracle_weights *w, const uint8_t *qx,
+                       const float *sx, const float *xf, float *s, float *gamma) {
     const int H = cfg->hidden, Is = cfg->shared_inter;
     float z = 0.0f;
     for (int h = 0; h < H; ++h) z += xf[h] * bf16_to_f32(w->sh_gate_w[h]);
     *gamma = 1.0f / (1.0f + expf(-z));
+    if (cfg->flags & ORACLE_SHARED_FP8) {
+        /* the shared expert stored block-FP8 runs exactly as a routed expert
+         * (same quantised x, same requantised h); gamma takes w's place */
+        fp8_expert(cfg, Is, (const uint8_t *)w->sh_gate, w->sh_s_gate,
+                   (const uint8_t *)w->sh_up, w->sh_s_up, (const uint8_t *)w->sh_down,
+                   w->sh_s_down, qx, sx, xf, s);
+        return;
+    }
     float *hs = (float *)malloc(sizeof(float) * (size_t)(Is > 0 ? Is : 1));
     for (int n = 0; n < Is; ++n) {
         float gs = 0.0f, us = 0.0f;
@@ -377,7 +397,7 @@ void oracle_forward(const oracle_cfg *cfg, const oracle_weights *w,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < T; ++t) {
         if (cfg->shared_inter > 0) {
-            shared_row(cfg, w, xf + t * H, s + t * H, gamma + t);
+            shared_row(cfg, w, qx + t * H, sx + t * G, xf + t * H, s + t * H, gamma + t);
         } else {
             gamma[t] = 0.0f;
             for (int m = 0; m < H; ++m) s[t * H + m] = 0.0f;

@@ -20,6 +20,7 @@ extern "C" {
 /* Variant switches of the oracle. */
 #define ORACLE_NO_ACT_QUANT  (1u << 0) /* skip both activation quantisations */
 #define ORACLE_LOGITS_FP32   (1u << 1) /* keep router logits in fp32 (no bf16 rounding) */
+#define ORACLE_SHARED_FP8    (1u << 2) /* shared expert stored block-FP8, run as the routed experts */
 
 typedef struct {
     int32_t hidden;       /* H */
@@ -39,10 +40,13 @@ typedef struct {
     const float *s_up;           /* fp32 [E][I/128,H/128] */
     const uint8_t *w_down;       /* e4m3 [E][H,I] */
     const float *s_down;         /* fp32 [E][H/128,I/128] */
-    const uint16_t *sh_gate;     /* bf16 [Is,H] */
-    const uint16_t *sh_up;       /* bf16 [Is,H] */
-    const uint16_t *sh_down;     /* bf16 [H,Is] */
+    const uint16_t *sh_gate;     /* bf16 [Is,H]; e4m3 bytes with ORACLE_SHARED_FP8 */
+    const uint16_t *sh_up;       /* bf16 [Is,H]; e4m3 bytes with ORACLE_SHARED_FP8 */
+    const uint16_t *sh_down;     /* bf16 [H,Is]; e4m3 bytes with ORACLE_SHARED_FP8 */
     const uint16_t *sh_gate_w;   /* bf16 [H] */
+    const float *sh_s_gate;      /* fp32 [Is/128,H/128], ORACLE_SHARED_FP8 only */
+    const float *sh_s_up;        /* fp32 [Is/128,H/128], ORACLE_SHARED_FP8 only */
+    const float *sh_s_down;      /* fp32 [H/128,Is/128], ORACLE_SHARED_FP8 only */
 } oracle_weights;
 
 float oracle_e4m3_decode(uint8_t code);

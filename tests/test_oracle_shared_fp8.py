@@ -1,0 +1,77 @@
+"""Pins of the oracle's block-FP8 shared-expert variant (ORACLE_SHARED_FP8):
+the shared matrices stored block-FP8 run exactly as a routed expert, with
+gamma in place of a routing weight. Pinned against the routed path (itself
+pinned bit for bit by the exact instances), not against the variant's own
+code."""
+import numpy as np
+import torch
+
+import oracle
+from block_fp8_mixture_router_amd import inputs
+
+SHAPE = inputs.TINY  # I = Is = 128, so an expert's matrices fit the shared slot
+
+
+def _shared_from_expert(lw, e):
+    """The layer with expert e's FP8 matrices as its shared expert and the
+    shared gate vector 2^-4 everywhere (so gamma_t = sigmoid(sum_h x_t,h / 16))."""
+    lw.sh_gate, lw.sh_s_gate = lw.w_gate[e].clone(), lw.s_gate[e].clone()
+    lw.sh_up, lw.sh_s_up = lw.w_up[e].clone(), lw.s_up[e].clone()
+    lw.sh_down, lw.sh_s_down = lw.w_down[e].clone(), lw.s_down[e].clone()
+    lw.sh_gate_w = torch.full_like(lw.sh_gate_w, 0.0625)
+    return lw
+
+
+def _all_experts_are(lw, e):
+    for name in ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down"):
+        t = getattr(lw, name)
+        setattr(lw, name, t[e:e + 1].expand_as(t).clone())
+    return lw
+
+
+def test_shared_fp8_is_a_routed_expert_with_weight_gamma():
+    x = inputs.make_x(SHAPE, 12, seed=4)
+    for e in (0, 5):
+        lw = _shared_from_expert(inputs.make_layer(SHAPE, seed=3, shared_fp8=True), e)
+        _, acc_routed, _, _ = oracle.forward(SHAPE, lw, x, shared=False)
+        _, acc_var, _, _ = oracle.forward(SHAPE, lw, x, flags=oracle.SHARED_FP8)
+        # expert e's output on each row, from the routed path alone: a layer
+        # whose experts are all expert e gives sum_j w_j e_e = (sum_j w_j) e_e
+        lid = _all_experts_are(inputs.make_layer(SHAPE, seed=3), e)
+        _, acc_id, _, w = oracle.forward(SHAPE, lid, x, shared=False)
+        ee = acc_id.astype(np.float64) / w.astype(np.float64).sum(1, keepdims=True)
+        xs = x.float().double().numpy()
+        gamma = 1.0 / (1.0 + np.exp(-xs.sum(1, keepdims=True) / 16.0))
+        assert np.ptp(gamma) > 0.1  # gamma varies across rows
+        want = acc_routed.astype(np.float64) + gamma * ee
+        err = np.abs(acc_var - want).max() / np.abs(want).max()
+        assert err < 1e-5, err
+        # and the variant really adds something of the size of an expert
+        assert np.abs(acc_var - acc_routed).max() > 0.1 * np.abs(ee).max()
+
+
+def test_zero_fp8_shared_down_removes_the_branch():
+    x = inputs.make_x(SHAPE, 6, seed=8)
+    lw = inputs.make_layer(SHAPE, seed=2, shared_fp8=True)
+    lw.sh_down = torch.zeros_like(lw.sh_down)  # every code +0
+    y0, a0, _, _ = oracle.forward(SHAPE, lw, x, shared=False)
+    y1, a1, _, _ = oracle.forward(SHAPE, lw, x, flags=oracle.SHARED_FP8)
+    assert np.array_equal(a0.view(np.uint32), a1.view(np.uint32))
+    assert np.array_equal(y0, y1)
+
+
+def test_shared_fp8_generator_matches_routed_recipe():
+    """The synthetic FP8 shared matrices follow the routed recipe: every
+    128x128 block's largest code is +-448 and code x scale reproduces a
+    matrix of the requested spread."""
+    lw = inputs.make_layer(inputs.DECODE, seed=1, shared_fp8=True)
+    for w, sc in ((lw.sh_gate, lw.sh_s_gate), (lw.sh_up, lw.sh_s_up),
+                  (lw.sh_down, lw.sh_s_down)):
+        assert w.dtype == torch.uint8 and sc.dtype == torch.float32
+        r, c = w.shape
+        assert sc.shape == (r // 128, c // 128)
+        f = w.view(torch.float8_e4m3fn).float()
+        blk = f.view(r // 128, 128, c // 128, 128).abs().amax(dim=(1, 3))
+        assert torch.all(blk == 448.0)
+        deq = (f.view(r // 128, 128, c // 128, 128) * sc[:, None, :, None]).reshape(r, c)
+        assert abs(float(deq.std()) - 0.02) < 0.002
