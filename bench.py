@@ -180,7 +180,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-addnorm", action="store_true")
     ap.add_argument("--no-control", action="store_true",
-                    help="skip the no-activation-quantisation control chunk")
+                    help="skip the chunks of the two variants (no activation quantisation, "
+                    "block-FP8 shared expert)")
     ap.add_argument("--live-launches", type=int, default=200)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -299,6 +300,25 @@ def main():
                 "us_per_chunk": round(nsecs / args.chunk_steps * 1e6, 2),
                 "note": "fidelity control: bf16 activations, decoded e4m3 weights"}
             del ws_nq
+            # the block-FP8 shared-expert variant on the uniform chunk (the
+            # shared matrices as one more grouped FP8 expert over every row)
+            cfg_sf = moe.config(shape, moe.SHARED_FP8)
+            ws_sf = moe.alloc_workspace(cfg_sf, 1024)
+            lsf = []
+            for l in range(nrot):
+                lw = inputs.make_layer(shape, seed=0, layer=l, device="cuda", shared_fp8=True)
+                lsf.append((lw, moe.weights_struct(lw)))
+
+            def fstep(i):
+                lw, wsr = lsf[i % nrot]
+                moe.forward(cfg_sf, lw, xc, y=yc, workspace=ws_sf, wstruct=wsr, stream=stream)
+
+            print(f"[bench] shared fp8: {args.chunk_steps} steps", file=sys.stderr, flush=True)
+            fsecs, _ = graph_time(fstep, args.chunk_steps, 2, stream)
+            chunk["chunk1024_uniform_shared_fp8"] = {
+                "us_per_chunk": round(fsecs / args.chunk_steps * 1e6, 2),
+                "note": "variant: block-FP8 shared expert run as a grouped expert"}
+            del ws_sf, lsf
         rec["chunk"] = chunk
     if not args.no_stack and L >= 2:
         # the per-frame stack: L independent decode layers chained on one row,

@@ -18,6 +18,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
           -4: "MOE_E_WORKSPACE", -5: "MOE_E_UNSUPPORTED", -6: "MOE_E_LAUNCH"}
 LOGITS_FP32 = 1 << 1
+SHARED_FP8 = 1 << 0  # shared expert stored block-FP8 (grouped path)
 NO_ACT_QUANT = 1 << 2  # fidelity control: no activation quantisation (grouped path)
 FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
@@ -41,7 +42,7 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "router_bias", "w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down",
-        "sh_gate", "sh_up", "sh_down", "sh_gate_w")]
+        "sh_gate", "sh_up", "sh_down", "sh_gate_w", "sh_s_gate", "sh_s_up", "sh_s_down")]
 
 
 _lib = None
@@ -203,7 +204,7 @@ def route(cfg: Config, x, router_w, router_bias=None, ids=None, weights=None, lo
 def weights_struct(lw) -> Weights:
     """Weights struct from an object with the tensor attributes of
     inputs.LayerWeights (all on the device)."""
-    return Weights(**{k: _ptr(getattr(lw, k)) for k, _ in Weights._fields_})
+    return Weights(**{k: _ptr(getattr(lw, k, None)) for k, _ in Weights._fields_})
 
 
 def forward(cfg: Config, lw, x, y=None, workspace=None, stream=None, wstruct=None):

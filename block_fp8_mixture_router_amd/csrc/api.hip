@@ -58,9 +58,12 @@ bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 moe_status check_cfg(const moe_config *c) {
     if (!c) return MOE_E_NULL;
-    const uint32_t known = MOE_LOGITS_FP32 | MOE_NO_ACT_QUANT | MOE_FORCE_GEMV | MOE_FORCE_GROUPED;
+    const uint32_t known =
+        MOE_SHARED_FP8 | MOE_LOGITS_FP32 | MOE_NO_ACT_QUANT | MOE_FORCE_GEMV | MOE_FORCE_GROUPED;
     if (c->flags & ~known) return MOE_E_UNSUPPORTED;
     if ((c->flags & MOE_FORCE_GEMV) && (c->flags & MOE_FORCE_GROUPED)) return MOE_E_UNSUPPORTED;
+    // the two variants are separate switches, not combined
+    if ((c->flags & MOE_SHARED_FP8) && (c->flags & MOE_NO_ACT_QUANT)) return MOE_E_UNSUPPORTED;
     if (c->hidden < 128 || c->hidden > 8192 || c->hidden % 128) return MOE_E_SHAPE;
     if (c->inter < 128 || c->inter > 4096 || c->inter % 128) return MOE_E_SHAPE;
     if (c->shared_inter < 0 || c->shared_inter > 4096 || c->shared_inter % 128) return MOE_E_SHAPE;
@@ -79,7 +82,7 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t sync, dlogits, dgamma, dhs, dh, dy, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
-        perm, tiles, n_tiles, qh, sh, stage, hb;
+        perm, tiles, n_tiles, qh, sh, stage, hb, sperm, stiles, sntiles, sqh, ssh, es;
     size_t total;
     int max_tiles;
 };
@@ -126,6 +129,15 @@ Layout layout_of(const moe_config *c, int T) {
     L.stage = take(t * K * H * 2);
     // bf16 h of the no-activation-quantisation control
     L.hb = take((c->flags & MOE_NO_ACT_QUANT) ? t * K * I * 2 : 0);
+    // the block-FP8 shared expert as one more grouped expert over all rows:
+    // its pair list and tiles, its h codes and scales, and its output
+    const bool sfp8 = (c->flags & MOE_SHARED_FP8) && Is > 0;
+    L.sperm = take(sfp8 ? t * 4 : 0);
+    L.stiles = take(sfp8 ? (t + GROUP_ROWS - 1) / GROUP_ROWS * 16 : 0);
+    L.sntiles = take(sfp8 ? 4 : 0);
+    L.sqh = take(sfp8 ? t * Is : 0);
+    L.ssh = take(sfp8 ? t * (Is / 128) * 4 : 0);
+    L.es = take(sfp8 ? t * H * 2 : 0);
     L.total = off;
     return L;
 }
@@ -292,6 +304,13 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     if (shared && (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down) ||
                    !al16(w->sh_gate_w)))
         return MOE_E_ALIGN;
+    const bool sfp8 = shared && (cfg->flags & MOE_SHARED_FP8);
+    if (sfp8) {
+        if (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down) return MOE_E_NULL;
+        const void *ss[] = {w->sh_s_gate, w->sh_s_up, w->sh_s_down};
+        for (const void *p : ss)
+            if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
+    }
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
     const Layout L = layout_of(cfg, T);
     if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
@@ -307,9 +326,10 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     float *gamma = at<float>(workspace, L.gamma);
     const bool fits = decode_fits(T, H, K, cfg->inter, shared ? cfg->shared_inter : 0);
     const bool noq = (cfg->flags & MOE_NO_ACT_QUANT) != 0;
-    if ((cfg->flags & MOE_FORCE_GEMV) && (!fits || noq)) return MOE_E_UNSUPPORTED;
+    const bool variant = noq || (cfg->flags & MOE_SHARED_FP8);  // grouped kernels only
+    if ((cfg->flags & MOE_FORCE_GEMV) && (!fits || variant)) return MOE_E_UNSUPPORTED;
     const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
-                      (!(cfg->flags & MOE_FORCE_GROUPED) && !noq && T <= 4 && fits);
+                      (!(cfg->flags & MOE_FORCE_GROUPED) && !variant && T <= 4 && fits);
     if (gemv) {
         FusedArgs a{};
         fill_decode_args(a, cfg, w, x, T, y, workspace, L);
@@ -354,18 +374,47 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                                   at<uint8_t>(workspace, L.qx), at<float>(workspace, L.sx), st));
     }
     MOE_TRY(launch_group_sort(g, st));
+    // the routed products (with the bf16 shared expert's gate/up tiles in
+    // the same launch, unless the shared expert is block-FP8)
+    GroupedArgs gr = g;
+    if (sfp8) gr.Is = 0;
     if (noq) {
-        // the shared expert's tiles alone (the launch holds no routed tiles
-        // when max_tiles is 0), then the control's routed products
-        GroupedArgs gs = g;
+        // the bf16 shared expert's tiles alone (the launch holds no routed
+        // tiles when max_tiles is 0), then the control's routed products
+        GroupedArgs gs = gr;
         gs.max_tiles = 0;
         MOE_TRY(launch_expert_gateup(gs, st));
-        MOE_TRY(launch_grouped_noq(g, st));
+        MOE_TRY(launch_grouped_noq(gr, st));
     } else {
-        MOE_TRY(launch_expert_gateup(g, st));
-        MOE_TRY(launch_grouped_down(g, st));
+        MOE_TRY(launch_expert_gateup(gr, st));
+        MOE_TRY(launch_grouped_down(gr, st));
     }
-    MOE_TRY(launch_shared_down_combine(g, st));
+    if (sfp8) {
+        // the block-FP8 shared expert: one expert holding every row (K = 1),
+        // through the routed kernels, its output staged in es
+        GroupedArgs gs = gr;
+        gs.K = 1;
+        gs.E = 1;
+        gs.I = cfg->shared_inter;
+        gs.w_gate = static_cast<const uint8_t *>(w->sh_gate);
+        gs.w_up = static_cast<const uint8_t *>(w->sh_up);
+        gs.w_down = static_cast<const uint8_t *>(w->sh_down);
+        gs.s_gate = w->sh_s_gate;
+        gs.s_up = w->sh_s_up;
+        gs.s_down = w->sh_s_down;
+        gs.perm = at<int32_t>(workspace, L.sperm);
+        gs.tiles = at<int32_t>(workspace, L.stiles);
+        gs.n_tiles = at<int32_t>(workspace, L.sntiles);
+        gs.max_tiles = (T + GROUP_ROWS - 1) / GROUP_ROWS;
+        gs.qh = at<uint8_t>(workspace, L.sqh);
+        gs.sh = at<float>(workspace, L.ssh);
+        gs.stage = at<uint16_t>(workspace, L.es);
+        MOE_TRY(launch_shared_tiles(T, gs.perm, gs.tiles, gs.n_tiles, st));
+        MOE_TRY(launch_expert_gateup(gs, st));
+        MOE_TRY(launch_grouped_down(gs, st));
+        gr.es = gs.stage;
+    }
+    MOE_TRY(launch_shared_down_combine(gr, st));
     return MOE_OK;
 }
 
@@ -375,7 +424,7 @@ moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, i
     static_assert(sizeof(LayerPtrs) == sizeof(moe_weights), "layer table layout");
     moe_status s = check_cfg(cfg);
     if (s != MOE_OK) return s;
-    if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_NO_ACT_QUANT))
+    if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_NO_ACT_QUANT | MOE_SHARED_FP8))
         return MOE_E_UNSUPPORTED;
     if (T < 0 || n_layers < 0 || n_layers > MAX_STACK_LAYERS) return MOE_E_SHAPE;
     if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;

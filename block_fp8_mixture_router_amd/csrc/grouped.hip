@@ -243,6 +243,33 @@ hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The block-FP8 shared expert as one expert holding every row: pair list
+// perm[r] = r (read with K = 1, so row r and stage row r) and 64-row tiles.
+__global__ __launch_bounds__(256) void shared_tiles_kernel(int T, int32_t *__restrict__ perm,
+                                                           int32_t *__restrict__ tiles,
+                                                           int32_t *__restrict__ n_tiles) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < T) {
+        perm[i] = i;
+        if (i % GR == 0) {
+            int32_t *tl = tiles + 4 * (i / GR);
+            tl[0] = 0;
+            tl[1] = i;
+            tl[2] = min(GR, T - i);
+            tl[3] = 0;
+        }
+    }
+    if (i == 0) *n_tiles = (T + GR - 1) / GR;
+}
+
+hipError_t launch_shared_tiles(int T, int32_t *perm, int32_t *tiles, int32_t *n_tiles,
+                               hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(shared_tiles_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st,
+                       T, perm, tiles, n_tiles);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------- FP8 MFMA helpers
 
 __device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
@@ -782,6 +809,15 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
             const float g = a.gamma[t];
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc8[i] = fmaf(g, Ss[row][c * 8 + i], acc8[i]);
+        } else if (a.es) {  // the block-FP8 shared expert's staged output
+            const float g = a.gamma[t];
+            const uint4 v = ld16(a.es + (int64_t)t * H + mb * GROUP + c * 8);
+            const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc8[2 * i] = fmaf(g, bf16_lo(vs[i]), acc8[2 * i]);
+                acc8[2 * i + 1] = fmaf(g, bf16_hi(vs[i]), acc8[2 * i + 1]);
+            }
         }
         uint4 out;
         out.x = f32_to_bf16(acc8[0]) | (f32_to_bf16(acc8[1]) << 16);

@@ -59,6 +59,7 @@ struct LayerPtrs {
     const uint8_t *w_down;
     const float *s_down;
     const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
+    const float *sh_s_gate, *sh_s_up, *sh_s_down;  // block-FP8 shared variant (unused here)
 };
 struct FusedArgs {
     int T, H, E, K, I, Is;
@@ -115,6 +116,7 @@ struct GroupedArgs {
     uint16_t *hs;        // [T, Is] bf16
     uint16_t *stage;     // [T*K, H] bf16 expert outputs e_j, pair order
     uint16_t *hb;        // [T*K, I] bf16 h, sorted order (no-quantisation control only)
+    const uint16_t *es;  // [T, H] bf16 block-FP8 shared expert output, or null
     uint16_t *y;         // [T, H]
 };
 constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
@@ -129,5 +131,9 @@ hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
 // the no-activation-quantisation control: routed gate/up and down on bf16
 // activations and decoded e4m3 weights (writes hb, then stage)
 hipError_t launch_grouped_noq(const GroupedArgs &a, hipStream_t st);
+// identity pair list and 64-row tiles over T rows (the block-FP8 shared
+// expert run through the routed kernels as one expert holding every row)
+hipError_t launch_shared_tiles(int T, int32_t *perm, int32_t *tiles, int32_t *n_tiles,
+                               hipStream_t st);
 
 }  // namespace moe

@@ -58,6 +58,10 @@ typedef enum {
 } moe_status;
 
 /* moe_config.flags */
+#define MOE_SHARED_FP8    (1u << 0) /* variant: the shared expert stored block-FP8 (codes and
+                                       128x128 block scales sh_s_*), run exactly as a routed
+                                       expert on the quantised rows, gamma in place of w;
+                                       moe_forward only, grouped path at any T */
 #define MOE_LOGITS_FP32   (1u << 1) /* decide on fp32 router logits (no bf16 rounding) */
 #define MOE_NO_ACT_QUANT  (1u << 2) /* fidelity control: the routed experts take bf16 x and
                                        bf16 h times the decoded e4m3 weights (no activation
@@ -86,10 +90,14 @@ typedef struct {
     const float *s_up;        /* fp32 [E][I/128, H/128] */
     const uint8_t *w_down;    /* e4m3 [E][H, I] */
     const float *s_down;      /* fp32 [E][H/128, I/128] */
-    const void *sh_gate;      /* bf16 [Is, H]; unused when Is = 0 */
-    const void *sh_up;        /* bf16 [Is, H] */
-    const void *sh_down;      /* bf16 [H, Is] */
+    const void *sh_gate;      /* bf16 [Is, H]; unused when Is = 0; e4m3 [Is, H]
+                                 with MOE_SHARED_FP8 */
+    const void *sh_up;        /* bf16 [Is, H]; e4m3 [Is, H] with MOE_SHARED_FP8 */
+    const void *sh_down;      /* bf16 [H, Is]; e4m3 [H, Is] with MOE_SHARED_FP8 */
     const void *sh_gate_w;    /* bf16 [H]: shared-expert gate vector */
+    const float *sh_s_gate;   /* fp32 [Is/128, H/128] with MOE_SHARED_FP8, else unused */
+    const float *sh_s_up;     /* fp32 [Is/128, H/128] with MOE_SHARED_FP8, else unused */
+    const float *sh_s_down;   /* fp32 [H/128, Is/128] with MOE_SHARED_FP8, else unused */
 } moe_weights;
 
 /* 1 if `device` is a gfx950 GPU this library was built for; 0 otherwise and
@@ -147,6 +155,10 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
  *   s         = Wsd . bf16(silu(Wsg x) * (Wsu x))   (bf16 shared expert);
  *   gamma     = sigmoid(sh_gate_w . x);
  *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
+ * With MOE_SHARED_FP8, s is instead the output of the block-FP8 shared
+ * matrices computed as e_j is (quantised x, requantised h); it runs on the
+ * expert-grouped kernels at any T and is refused with MOE_FORCE_GEMV or
+ * together with MOE_NO_ACT_QUANT.
  * With MOE_NO_ACT_QUANT (a fidelity control, not a fast path): g_j and u_j
  * take bf16 x unquantised, h_j is rounded to bf16 instead of re-quantised,
  * and e_j takes that h; every product is with the decoded e4m3 weights times
@@ -184,7 +196,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
  * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL;
  * T rows of the decode path only (MOE_E_UNSUPPORTED where its LDS plan does
  * not fit, e.g. beyond 16 rows); cfg->flags may not force a path or set
- * MOE_NO_ACT_QUANT;
+ * MOE_NO_ACT_QUANT or MOE_SHARED_FP8;
  * 0 <= n_layers <= 4096; 0 <= eps <= 1; workspace as for moe_forward.
  * STATUS: switched off. The arguments are checked as above (T = 0 or
  * n_layers = 0 still returns MOE_OK); every other valid call returns

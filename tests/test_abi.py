@@ -203,3 +203,25 @@ def test_no_act_quant_flag():
     w = _fake_weights()
     gemv = _cfg(flags=moe.NO_ACT_QUANT | moe.FORCE_GEMV)
     assert _fwd(gemv, w, X, 1, Y, WS, moe.workspace_bytes(gemv, 1)) == -5
+
+
+def test_shared_fp8_flag():
+    """The block-FP8 shared flag is known, adds its own workspace regions,
+    needs the three shared scale arrays, and is refused with the control, in
+    a stack and with the decode path forced."""
+    c, f = _cfg(), _cfg(flags=moe.SHARED_FP8)
+    assert moe.workspace_bytes(f, 1024) > moe.workspace_bytes(c, 1024)
+    assert moe.workspace_bytes(_cfg(flags=moe.SHARED_FP8 | moe.NO_ACT_QUANT), 1) == 0
+    L = moe.lib()
+    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    eps = ctypes.c_float(1e-6)
+    nf = moe.workspace_bytes(f, 1)
+    assert L.moe_forward_stack(ctypes.byref(f), TB, 40, X, 1, eps, Y, None, WS, nf, None) == -5
+    w = _fake_weights()
+    assert _fwd(f, w, X, 1, Y, WS, nf) == -5  # valid, but no gfx950 device here
+    w.sh_s_down = None
+    assert _fwd(f, w, X, 1, Y, WS, nf) == -1  # the scales are required
+    w = _fake_weights()
+    w.sh_s_up = w.sh_s_up + 2
+    assert _fwd(f, w, X, 1, Y, WS, nf) == -3
+    assert _fwd(c, _fake_weights(), X, 1, Y, WS, moe.workspace_bytes(c, 1)) == -5
