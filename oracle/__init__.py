@@ -74,6 +74,7 @@ def lib():
         L.oracle_route.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp]
         L.oracle_rms_renorm.argtypes = [vp, i64, i64, ctypes.c_float, vp]
+        L.oracle_bf16_gemv.argtypes = [vp, i64, i64, vp, i64, vp]
         L.oracle_add_rmsnorm_quant.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp, vp,
                                                vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -170,6 +171,19 @@ def add_rmsnorm_quant(hidden, residual, norm_w, eps: float = 1e-6):
     s = np.empty((T, H // 128), dtype=np.float32)
     lib().oracle_add_rmsnorm_quant(_p(ha), _p(ra), _p(wa), T, H, eps, _p(ro), _p(x), _p(q), _p(s))
     return ro, x, q, s
+
+
+def bf16_gemv(W, x):
+    """One-row bf16 projection: W bf16 [N, K], x bf16 [T, K] -> y bf16 bits
+    [T, N], y = bf16(fp32(exact sum of products))."""
+    wa = _np(W, np.uint16)
+    xa = _np(x, np.uint16)
+    N, K = wa.shape
+    T = xa.shape[0]
+    assert xa.shape == (T, K)
+    y = np.empty((T, N), dtype=np.uint16)
+    lib().oracle_bf16_gemv(_p(wa), N, K, _p(xa), T, _p(y))
+    return y
 
 
 def route(shape, x, router_w, router_bias=None, flags: int = 0):

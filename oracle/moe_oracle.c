@@ -423,6 +423,18 @@ void oracle_forward(const oracle_cfg *cfg, const oracle_weights *w,
     free(gamma);
 }
 
+void oracle_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const uint16_t *x, int64_t T,
+                      uint16_t *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)bf16_to_f32(x[t * K + k]) * (double)bf16_to_f32(W[n * K + k]);
+            y[t * N + n] = oracle_bf16_round((float)acc);
+        }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

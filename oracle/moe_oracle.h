@@ -89,6 +89,17 @@ void oracle_add_rmsnorm_quant(const uint16_t *hidden, const uint16_t *res_in,
                               const uint16_t *norm_w, int64_t T, int64_t H, float eps,
                               uint16_t *res_out, uint16_t *x, uint8_t *q, float *s);
 
+/* One-row bf16 projection, the backbone's other bf16 projections (PR #925
+ * "drama: load the checkpoint with direct I/O in file order and build the
+ * codec on its own thread", commit summaries: the backbone's bf16 GEMMs and
+ * the single-row projection that streams its weights):
+ *   y[t,n] = bf16(fp32(sum_k x[t,k] * W[n,k])),
+ * the sum of exact bf16 products taken in fp64 in ascending k and rounded
+ * once to fp32 (the router logits' rule). W: bf16 [N, K] row-major;
+ * x: bf16 [T, K]; y: bf16 [T, N]. */
+void oracle_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const uint16_t *x, int64_t T,
+                      uint16_t *y);
+
 /* Threads the OpenMP runtime will use (for the baseline record). */
 int oracle_num_threads(void);
 
