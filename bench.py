@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-addnorm", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true",
+                    help="skip the one-row bf16 projections")
     ap.add_argument("--no-control", action="store_true",
                     help="skip the chunks of the two variants (no activation quantisation, "
                     "block-FP8 shared expert)")
@@ -373,6 +375,33 @@ def main():
             an[f"rows{rows}"] = {"us": round(aus, 3), "bytes": abytes,
                                  "hbm_tbs": round(abytes / (aus * 1e-6) / 1e12, 3)}
         rec["add_rmsnorm_quant"] = an
+    if not args.no_gemv:
+        # one-row bf16 projections of the rest of the backbone row (sizes
+        # around hidden 2048), each over enough rotated weight copies (more
+        # than 256 MiB) that no cache holds them between launches
+        gv = {}
+        K0 = shape.hidden
+        for (N, K) in ((4096, K0), (K0, 2 * K0), (8 * K0, K0)):
+            ncopy = max(4, -(-(384 << 20) // (N * K * 2)))
+            g = torch.Generator(device="cuda").manual_seed(N + K)
+            Ws = [(torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+                  for _ in range(ncopy)]
+            xg = torch.randn(1, K, device="cuda", generator=g).to(torch.bfloat16)
+            yg = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
+
+            def gstep(i, Ws=Ws, xg=xg, yg=yg):
+                moe.bf16_gemv(Ws[i % len(Ws)], xg, y=yg, stream=stream)
+
+            n = 4 * ncopy
+            gsecs, _ = graph_time(gstep, n, ncopy, stream)
+            gus = gsecs / n * 1e6
+            gbytes = N * K * 2 + K * 2 + N * 2
+            tbs = gbytes / (gus * 1e-6) / 1e12
+            gv[f"N{N}_K{K}_rows1"] = {"us": round(gus, 3), "bytes": gbytes,
+                                      "hbm_tbs": round(tbs, 3),
+                                      "frac_hbm_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 3)}
+            del Ws
+        rec["bf16_gemv"] = gv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))

@@ -24,7 +24,8 @@ FORCE_GEMV = 1 << 8
 FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
-           "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant")
+           "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant",
+           "moe_bf16_gemv")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
         L.moe_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
                                             vp, vp]
         L.moe_add_rmsnorm_quant.restype = ctypes.c_int
+        L.moe_bf16_gemv.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+        L.moe_bf16_gemv.restype = ctypes.c_int
         L.moe_forward_stack.argtypes = [vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.moe_forward_stack.restype = ctypes.c_int
         _lib = L
@@ -170,6 +173,19 @@ def add_rmsnorm_quant(hidden, residual, norm_w, eps: float = 1e-6, residual_out=
         _ptr(hidden), _ptr(residual), _ptr(residual_out), _ptr(norm_w), T, H, eps, _ptr(x),
         _ptr(q), _ptr(scales), _stream(stream)))
     return residual_out, x, q, scales
+
+
+def bf16_gemv(W, x, y=None, stream=None):
+    """One-row bf16 projection: W bf16 [N, K], x bf16 [T, K] (T <= 4) ->
+    y bf16 [T, N] = bf16(fp32(exact sum of products))."""
+    import torch
+    N, K = W.shape
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check("moe_bf16_gemv", lib().moe_bf16_gemv(_ptr(W), N, K, _ptr(x), T, _ptr(y),
+                                                _stream(stream)))
+    return y
 
 
 def quant_act(x, q=None, scales=None, stream=None):

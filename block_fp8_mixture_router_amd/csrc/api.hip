@@ -13,6 +13,13 @@
 #include "../../include/moe.h"
 #include "kernels.h"
 
+namespace moe {
+// csrc/gemv.hip (declared here so that the decode kernel's sources stay as
+// they are)
+hipError_t launch_bf16_gemv(const uint16_t *W, int N, int K, const uint16_t *x, int T,
+                            uint16_t *y, hipStream_t st);
+}  // namespace moe
+
 using namespace moe;
 
 namespace {
@@ -211,6 +218,21 @@ moe_status moe_add_rmsnorm_quant(const void *hidden, const void *residual_in,
         static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(residual_in),
         static_cast<const uint16_t *>(norm_w), T, H, eps, static_cast<uint16_t *>(residual_out),
         static_cast<uint16_t *>(x), q, scales, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+moe_status moe_bf16_gemv(const void *W, int32_t N, int32_t K, const void *x, int32_t T, void *y,
+                         void *stream) {
+    if (N < 0 || N > (1 << 20) || T < 0 || T > 4 || K < 128 || K > 8192 || K % 128)
+        return MOE_E_SHAPE;
+    if (N == 0 || T == 0) return MOE_OK;
+    if (!W || !x || !y) return MOE_E_NULL;
+    if (!al16(W) || !al16(x) || (reinterpret_cast<uintptr_t>(y) & 1u)) return MOE_E_ALIGN;
+    if (y == x || y == W) return MOE_E_UNSUPPORTED;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    MOE_TRY(launch_bf16_gemv(static_cast<const uint16_t *>(W), N, K,
+                             static_cast<const uint16_t *>(x), T, static_cast<uint16_t *>(y),
+                             static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 

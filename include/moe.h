@@ -244,6 +244,23 @@ moe_status moe_add_rmsnorm_quant(const void *hidden, const void *residual_in,
                                  void *residual_out, const void *norm_w, int32_t T, int32_t H,
                                  float eps, void *x, uint8_t *q, float *scales, void *stream);
 
+/*
+ * One-row bf16 projection, for the backbone's other bf16 projections around
+ * the layer (PR #925 "drama: load the checkpoint with direct I/O in file
+ * order and build the codec on its own thread", commit summaries: the
+ * backbone's bf16 GEMMs and the single-row projection that streams its
+ * weights ahead of use). For t < T and n < N:
+ *   y[t,n] = bf16(fp32(sum_k x[t,k] * W[n,k])),
+ * the products exact and accumulated in fp64, rounded once to fp32 (the rule
+ * of the router logits). W: bf16 [N, K] row-major; x: bf16 [T, K]; y: bf16
+ * [T, N]. 0 <= T <= 4 (the one-row decode regime; MOE_E_SHAPE beyond);
+ * 0 <= N <= 2^20; K a multiple of 128 up to 8192. W and x 16-byte aligned, y
+ * 2-byte aligned; y must not alias x or W (MOE_E_UNSUPPORTED). T = 0 or
+ * N = 0 is a no-op.
+ */
+moe_status moe_bf16_gemv(const void *W, int32_t N, int32_t K, const void *x, int32_t T, void *y,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -225,3 +225,19 @@ def test_shared_fp8_flag():
     w.sh_s_up = w.sh_s_up + 2
     assert _fwd(f, w, X, 1, Y, WS, nf) == -3
     assert _fwd(c, _fake_weights(), X, 1, Y, WS, moe.workspace_bytes(c, 1)) == -5
+
+
+def test_bf16_gemv_refusals():
+    L = moe.lib()
+    W, X, Y = 0x20000000, 0x30000000, 0x40000000
+    assert L.moe_bf16_gemv(W, 16, 100, X, 1, Y, None) == -2     # K not a multiple of 128
+    assert L.moe_bf16_gemv(W, 16, 16384, X, 1, Y, None) == -2   # K beyond 8192
+    assert L.moe_bf16_gemv(W, 16, 2048, X, 5, Y, None) == -2    # more than 4 rows
+    assert L.moe_bf16_gemv(W, -1, 2048, X, 1, Y, None) == -2
+    assert L.moe_bf16_gemv(W, 0, 2048, X, 1, Y, None) == 0       # no-op
+    assert L.moe_bf16_gemv(W, 16, 2048, X, 0, Y, None) == 0      # no-op
+    assert L.moe_bf16_gemv(None, 16, 2048, X, 1, Y, None) == -1
+    assert L.moe_bf16_gemv(W + 8, 16, 2048, X, 1, Y, None) == -3
+    assert L.moe_bf16_gemv(W, 16, 2048, X, 1, Y + 1, None) == -3
+    assert L.moe_bf16_gemv(W, 16, 2048, X, 1, X, None) == -5     # y aliases x
+    assert L.moe_bf16_gemv(W, 16, 2048, X, 1, Y, None) == -5     # no gfx950 device here
