@@ -27,7 +27,7 @@ template <int NC>
 __global__ __launch_bounds__(GV_WAVES * 64) void bf16_gemv_kernel(
     const uint16_t *__restrict__ W, int N, int K, const uint16_t *__restrict__ x, int T,
     uint16_t *__restrict__ y) {
-    __shared__ __align__(16) uint16_t xs[4 * GV_MAXK];
+    extern __shared__ __align__(16) uint16_t xs[];  // T x K, sized at launch
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nc8 = K / 8;  // 16-byte chunks per row
     const int n0 = (blockIdx.x * GV_WAVES + wave) * GV_ROWS;
@@ -97,8 +97,9 @@ hipError_t launch_bf16_gemv(const uint16_t *W, int N, int K, const uint16_t *x, 
     const int rows_per_wg = GV_WAVES * GV_ROWS;
     const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(GV_WAVES * 64);
     const int nc = (K / 8 + 63) / 64;
+    const size_t lds = (size_t)T * K * sizeof(uint16_t);  // x only: many workgroups per CU
 #define MOE_GEMV(NCV) \
-    hipLaunchKernelGGL(bf16_gemv_kernel<NCV>, grid, block, 0, st, W, N, K, x, T, y)
+    hipLaunchKernelGGL(bf16_gemv_kernel<NCV>, grid, block, lds, st, W, N, K, x, T, y)
     if (nc <= 1) MOE_GEMV(1);
     else if (nc <= 2) MOE_GEMV(2);
     else if (nc <= 4) MOE_GEMV(4);
