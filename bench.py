@@ -245,6 +245,23 @@ def main():
                            "kernel_us_avg": round(k_avg * 1e6, 3),
                            "kernel_us_min_batch": round(k_min * 1e6, 3),
                            "launches_timed": 5 * args.live_launches}
+    if not args.no_decode and not args.no_control:
+        # one row through the expert-grouped kernels (MOE_FORCE_GROUPED): the
+        # chunk-invariant way to run a row, its bytes equal to that row's
+        # inside any chunk; same 40 rotated layers as the decode line
+        cfg_g = moe.config(shape, moe.FORCE_GROUPED)
+
+        def gstep1(i):
+            j = i % L
+            moe.forward(cfg_g, layers[j], xs[j:j + 1], y=ys[j:j + 1], workspace=ws,
+                        wstruct=wstructs[j], stream=stream)
+
+        n1 = max(L, args.steps // 8)
+        print(f"[bench] one row, grouped kernels: {n1} steps", file=sys.stderr, flush=True)
+        g1secs, _ = graph_time(gstep1, n1, L, stream)
+        rec["row1_grouped_invariant"] = {"us_per_layer": round(g1secs / n1 * 1e6, 3),
+                                         "note": "one row on the grouped kernels "
+                                                 "(chunk-invariant bytes)"}
     if not args.no_chunk:
         chunk = {}
         xc = inputs.make_x(shape, 1024, seed=1, device="cuda")
