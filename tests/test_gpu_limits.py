@@ -1,0 +1,62 @@
+"""The layer at the edges of what the ABI accepts: the largest row count
+(65,536 rows, 524,288 pairs through the multi-pass sort) and the largest
+shapes (hidden 8192, 1024 experts, top-16, intermediate 4096), each
+against the oracle on sampled rows (rows are independent)."""
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_router_amd as moe
+import oracle
+from block_fp8_mixture_router_amd import inputs
+from tests.gpu_common import OUT_TOL, bits, need_gpu, rel_rows, run_forward, say, x_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _check_rows(shape, host, xh, y, rows):
+    _, acc, _, _ = oracle.forward(shape, host, xh[rows])
+    rel, worst = rel_rows(bits(y.cpu())[rows], acc)
+    say(f"  relL2 {rel:.2e} worst row {worst:.2e} over {len(rows)} rows")
+    assert rel <= OUT_TOL, (rel, worst)
+
+
+def test_max_rows():
+    shape = inputs.DECODE
+    T = 65536
+    say(f"forward T={T} (the maximum)")
+    dev = inputs.make_layer(shape, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    host = dev.to("cpu")
+    x, xh = x_rows(shape, T, seed=65536)
+    y = run_forward(shape, dev, x)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 32767, 32768, T - 2, T - 1],
+                                     np.random.default_rng(1).choice(T, 16, replace=False)]))
+    _check_rows(shape, host, xh, y, rows)
+    del dev, x, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape,T", [
+    (inputs.LayerShape(hidden=8192, n_experts=64, top_k=8, inter=1024, shared_inter=1024), 1),
+    (inputs.LayerShape(hidden=8192, n_experts=64, top_k=8, inter=1024, shared_inter=1024), 40),
+    (inputs.LayerShape(hidden=1024, n_experts=1024, top_k=16, inter=256, shared_inter=0), 3),
+    (inputs.LayerShape(hidden=1024, n_experts=1024, top_k=16, inter=256, shared_inter=0), 300),
+    (inputs.LayerShape(hidden=512, n_experts=8, top_k=2, inter=4096, shared_inter=4096), 2),
+    (inputs.LayerShape(hidden=512, n_experts=8, top_k=2, inter=4096, shared_inter=4096), 33),
+])
+def test_large_shapes(shape, T):
+    say(f"forward {shape} T={T}")
+    dev = inputs.make_layer(shape, seed=1, device="cuda")
+    torch.cuda.synchronize()
+    host = dev.to("cpu")
+    x, xh = x_rows(shape, T, seed=T)
+    y = run_forward(shape, dev, x, shared=shape.shared_inter > 0)
+    rows = np.arange(T) if T <= 8 else np.unique(
+        np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, 6, replace=False)]))
+    _check_rows(shape, host, xh, y, rows)
