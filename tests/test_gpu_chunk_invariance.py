@@ -1,4 +1,4 @@
-"""Chunk invariance (survey row f2): a row's output bytes do not depend on
+"""Chunk invariance: a row's output bytes do not depend on
 the other rows it is computed with. On the expert-grouped kernels every
 per-row result is a function of that row alone, so row t of a 1024-row
 chunk equals, byte for byte, the same row run alone through the grouped
