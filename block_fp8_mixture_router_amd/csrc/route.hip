@@ -148,70 +148,82 @@ hipError_t launch_route_logits(const uint16_t *x, int T, const uint16_t *router_
 
 // ------------------------------------------------------ bounded scores
 
-// A workgroup owns 16 rows x 64 experts; wave w sums the 128-column blocks
-// w, w+4, ...; lane (l16, kq) supplies columns [32kq, 32kq + 32) of each
-// block of its row (A operand) and of its experts' rows (B operands), split
-// over four 16x16x32 MFMAs. Each MFMA starts from zero and its 32-product
-// partial is added in fp64, so a score carries the rounding error of one
-// 32-term fp32 sum per chunk only. A second MFMA on the sign-stripped
-// operands sums |x||w| in fp32 (chained), for the bound. The four waves'
-// partials are added in LDS in a fixed order.
-// 1-D grid: the four expert blocks of a row tile sit 8 workgroups apart, so
-// with workgroups dealt round-robin over the 8 XCDs they share one L2 and
-// the tile's rows come from memory once.
+// A workgroup owns 32 rows x 32 experts (two 16-row tiles times two
+// 16-expert tiles: 256 KiB of operands per workgroup at H = 2048, the least
+// for 256 workgroups over these shapes; the kernel is bound by what each CU
+// pulls from L2); wave w sums the 128-column blocks w, w+4, ...; lane
+// (l16, kq) supplies columns [32kq, 32kq + 32) of each block of its rows
+// (A operands) and of its experts' rows (B operands), split over four
+// 16x16x32 MFMAs. Each MFMA starts from zero and its 32-product partial is
+// added in fp64, so a score carries the rounding error of one 32-term fp32
+// sum per chunk only. A second MFMA on the sign-stripped operands sums
+// |x||w| in fp32 (chained), for the bound. The four waves' partials are
+// added in LDS in a fixed order.
+// 1-D grid: the expert blocks of a row tile sit 8 workgroups apart, so with
+// workgroups dealt round-robin over the 8 XCDs they share one L2 and the
+// tile's rows come from memory once.
 __global__ __launch_bounds__(256) void route_scores_bf16(const uint16_t *__restrict__ x, int T,
                                                          const uint16_t *__restrict__ rw, int H,
                                                          int E, float *__restrict__ S,
                                                          float *__restrict__ A) {
-    __shared__ double sp[4][4][64][4];  // [wave][expert tile][lane][element]
+    __shared__ double sp[4][4][64][4];  // [wave][(row tile, expert tile)][lane][element]
     __shared__ float ap[4][4][64][4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int nE = (E + 63) / 64, nT = (T + 15) / 16;
+    const int nE = (E + 31) / 32, nT = (T + 31) / 32;
     // linear id L -> (row tile, expert block): L = 8 * (nE * g + eb) + r, tile = 8g + r
     const int L = blockIdx.x, r8 = L % 8, q = L / 8;
     const int eb = q % nE, tt = (q / nE) * 8 + r8;
     if (tt >= nT) return;
-    const int e0 = eb * 64, t0 = tt * 16;
+    const int e0 = eb * 32, t0 = tt * 32;
     // rows and experts past the end read a valid row; their results are dropped
-    const uint16_t *xr = x + (int64_t)min(t0 + l16, T - 1) * H + 32 * kq;
-    const uint16_t *wr[4];
+    const uint16_t *xr[2], *wr[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wr[j] = rw + (int64_t)min(e0 + 16 * j + l16, E - 1) * H + 32 * kq;
-    double sd[4][4] = {};
-    v4f aa[4];
+    for (int u = 0; u < 2; ++u) {
+        xr[u] = x + (int64_t)min(t0 + 16 * u + l16, T - 1) * H + 32 * kq;
+        wr[u] = rw + (int64_t)min(e0 + 16 * u + l16, E - 1) * H + 32 * kq;
+    }
+    double sd[2][2][4] = {};  // [row tile][expert tile][element]
+    v4f aa[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aa[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) aa[rt][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     const int KB = H / GROUP;
-    uint4 xv[2][4], wv[2][4][4];
-    auto load = [&](int kb, uint4 (&xs)[4], uint4 (&ws)[4][4]) {
+    uint4 xv[2][2][4], wv[2][2][4];
+    auto load = [&](int kb, uint4 (&xs)[2][4], uint4 (&ws)[2][4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[i] = ld16(xr + kb * GROUP + 8 * i);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ws[j][i] = ld16(wr[j] + kb * GROUP + 8 * i);
+            for (int i = 0; i < 4; ++i) {
+                xs[u][i] = ld16(xr[u] + kb * GROUP + 8 * i);
+                ws[u][i] = ld16(wr[u] + kb * GROUP + 8 * i);
+            }
     };
-    auto step = [&](const uint4 (&xs)[4], const uint4 (&ws)[4][4]) {
+    auto step = [&](const uint4 (&xs)[2][4], const uint4 (&ws)[2][4]) {
         constexpr uint32_t M = 0x7FFF7FFFu;  // clears both bf16 sign bits
         const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const v8bf af = __builtin_bit_cast(v8bf, xs[i]);
-            const v8bf aabs = __builtin_bit_cast(
-                v8bf, make_uint4(xs[i].x & M, xs[i].y & M, xs[i].z & M, xs[i].w & M));
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 w = ws[j][i];
-                const v4f p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    af, __builtin_bit_cast(v8bf, w), z, 0, 0, 0);
+            for (int rt = 0; rt < 2; ++rt) {
+                const uint4 xa = xs[rt][i];
+                const v8bf af = __builtin_bit_cast(v8bf, xa);
+                const v8bf aabs =
+                    __builtin_bit_cast(v8bf, make_uint4(xa.x & M, xa.y & M, xa.z & M, xa.w & M));
 #pragma unroll
-                for (int k = 0; k < 4; ++k) sd[j][k] += (double)p[k];
-                aa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    aabs, __builtin_bit_cast(v8bf, make_uint4(w.x & M, w.y & M, w.z & M, w.w & M)),
-                    aa[j], 0, 0, 0);
+                for (int j = 0; j < 2; ++j) {
+                    const uint4 w = ws[j][i];
+                    const v4f p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af, __builtin_bit_cast(v8bf, w), z, 0, 0, 0);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) sd[rt][j][k] += (double)p[k];
+                    aa[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        aabs,
+                        __builtin_bit_cast(v8bf, make_uint4(w.x & M, w.y & M, w.z & M, w.w & M)),
+                        aa[rt][j], 0, 0, 0);
+                }
             }
-        }
     };
     // this wave's blocks kb = wave + 4i, i < nit; two blocks of loads in flight
     const int nit = KB > wave ? (KB - wave + 3) / 4 : 0;
@@ -226,24 +238,28 @@ __global__ __launch_bounds__(256) void route_scores_bf16(const uint16_t *__restr
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sp[wave][j][lane][i] = sd[j][i];
-            ap[wave][j][lane][i] = aa[j][i];
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sp[wave][2 * rt + j][lane][k] = sd[rt][j][k];
+                ap[wave][2 * rt + j][lane][k] = aa[rt][j][k];
+            }
     __syncthreads();
-    // wave w finishes expert tile w; element i of lane (l16, kq) = row 4kq + i
-    const int j = wave, e = e0 + 16 * j + l16;
+    // wave w finishes tile (rt, j) = (w / 2, w % 2); element k of lane
+    // (l16, kq) = row 16rt + 4kq + k, expert 16j + l16
+    const int tl = wave, rt = wave >> 1, j = wave & 1;
+    const int e = e0 + 16 * j + l16;
     if (e >= E) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * kq + i;
+    for (int k = 0; k < 4; ++k) {
+        const int t = t0 + 16 * rt + 4 * kq + k;
         if (t >= T) continue;
-        const double sv = ((sp[0][j][lane][i] + sp[1][j][lane][i]) + sp[2][j][lane][i]) +
-                          sp[3][j][lane][i];
-        const float av = ((ap[0][j][lane][i] + ap[1][j][lane][i]) + ap[2][j][lane][i]) +
-                         ap[3][j][lane][i];
+        const double sv = ((sp[0][tl][lane][k] + sp[1][tl][lane][k]) + sp[2][tl][lane][k]) +
+                          sp[3][tl][lane][k];
+        const float av = ((ap[0][tl][lane][k] + ap[1][tl][lane][k]) + ap[2][tl][lane][k]) +
+                         ap[3][tl][lane][k];
         S[(int64_t)t * E + e] = (float)sv;
         A[(int64_t)t * E + e] = av;
     }
@@ -252,7 +268,7 @@ __global__ __launch_bounds__(256) void route_scores_bf16(const uint16_t *__restr
 hipError_t launch_route_scores(const uint16_t *x, int T, const uint16_t *router_w, int H, int E,
                                float *S, float *A, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    const int nE = (E + 63) / 64, nT = (T + 15) / 16;
+    const int nE = (E + 31) / 32, nT = (T + 31) / 32;
     const int groups = (nT + 7) / 8;  // row tiles come in groups of 8 (one per XCD)
     hipLaunchKernelGGL(route_scores_bf16, dim3(groups * nE * 8), dim3(256), 0, st, x, T,
                        router_w, H, E, S, A);
