@@ -379,15 +379,19 @@ constexpr int EXACT_BATCH = 4;  // candidate rows fetched per round trip
 
 // One wave per row t. NL logits per lane (expert e = lane + 64i), NB 16-byte
 // chunks of the x row per lane. Writes ids/weights; with gate_w also gamma;
-// with qx also the 1x128 quantisation of x[t].
-template <int NL, int NB>
-__global__ __launch_bounds__(256) void route_topk_bounded_kernel(
+// with qx also the 1x128 quantisation of x[t]. With SPLIT the workgroup has
+// eight waves: waves 0-3 pick the experts of rows 4b..4b+3 and waves 4-7
+// compute the same rows' gamma and FP8 groups, so neither chain waits for
+// the other.
+template <int NL, int NB, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 512 : 256) void route_topk_bounded_kernel(
     const float *__restrict__ S, const float *__restrict__ A, int T, int E, int K,
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ rw,
     const float *__restrict__ bias, uint32_t flags, int H, int32_t *__restrict__ ids,
     float *__restrict__ wts, const uint16_t *__restrict__ gate_w, float *__restrict__ gamma,
     uint8_t *__restrict__ qx, float *__restrict__ sx) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = blockIdx.x * 4 + ((threadIdx.x >> 6) & 3);
+    const bool side = SPLIT && (threadIdx.x >> 8) != 0;
     const int lane = threadIdx.x & 63;
     if (t >= T) return;  // whole waves leave together
     const int nc8 = H / 8;
@@ -397,8 +401,59 @@ __global__ __launch_bounds__(256) void route_topk_bounded_kernel(
     for (int i = 0; i < NB; ++i) {
         const int c = lane + WAVE * i;
         xv[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-        gv[i] = (gate_w && c < nc8) ? ld16(gate_w + c * 8) : make_uint4(0, 0, 0, 0);
+        gv[i] = ((!SPLIT || side) && gate_w && c < nc8) ? ld16(gate_w + c * 8)
+                                                        : make_uint4(0, 0, 0, 0);
     }
+    // gamma[t] and the FP8 groups of x[t]
+    auto side_work = [&]() {
+        if (gate_w) {
+            float z = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int c = lane + WAVE * i;
+                if (c < nc8) {
+                    const uint4 b = gv[i];
+                    const uint32_t av[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                    const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        z = fmaf(bf16_lo(av[k]), bf16_lo(bv[k]), z);
+                        z = fmaf(bf16_hi(av[k]), bf16_hi(bv[k]), z);
+                    }
+                }
+            }
+            z = wave_allsum(z);
+            if (lane == 0) gamma[t] = 1.0f / (1.0f + expf(-z));
+        }
+        if (qx) {
+            // 16 lanes per 128-column group: chunk c = lane + 64i is in group c / 16
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int c = lane + WAVE * i;
+                if (WAVE * i >= nc8) break;  // wave-uniform
+                const uint4 v = xv[i];
+                float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                              bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+                float amax = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
+                amax = group16_max(amax);
+                const float sc = group_scale(amax);
+                if (c < nc8) {
+                    uint2 out;
+                    out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+                    out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+                    *reinterpret_cast<uint2 *>(qx + (int64_t)t * H + c * 8) = out;
+                    if ((c & 15) == 0) sx[(int64_t)t * (H / GROUP) + c / 16] = sc;
+                }
+            }
+        }
+    };
+    if (side) {
+        side_work();
+        return;
+    }
+
     // intervals [lo, hi] that hold each exact logit
     float lo[NL], hi[NL];
 #pragma unroll
@@ -495,48 +550,7 @@ __global__ __launch_bounds__(256) void route_topk_bounded_kernel(
         for (int i = 0; i < NL; ++i) ix[i] = lane + WAVE * i < E ? lane + WAVE * i : 0x7FFFFFFF;
         topk_select_n<NL>(val, ix, K, lane, ids + (int64_t)t * K, wts + (int64_t)t * K);
     }
-    if (gate_w) {
-        float z = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c = lane + WAVE * i;
-            if (c < nc8) {
-                const uint4 b = gv[i];
-                const uint32_t av[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-                const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    z = fmaf(bf16_lo(av[k]), bf16_lo(bv[k]), z);
-                    z = fmaf(bf16_hi(av[k]), bf16_hi(bv[k]), z);
-                }
-            }
-        }
-        z = wave_allsum(z);
-        if (lane == 0) gamma[t] = 1.0f / (1.0f + expf(-z));
-    }
-    if (qx) {
-        // 16 lanes per 128-column group: chunk c = lane + 64i is in group c / 16
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c = lane + WAVE * i;
-            if (WAVE * i >= nc8) break;  // wave-uniform
-            const uint4 v = xv[i];
-            float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            float amax = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
-            amax = group16_max(amax);
-            const float sc = group_scale(amax);
-            if (c < nc8) {
-                uint2 out;
-                out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
-                out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
-                *reinterpret_cast<uint2 *>(qx + (int64_t)t * H + c * 8) = out;
-                if ((c & 15) == 0) sx[(int64_t)t * (H / GROUP) + c / 16] = sc;
-            }
-        }
-    }
+    if (!SPLIT) side_work();
 }
 
 template <int NL>
@@ -545,16 +559,26 @@ static hipError_t launch_bounded_nl(const float *S, const float *A, int T, int E
                                     uint32_t flags, int H, int32_t *ids, float *wts,
                                     const uint16_t *gate_w, float *gamma, uint8_t *qx,
                                     float *sx, hipStream_t st) {
-    const dim3 grid((T + 3) / 4), block(256);
+    const dim3 grid((T + 3) / 4);
     const int nb = (H / 8 + WAVE - 1) / WAVE;
-#define MOE_BOUNDED(NBV)                                                                     \
-    hipLaunchKernelGGL((route_topk_bounded_kernel<NL, NBV>), grid, block, 0, st, S, A, T, E, \
-                       K, x, rw, bias, flags, H, ids, wts, gate_w, gamma, qx, sx)
-    if (nb <= 1) MOE_BOUNDED(1);
-    else if (nb <= 2) MOE_BOUNDED(2);
-    else if (nb <= 4) MOE_BOUNDED(4);
-    else if (nb <= 8) MOE_BOUNDED(8);
-    else MOE_BOUNDED(16);
+    // side waves for gamma and the FP8 groups when there is such work (and
+    // the row fits the 256 registers a wave gets at eight waves per CU)
+    const bool split = (gate_w || qx) && nb <= 8;
+#define MOE_BOUNDED(NBV, SP)                                                                  \
+    hipLaunchKernelGGL((route_topk_bounded_kernel<NL, NBV, SP>), grid, dim3(SP ? 512 : 256), 0, \
+                       st, S, A, T, E, K, x, rw, bias, flags, H, ids, wts, gate_w, gamma, qx, sx)
+    if (split) {
+        if (nb <= 1) MOE_BOUNDED(1, true);
+        else if (nb <= 2) MOE_BOUNDED(2, true);
+        else if (nb <= 4) MOE_BOUNDED(4, true);
+        else MOE_BOUNDED(8, true);
+    } else {
+        if (nb <= 1) MOE_BOUNDED(1, false);
+        else if (nb <= 2) MOE_BOUNDED(2, false);
+        else if (nb <= 4) MOE_BOUNDED(4, false);
+        else if (nb <= 8) MOE_BOUNDED(8, false);
+        else MOE_BOUNDED(16, false);
+    }
 #undef MOE_BOUNDED
     return hipGetLastError();
 }
