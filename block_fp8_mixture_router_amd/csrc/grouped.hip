@@ -679,9 +679,11 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
 
 // One launch for both gate/up products: the shared expert's tiles come
 // first (they need only x and start at once; bound by L2), then the routed
-// experts' tiles (bound by HBM), so the two overlap.
-template <int PD>
-__global__ __launch_bounds__(256, 2) void expert_gateup_kernel(GroupedArgs a, int n_shared) {
+// experts' tiles (bound by HBM), so the two overlap. OCC workgroups per CU:
+// a launch with fewer workgroups than CUs (a few rows) runs one per CU with
+// a ring twice as deep; the arithmetic, K steps in order, is the same.
+template <int PD, int OCC>
+__global__ __launch_bounds__(256, OCC) void expert_gateup_kernel(GroupedArgs a, int n_shared) {
     if ((int)blockIdx.x < n_shared) {
         shared_gateup_block<PD>(a, blockIdx.x);
         return;
@@ -693,10 +695,13 @@ hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st) {
     const int n_shared = a.Is > 0 ? ((a.T + SRG - 1) / SRG) * (a.Is / 64) : 0;
     const dim3 grid((unsigned)(n_shared + a.max_tiles * (a.I / GROUP)));
     if (grid.x == 0) return hipSuccess;
-    if ((a.H / GROUP) % 2 == 0)
-        hipLaunchKernelGGL(expert_gateup_kernel<2>, grid, dim3(256), 0, st, a, n_shared);
+    const int kb = a.H / GROUP;
+    if (grid.x <= 256 && kb % 4 == 0)
+        hipLaunchKernelGGL((expert_gateup_kernel<4, 1>), grid, dim3(256), 0, st, a, n_shared);
+    else if (kb % 2 == 0)
+        hipLaunchKernelGGL((expert_gateup_kernel<2, 2>), grid, dim3(256), 0, st, a, n_shared);
     else
-        hipLaunchKernelGGL(expert_gateup_kernel<1>, grid, dim3(256), 0, st, a, n_shared);
+        hipLaunchKernelGGL((expert_gateup_kernel<1, 2>), grid, dim3(256), 0, st, a, n_shared);
     return hipGetLastError();
 }
 
