@@ -60,3 +60,21 @@ def test_large_shapes(shape, T):
     rows = np.arange(T) if T <= 8 else np.unique(
         np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, 6, replace=False)]))
     _check_rows(shape, host, xh, y, rows)
+
+
+@pytest.mark.parametrize("T", [1, 37])
+def test_variants_at_odd_shape(T):
+    """Both variants on a shape with three 128-blocks everywhere (odd block
+    counts: the one-step rings and the odd column-block counts)."""
+    shape = inputs.LayerShape(hidden=384, n_experts=12, top_k=3, inter=384, shared_inter=384)
+    x, xh = x_rows(shape, T, seed=70 + T)
+    for flags, oflags, fp8 in ((moe.NO_ACT_QUANT, oracle.NO_ACT_QUANT, False),
+                               (moe.SHARED_FP8, oracle.SHARED_FP8, True)):
+        dev = inputs.make_layer(shape, seed=3, device="cuda", shared_fp8=fp8)
+        torch.cuda.synchronize()
+        host = dev.to("cpu")
+        y = run_forward(shape, dev, x, flags)
+        _, acc, _, _ = oracle.forward(shape, host, xh, flags=oflags)
+        rel, worst = rel_rows(bits(y.cpu()), acc)
+        say(f"  flags {flags}: relL2 {rel:.2e} worst row {worst:.2e}")
+        assert rel <= OUT_TOL, (flags, rel, worst)
