@@ -241,3 +241,16 @@ def test_bf16_gemv_refusals():
     assert L.moe_bf16_gemv(W, 16, 2048, X, 1, Y + 1, None) == -3
     assert L.moe_bf16_gemv(W, 16, 2048, X, 1, X, None) == -5     # y aliases x
     assert L.moe_bf16_gemv(W, 16, 2048, X, 1, Y, None) == -5     # no gfx950 device here
+
+
+def test_flag_values_match_the_header():
+    src = open(HEADER).read()
+    vals = {m.group(1): 1 << int(m.group(2))
+            for m in re.finditer(r"#define\s+MOE_(\w+)\s+\(1u\s*<<\s*(\d+)\)", src)}
+    assert vals == {"SHARED_FP8": moe.SHARED_FP8, "LOGITS_FP32": moe.LOGITS_FP32,
+                    "NO_ACT_QUANT": moe.NO_ACT_QUANT, "FORCE_GEMV": moe.FORCE_GEMV,
+                    "FORCE_GROUPED": moe.FORCE_GROUPED}
+    # and the weights struct has the header's fields, in order
+    body = re.search(r"typedef struct \{(.*?)\} moe_weights;", src, re.S).group(1)
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == [n for n, _ in moe.Weights._fields_]
