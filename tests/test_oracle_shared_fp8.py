@@ -75,3 +75,16 @@ def test_shared_fp8_generator_matches_routed_recipe():
         assert torch.all(blk == 448.0)
         deq = (f.view(r // 128, 128, c // 128, 128) * sc[:, None, :, None]).reshape(r, c)
         assert abs(float(deq.std()) - 0.02) < 0.002
+
+
+def test_oracle_weights_struct_matches_its_header():
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} oracle_weights;", hdr, re.S).group(1)
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == [n for n, _ in oracle._Weights._fields_]
+    flags = {m.group(1): 1 << int(m.group(2))
+             for m in re.finditer(r"#define\s+ORACLE_(\w+)\s+\(1u\s*<<\s*(\d+)\)", hdr)}
+    assert flags == {"NO_ACT_QUANT": oracle.NO_ACT_QUANT, "LOGITS_FP32": oracle.LOGITS_FP32,
+                     "SHARED_FP8": oracle.SHARED_FP8}
