@@ -1,7 +1,10 @@
 """Builds libmoe.so (the gfx950 HIP library behind include/moe.h) in-tree.
 
 Every source is compiled for gfx950 only, with IEEE fp32 division and square
-root, denormals kept, no fast-math, and packed-fp32 instructions disabled.
+root, denormals kept, no fast-math, no implicit contraction of a*b+c into one
+rounding (every fused multiply-add in the kernels is an explicit fmaf/fma, so
+each rounding point is the one written), and packed-fp32 instructions
+disabled.
 Objects go to ``_build/``; the library lands next to this file.
 """
 from __future__ import annotations
@@ -21,7 +24,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-    "-fno-fast-math", "-ffp-contract=fast",
+    "-fno-fast-math", "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

@@ -582,16 +582,16 @@ __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
 
 // ---------------------------------------------------- shared gate / up
 // Tile: 64 rows x 64 columns of Is. Wave w owns 16 columns of gate and up.
-// All 16 row tiles of a column block read the same weight rows; walking K in
-// the same order they would request the same lines at the same moment, which
-// measured over 2x slower. So tile r walks the K steps starting at step
-// 2r (mod KB). Each K step's partial product (four chained MFMAs from zero,
-// 128 columns) does not depend on the tile, and the partials are added in
-// fp64, so a row's result does not depend on which tile it sits in (up to
-// fp64 rounding, far below the bf16 rounding that follows). Each lane reads 64 contiguous bytes
-// of its weight row per 128 columns of H and splits them over four MFMAs;
-// the LDS activation fragments follow the same column split. Loads run two
-// K steps ahead, unconditionally (see the routed kernels).
+// Per 128-column K step, four chained bf16 MFMAs from zero give the step's
+// partial product Q (an MFMA output element depends only on its own row of
+// A and column of B), and the partials are added in fp64 in ascending K
+// order, d = ((0 + Q_0) + Q_1) + ...: every row's gs and us are the same
+// bits whatever tile it sits in and however many rows come with it, and the
+// one-row kernel repeats this sequence exactly. Each lane reads 64
+// contiguous bytes of its weight row per 128 columns of H and splits them
+// over four MFMAs (MFMA i takes elements [32 kq + 8 i, +8) of lane
+// (l16, kq)); the LDS activation fragments follow the same split. Loads run
+// two K steps ahead, unconditionally (see the routed kernels).
 
 constexpr int SR = 32;  // rows per combine tile
 
@@ -616,10 +616,9 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
     const uint8_t *gp = reinterpret_cast<const uint8_t *>(a.sh_gate + (int64_t)n * H) + 64 * kq;
     const uint8_t *up = reinterpret_cast<const uint8_t *>(a.sh_up + (int64_t)n * H) + 64 * kq;
     double dg[NRT][4] = {}, du[NRT][4] = {};
-    const int krot = (2 * (blk / snb)) % KB;
     uint4 bg[PD][4], bu[PD][4], av[PD][ARR][2];
     auto load = [&](int kb, uint4 (&g)[4], uint4 (&u)[4], uint4 (&x)[ARR][2]) {
-        const int off = ((kb + krot) % KB) * GROUP * 2;
+        const int off = kb * GROUP * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             g[i] = ld16(gp + off + 16 * i);
