@@ -120,26 +120,30 @@ def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def layer_table(layers, device="cuda"):
-    """Device array of moe_weights structs for moe_forward_stack (the caller
-    keeps the layers' tensors alive while the table is in use)."""
-    import torch
-    rows = [[getattr(weights_struct(lw), k) or 0 for k, _ in Weights._fields_] for lw in layers]
-    return torch.tensor(rows, dtype=torch.int64).to(device)
+def weights_array(layers):
+    """A host array of moe_weights structs for moe_forward_stack, from
+    objects with the tensor attributes of inputs.LayerWeights or from Weights
+    structs (the caller keeps the layers' tensors alive)."""
+    structs = [lw if isinstance(lw, Weights) else weights_struct(lw) for lw in layers]
+    return (Weights * len(structs))(*structs)
 
 
-def forward_stack(cfg: Config, table, n_layers: int, x, y=None, ys=None, eps: float = 1e-6,
+def forward_stack(cfg: Config, layers, x, y=None, ys=None, eps: float = 1e-6,
                   workspace=None, stream=None):
-    """n_layers layers in sequence with RMS renormalisation between them, one
-    launch; table from layer_table(). Returns the last layer's output."""
+    """The layers in sequence on the rows x (T <= 4), each layer after the
+    first renormalising its predecessor's output in its own launch; equals
+    forward() and rms_renorm() called in turn, bit for bit. layers: a list
+    (see weights_array) or an array from weights_array(). ys, if given, gets
+    every layer's output [n_layers, T, H]. Returns the last layer's output."""
     import torch
     T = x.shape[0]
+    arr = layers if isinstance(layers, ctypes.Array) else weights_array(layers)
     if y is None:
         y = torch.empty_like(x)
     if workspace is None:
         workspace = alloc_workspace(cfg, max(T, 1), x.device)
     _check("moe_forward_stack", lib().moe_forward_stack(
-        ctypes.byref(cfg), _ptr(table), n_layers, _ptr(x), T, eps, _ptr(y), _ptr(ys),
+        ctypes.byref(cfg), arr, len(arr), _ptr(x), T, eps, _ptr(y), _ptr(ys),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 

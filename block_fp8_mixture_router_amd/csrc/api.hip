@@ -87,9 +87,24 @@ constexpr int BOUNDED_MIN_ROWS = 16;
 
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+bool is_variant(const moe_config *c) {
+    return (c->flags & (MOE_SHARED_FP8 | MOE_NO_ACT_QUANT)) != 0;
+}
+
+// The most rows the one-row path can take for this config (0 if none): it
+// alone fixes the size of the decode handoff regions, so that no region of
+// the workspace moves with T (a grouped call's plain data can never sit
+// where a later decode call polls for tagged words).
+int decode_rows_max(const moe_config *c) {
+    if (is_variant(c)) return 0;
+    for (int t = DECODE_MAX_ROWS; t >= 1; --t)
+        if (decode_fits(t, c->hidden, c->top_k, c->inter, c->shared_inter)) return t;
+    return 0;
+}
+
 struct Layout {
-    size_t sync, dlogits, dgamma, dhs, dh, dy, logits, absums, ids, wts, gamma, hs, qx, sx, offsets,
-        perm, tiles, n_tiles, qh, sh, stage, hb, sperm, stiles, sntiles, sqh, ssh, es;
+    size_t sync, dlogits, dgamma, dhs, dh, ybuf, logits, absums, ids, wts, gamma, hs, qx, sx,
+        offsets, perm, tiles, n_tiles, qh, sh, stage, hb, sperm, stiles, sntiles, sqh, ssh, es;
     size_t total;
     int max_tiles;
 };
@@ -108,17 +123,17 @@ Layout layout_of(const moe_config *c, int T) {
     L.sync = take((size_t)SYNC_WORDS * 4);
     // The decode path hands logits, gamma, hs and h between workgroups as
     // 64-bit tagged words in DECODE_REPLICAS copies (regions d*, used by it
-    // alone, so no plain value can ever be read as a tag); the grouped path
-    // keeps one plain copy of logits (fp32), gamma (fp32) and hs (bf16).
-    // Every size is non-decreasing in T, so a workspace sized for max_rows
+    // alone, so no plain value can ever be read as a tag), sized for the
+    // most rows it can take whatever T is; the grouped path keeps one plain
+    // copy of logits (fp32), gamma (fp32) and hs (bf16) after them. Every
+    // other size is non-decreasing in T, so a workspace sized for max_rows
     // serves every T <= max_rows.
-    const size_t R = DECODE_REPLICAS, td = t < DECODE_MAX_ROWS ? t : DECODE_MAX_ROWS;
-    // (two halves each: consecutive layers of a stack alternate between them)
-    L.dlogits = take(2 * R * td * E * 8);
-    L.dgamma = take(2 * R * td * 8);
-    L.dhs = take(2 * R * td * Is * 8);
-    L.dh = take(2 * R * td * K * I * 8);
-    L.dy = take(2 * R * td * H * 8);
+    const size_t R = DECODE_REPLICAS, td = (size_t)decode_rows_max(c);
+    L.dlogits = take(R * td * E * 8);
+    L.dgamma = take(R * td * 8);
+    L.dhs = take(R * td * Is * 8);
+    L.dh = take(R * td * K * I * 8);
+    L.ybuf = take(2 * td * H * 2);  // a stack's layer outputs, alternating
     L.logits = take(t * E * 4);  // exact logits, or the bounded scores S
     L.absums = take(t * E * 4);  // the bounded scores' sums of |x||w|
     L.ids = take(t * K * 4);
@@ -279,29 +294,50 @@ moe_status moe_route(const moe_config *cfg, const void *x, int32_t T, const void
 }
 
 namespace {
-void fill_decode_args(FusedArgs &a, const moe_config *cfg, const moe_weights *w, const void *x,
-                      int T, void *y, void *workspace, const Layout &L) {
+void fill_decode_args(FusedArgs &a, const moe_config *cfg, const moe_weights *w, int T,
+                      void *workspace, const Layout &L) {
     a.T = T; a.H = cfg->hidden; a.E = cfg->n_experts; a.K = cfg->top_k; a.I = cfg->inter;
     a.Is = cfg->shared_inter;
     a.flags = cfg->flags;
-    a.x = static_cast<const uint16_t *>(x);
-    if (w) {
-        a.router_w = static_cast<const uint16_t *>(w->router_w);
-        a.bias = w->router_bias;
-        a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
-        a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
-        a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
-        a.sh_up = static_cast<const uint16_t *>(w->sh_up);
-        a.sh_down = static_cast<const uint16_t *>(w->sh_down);
-        a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
-    }
+    a.router_w = static_cast<const uint16_t *>(w->router_w);
+    a.bias = w->router_bias;
+    a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+    a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+    a.sh_gate = static_cast<const uint16_t *>(w->sh_gate);
+    a.sh_up = static_cast<const uint16_t *>(w->sh_up);
+    a.sh_down = static_cast<const uint16_t *>(w->sh_down);
+    a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
     a.logits = at<uint64_t>(workspace, L.dlogits);
     a.gamma = at<uint64_t>(workspace, L.dgamma);
     a.hs = at<uint64_t>(workspace, L.dhs);
     a.h = at<uint64_t>(workspace, L.dh);
     a.sync = at<uint32_t>(workspace, L.sync);
-    a.y = static_cast<uint16_t *>(y);
     a.nwg = device_cus();
+}
+
+// the checks of moe_forward on one layer's weights
+moe_status check_weights(const moe_config *cfg, const moe_weights *w) {
+    if (!w->router_w || !w->w_gate || !w->s_gate || !w->w_up || !w->s_up || !w->w_down ||
+        !w->s_down)
+        return MOE_E_NULL;
+    const bool shared = cfg->shared_inter > 0;
+    if (shared && (!w->sh_gate || !w->sh_up || !w->sh_down || !w->sh_gate_w)) return MOE_E_NULL;
+    const void *ptrs[] = {w->router_w, w->w_gate, w->w_up, w->w_down};
+    for (const void *p : ptrs)
+        if (!al16(p)) return MOE_E_ALIGN;
+    const void *scalars[] = {w->s_gate, w->s_up, w->s_down, w->router_bias};
+    for (const void *p : scalars)
+        if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
+    if (shared && (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down) ||
+                   !al16(w->sh_gate_w)))
+        return MOE_E_ALIGN;
+    if (shared && (cfg->flags & MOE_SHARED_FP8)) {
+        if (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down) return MOE_E_NULL;
+        const void *ss[] = {w->sh_s_gate, w->sh_s_up, w->sh_s_down};
+        for (const void *p : ss)
+            if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
+    }
+    return MOE_OK;
 }
 }  // namespace
 
@@ -312,27 +348,10 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     if (T < 0 || T > MAX_ROWS) return MOE_E_SHAPE;
     if (T == 0) return MOE_OK;
     if (!w || !x || !y || !workspace) return MOE_E_NULL;
-    if (!w->router_w || !w->w_gate || !w->s_gate || !w->w_up || !w->s_up || !w->w_down ||
-        !w->s_down)
-        return MOE_E_NULL;
+    if ((s = check_weights(cfg, w)) != MOE_OK) return s;
+    if (!al16(x) || !al16(y)) return MOE_E_ALIGN;
     const bool shared = cfg->shared_inter > 0;
-    if (shared && (!w->sh_gate || !w->sh_up || !w->sh_down || !w->sh_gate_w)) return MOE_E_NULL;
-    const void *ptrs[] = {x, y, w->router_w, w->w_gate, w->w_up, w->w_down};
-    for (const void *p : ptrs)
-        if (!al16(p)) return MOE_E_ALIGN;
-    const void *scalars[] = {w->s_gate, w->s_up, w->s_down, w->router_bias};
-    for (const void *p : scalars)
-        if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
-    if (shared && (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down) ||
-                   !al16(w->sh_gate_w)))
-        return MOE_E_ALIGN;
     const bool sfp8 = shared && (cfg->flags & MOE_SHARED_FP8);
-    if (sfp8) {
-        if (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down) return MOE_E_NULL;
-        const void *ss[] = {w->sh_s_gate, w->sh_s_up, w->sh_s_down};
-        for (const void *p : ss)
-            if (reinterpret_cast<uintptr_t>(p) & 3u) return MOE_E_ALIGN;
-    }
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
     const Layout L = layout_of(cfg, T);
     if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
@@ -346,15 +365,17 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     int32_t *ids = at<int32_t>(workspace, L.ids);
     float *wts = at<float>(workspace, L.wts);
     float *gamma = at<float>(workspace, L.gamma);
-    const bool fits = decode_fits(T, H, K, cfg->inter, shared ? cfg->shared_inter : 0);
+    const bool fits = T <= decode_rows_max(cfg);
     const bool noq = (cfg->flags & MOE_NO_ACT_QUANT) != 0;
-    const bool variant = noq || (cfg->flags & MOE_SHARED_FP8);  // grouped kernels only
+    const bool variant = is_variant(cfg);  // grouped kernels only
     if ((cfg->flags & MOE_FORCE_GEMV) && (!fits || variant)) return MOE_E_UNSUPPORTED;
     const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
-                      (!(cfg->flags & MOE_FORCE_GROUPED) && !variant && T <= 4 && fits);
+                      (!(cfg->flags & MOE_FORCE_GROUPED) && !variant && fits);
     if (gemv) {
         FusedArgs a{};
-        fill_decode_args(a, cfg, w, x, T, y, workspace, L);
+        fill_decode_args(a, cfg, w, T, workspace, L);
+        a.x = xb;
+        a.y = static_cast<uint16_t *>(y);
         if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
         MOE_TRY(launch_decode_fused(a, st));
         return MOE_OK;
@@ -443,36 +464,49 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
 moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, int32_t n_layers,
                              const void *x, int32_t T, float eps, void *y, void *ys,
                              void *workspace, size_t workspace_bytes, void *stream) {
-    static_assert(sizeof(LayerPtrs) == sizeof(moe_weights), "layer table layout");
     moe_status s = check_cfg(cfg);
     if (s != MOE_OK) return s;
     if (cfg->flags & (MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_NO_ACT_QUANT | MOE_SHARED_FP8))
         return MOE_E_UNSUPPORTED;
-    if (T < 0 || n_layers < 0 || n_layers > MAX_STACK_LAYERS) return MOE_E_SHAPE;
+    if (T < 0 || T > MAX_ROWS || n_layers < 0 || n_layers > MAX_STACK_LAYERS) return MOE_E_SHAPE;
     if (!(eps >= 0.0f) || eps > 1.0f) return MOE_E_SHAPE;
     if (T == 0 || n_layers == 0) return MOE_OK;
     if (!layers || !x || !y || !workspace) return MOE_E_NULL;
-    if (!al16(x) || !al16(y) || (ys && !al16(ys)) || !al16(layers)) return MOE_E_ALIGN;
+    for (int l = 0; l < n_layers; ++l)
+        if ((s = check_weights(cfg, &layers[l])) != MOE_OK) return s;
+    if (!al16(x) || !al16(y) || (ys && !al16(ys))) return MOE_E_ALIGN;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
     const Layout L = layout_of(cfg, T);
     if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
     if (x == y) return MOE_E_UNSUPPORTED;
-    if (!decode_fits(T, cfg->hidden, cfg->top_k, cfg->inter, cfg->shared_inter, true))
-        return MOE_E_UNSUPPORTED;
+    if (T > decode_rows_max(cfg)) return MOE_E_UNSUPPORTED;
     if (!current_device_ok()) return MOE_E_UNSUPPORTED;
-    FusedArgs a{};
-    fill_decode_args(a, cfg, nullptr, x, T, y, workspace, L);
-    if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
-    a.layers = reinterpret_cast<const LayerPtrs *>(layers);
-    a.n_layers = n_layers;
-    a.eps = eps;
-    a.ytag = at<uint64_t>(workspace, L.dy);
-    a.ys = static_cast<uint16_t *>(ys);
-    // the one-launch stack kernel is switched off (launch_decode_stack
-    // refuses): every valid call ends here without touching the device
-    const hipError_t e = launch_decode_stack(a, static_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return MOE_E_UNSUPPORTED;
-    return e == hipSuccess ? MOE_OK : MOE_E_LAUNCH;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t row_elems = (size_t)T * cfg->hidden;
+    uint16_t *ybuf = at<uint16_t>(workspace, L.ybuf);
+    uint16_t *ysb = static_cast<uint16_t *>(ys);
+    const uint16_t *prev = nullptr;
+    for (int l = 0; l < n_layers; ++l) {
+        FusedArgs a{};
+        fill_decode_args(a, cfg, &layers[l], T, workspace, L);
+        if (a.nwg <= 0 || a.nwg > SYNC_WORDS - SYNC_FLAGS) return MOE_E_UNSUPPORTED;
+        // layer l > 0 renormalises the output of layer l - 1 in its prologue
+        if (l == 0) a.x = static_cast<const uint16_t *>(x);
+        else {
+            a.y_prev = prev;
+            a.eps = eps;
+        }
+        uint16_t *out = ysb ? ysb + (size_t)l * row_elems : ybuf + (size_t)(l & 1) * row_elems;
+        if (l == n_layers - 1) {
+            a.y = static_cast<uint16_t *>(y);
+            a.y2 = ysb ? out : nullptr;
+        } else {
+            a.y = out;
+        }
+        MOE_TRY(launch_decode_fused(a, st));
+        prev = out;
+    }
+    return MOE_OK;
 }
 
 }  // extern "C"

@@ -174,11 +174,51 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// fp32 rounded to the nearest bf16 value (kept as fp32)
+__device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(f32_to_bf16(f) << 16); }
+
+// ------------------------------------------------------------ matrix cores
+// Block products shared by the expert-grouped kernels and the one-row
+// kernel. An output element of these MFMAs depends only on its own row of A
+// and column of B: on gfx950 it is the same bits at every position in the
+// tile, whatever the other rows and columns hold, and with the operands
+// swapped. So a row computed alone, in any tile position, gets the bits it
+// gets inside a chunk, provided the same operand bytes meet in the same
+// instruction sequence.
+
+__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// One 128x128 weight block: v_mfma_scale_f32_16x16x128_f8f6f4 on e4m3
+// operands, from zero, E8M0 scales 127 (x1). Lane (l16, kq) supplies A row
+// l16 and B column l16, bytes [32 kq, 32 kq + 32) of the block; element i of
+// its result is row 4 kq + i, column l16.
+__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+// bf16 16x16x32 MFMA accumulating into c. Lane (l16, kq) supplies A row l16
+// and B column l16, eight bf16 elements each.
+__device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row RMS normalisation between stacked layers, shared by the stand-alone
-// kernel and the multi-layer decode kernel so both give the same bits: each
-// thread adds the exact squares of its 8-value chunks in element order (fp64),
-// then the wave and workgroup sums follow a fixed order; the scale is
-// 1 / sqrt(fp32(sum / H) + eps) in fp32.
+// kernel and the renormalising prologue of the one-row kernel so both give
+// the same bits. A workgroup of 256 threads owns the row; thread tid holds
+// the 16-byte chunks tid + 256 i, i < RENORM_CHUNKS (H <= 8192). It adds the
+// exact squares of its chunks in element order (fp64), a DPP wave sum and
+// the four wave totals in order give the row sum, the scale is
+// 1 / sqrt(fp32(sum / H) + eps) in fp32 and x = bf16(fp32(y * scale)).
+constexpr int RENORM_CHUNKS = 4;
+
 __device__ __forceinline__ double sumsq8(const float (&v)[8], double acc) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc = fma((double)v[k], (double)v[k], acc);
@@ -187,6 +227,37 @@ __device__ __forceinline__ double sumsq8(const float (&v)[8], double acc) {
 __device__ __forceinline__ float rms_scale(double sum, int H, float eps) {
     const float ms = (float)(sum / (double)H);
     return 1.0f / sqrtf(ms + eps);
+}
+
+// The row's scale from this thread's chunks (zero past H). part: 4 doubles
+// of LDS; every thread of the workgroup calls this (it has a barrier), and
+// part may be written again only after a later barrier.
+__device__ __forceinline__ float renorm_row_scale(const uint4 (&v)[RENORM_CHUNKS], int H,
+                                                  float eps, double *part) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < RENORM_CHUNKS; ++i) {
+        const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                            bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        acc = sumsq8(f, acc);
+    }
+    acc = wave_allsum_d(acc);
+    if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = acc;
+    __syncthreads();
+    const double sum = ((part[0] + part[1]) + part[2]) + part[3];
+    return rms_scale(sum, H, eps);
+}
+
+// eight bf16 values times the row scale, rounded back to bf16
+__device__ __forceinline__ uint4 renorm_chunk(uint4 v, float r) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo(w[k]) * r, hi = bf16_hi(w[k]) * r;
+        o[k] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // 16-byte global load/store helpers.

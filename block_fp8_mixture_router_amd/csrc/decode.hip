@@ -1,83 +1,66 @@
-// Row-at-a-time path (decode): the whole layer in one persistent kernel.
+// Row-at-a-time path (decode): the whole layer for up to four rows in one
+// persistent kernel, computing every value with the arithmetic of the
+// expert-grouped kernels, so that a row's output bytes are the ones it gets
+// inside any chunk.
 //
-// The pages' one-row projection streams weight chunks through a ring, and
-// their frame step chains its kernels with programmatic dependent launch so
-// a kernel can stream immutable weights before waiting on its predecessor
-// (PR #925 "drama: load the checkpoint with direct I/O in file order and build
-// the codec on its own thread", commit summaries of the single-row
-// projection; PR #927, "What this changes"). On gfx950 the layer for one row
-// is purely HBM-bound (1.5 FLOP per weight byte) and latency-bound by its
-// three dependent steps, so it runs as ONE launch of one workgroup per
-// compute unit, with no grid-wide barrier at all:
+// The pages' one-row projection issues the same matrix instructions on the
+// same fragments in the same K order as the row tiling it replaces, so its
+// results are the same bits, and their backbone outputs are hash-identical
+// at every chunk size (PR #925 "drama: load the checkpoint with direct I/O in
+// file order and build the codec on its own thread", commit summaries of the
+// single-row projection; PR #920 "drama: Drama 3 (fishaudio/drama-3)
+// text-to-speech on CUDA", Receipt). Their frame step also lets a kernel
+// stream immutable weights before waiting on its predecessor (PR #927,
+// "What this changes"). On gfx950 the layer for one row is bound by HBM
+// (1.5 FLOP per weight byte) and by the latency of its three dependent
+// steps, so it runs as ONE launch of one workgroup per compute unit, with no
+// grid-wide barrier:
 //
-//  A. router logits (exact fp64 sums), shared-expert gate/up rows
-//     (hs = bf16(silu(gs) * us)) and the shared gate; every load that does not
-//     depend on the routing, the phase-C shared down rows included, is issued
-//     here; every workgroup also quantises x (1x128) into LDS;
+//  A. router logits (exact fp64 sums), one per workgroup at a time, and x
+//     into LDS (bf16 and its 1x128 e4m3 groups); on waves 1-3 the shared
+//     expert's gate/up columns and the shared gate, which need x alone;
 //  B. every workgroup waits for the logits of its rows, selects the top-K
-//     itself (wave argmax, DPP lane moves), streams its share of the routed
-//     gate/up rows, h = silu(g) * u, and then issues the loads of its
-//     phase-C routed down rows, which arrive during the h handoff;
+//     itself, streams its share of the routed gate/up rows, h = silu(g) * u,
+//     and issues the loads of its phase-C down rows, which arrive during the
+//     h handoff;
 //  C. every workgroup waits for h, hs and gamma, re-quantises h (1x128) into
-//     LDS and owns whole output rows m: all K down rows plus the shared down
-//     row, then writes y = bf16(sum_j w_j e_j + gamma s) in slot order.
+//     LDS and owns blocks of 8 output rows m: every slot's down rows, the
+//     shared down rows and the combine y = bf16(sum_j w_j e_j + gamma s).
 //
-// Work is spread over waves workgroup-major, so consecutive items land on
-// different compute units. Each lane streams 16 contiguous weight bytes per
-// load; a wave covers 1 KiB of a weight row per load.
+// The block products are the grouped kernels' MFMA instructions on the same
+// operand bytes: an MFMA output element depends only on its own row of A and
+// column of B, so a row alone can sit in any row of a tile and the tiles can
+// pair blocks along the diagonal (two K halves, four K steps, two slots) to
+// use the matrix cores' spare rows, with the same bits.
 //
 // Cross-workgroup values carry their call's epoch. Every value one workgroup
 // hands to others (a logit, an hs or h element, gamma) is one 64-bit word:
 // the value's 32 bits and the epoch of the call that wrote it, stored and
-// loaded with device-coherent (sc1) accesses that bypass the per-XCD L2 for
-// that access only. A consumer polls the words themselves until all carry
-// the current epoch, so there is no flag, no fence and no barrier: each
-// workgroup moves on as soon as its own inputs exist. (A device-scope fence
-// would write back or invalidate a whole L2, and a flag costs an extra round
-// trip to memory after the payload's stores drain.) Each word is stored in
-// DECODE_REPLICAS copies and workgroup b reads copy b % DECODE_REPLICAS, so no
-// cache line is polled by more than 1/8 of the workgroups.
+// loaded with device-coherent accesses. A consumer polls the words
+// themselves until all carry the current epoch, so there is no flag, no
+// fence and no barrier: each workgroup moves on as soon as its own inputs
+// exist. Each word is stored in DECODE_REPLICAS copies and workgroup b reads
+// copy b % DECODE_REPLICAS, so no line is polled by more than 1/8 of the
+// workgroups.
 //
 // Epochs: every workgroup keeps its own call counter in the workspace, reads
 // it at the start and writes the next value at the end; all counters advance
 // together, so all workgroups of a call agree on its epoch as long as the
 // workspace started out filled with one repeated byte. Epochs are odd, below
 // 2^30 and differ from the counter they come from, so neither such a fill nor
-// words left by an earlier call (or an earlier replay of a captured graph)
-// can satisfy a wait. Waits are bounded: a spin-out (workgroups not co-resident)
-// sets an error word and the kernel still finishes.
+// words left by an earlier call can satisfy a wait. Waits are bounded: after
+// SPIN_LIMIT unsuccessful poll rounds (workgroups not all resident) the
+// spin-out word is set and the kernel still finishes.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
 
 namespace moe {
 
-constexpr int GU_ROWS = 4;       // routed gate/up rows per wave item
-constexpr int REPL = DECODE_REPLICAS;  // copies of every cross-workgroup value
-constexpr uint32_t SPIN_LIMIT = 1u << 17;  // ~0.2 s of polling, then give up
-
-// Dot product of 16 decoded e4m3 activation values with 16 e4m3 weights.
-__device__ __forceinline__ float dot16_fp8(const float (&a)[16], uint4 w) {
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    float p = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float b0, b1, b2, b3;
-        e4m3x4_to_f32(wv[i], b0, b1, b2, b3);
-        p = fmaf(a[4 * i + 0], b0, p);
-        p = fmaf(a[4 * i + 1], b1, p);
-        p = fmaf(a[4 * i + 2], b2, p);
-        p = fmaf(a[4 * i + 3], b3, p);
-    }
-    return p;
-}
-
-__device__ __forceinline__ void decode16(uint4 q, float (&f)[16]) {
-    e4m3x4_to_f32(q.x, f[0], f[1], f[2], f[3]);
-    e4m3x4_to_f32(q.y, f[4], f[5], f[6], f[7]);
-    e4m3x4_to_f32(q.z, f[8], f[9], f[10], f[11]);
-    e4m3x4_to_f32(q.w, f[12], f[13], f[14], f[15]);
-}
+constexpr int REPL = DECODE_REPLICAS;   // copies of every cross-workgroup value
+constexpr uint32_t SPIN_LIMIT = 1u << 17;  // poll rounds before giving up (0.1-0.3 s)
+constexpr int ERR_WORD = SYNC_ERR_WORD;
+constexpr int MB = 8;  // output rows per phase-C unit
 
 // ------------------------------------------------------ tagged handoffs
 
@@ -106,15 +89,10 @@ __device__ __forceinline__ bool has_epoch(uint64_t w, uint32_t epoch) {
     return (uint32_t)(w >> 32) == epoch;
 }
 
-// this call's first epoch from a workgroup's call counter c: odd, below 2^30
-// and never equal to c itself, so a workspace filled with one repeated byte
-// (zeros included) holds no word tagged with it; layer l of a stack uses
-// epoch + 4l
+// this call's epoch from a workgroup's call counter c: odd, below 2^30 and
+// never equal to c itself, so a workspace filled with one repeated byte
+// (zeros included) holds no word tagged with it
 __device__ __forceinline__ uint32_t call_epoch(uint32_t c) { return (c & 0x3FFFFFFEu) + 3u; }
-
-// sync words: [ERR_WORD] spin-out flag; [SYNC_FLAGS + b] workgroup b's call
-// counter
-constexpr int ERR_WORD = 32;
 
 // First loads of the tagged words p[idx[i]], i < n (valid entries form a
 // prefix; the others read as already carrying `epoch`). Nothing waits for
@@ -130,9 +108,6 @@ __device__ __forceinline__ void poll_issue(const uint64_t *p, const int (&idx)[N
     }
 }
 
-// Polls the words of an earlier poll_issue that do not yet carry `epoch`
-// until all do (bounded: past SPIN_LIMIT rounds the error word is set and
-// the stale values are returned). The words' value halves go to v.
 template <int N>
 __device__ __forceinline__ bool all_have_epoch(const uint64_t (&w)[N], uint32_t epoch) {
     bool ok = true;
@@ -141,6 +116,9 @@ __device__ __forceinline__ bool all_have_epoch(const uint64_t (&w)[N], uint32_t 
     return ok;
 }
 
+// Polls the words of an earlier poll_issue that do not yet carry `epoch`
+// until all do (bounded: past SPIN_LIMIT rounds the error word is set and
+// the stale values are returned). The words' value halves go to v.
 template <int N>
 __device__ __forceinline__ void poll_finish(uint32_t *err, const uint64_t *p,
                                             const int (&idx)[N], int n, uint32_t epoch,
@@ -196,6 +174,92 @@ __device__ __forceinline__ void poll_words(uint32_t *err, const uint64_t *p,
     poll_finish<N>(err, p, idx, n, epoch, w, v);
 }
 
+// Pipelined re-polls. A handoff region as a raw buffer: a load at an offset
+// past its end returns zero and touches no memory, so a lane can take part
+// in a load instruction without requesting its word. Loads are
+// device-coherent (sc1), as the tagged stores are.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int POLL_OOB = 0x7FFFFFF0;  // past every handoff region
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t handoff_region(const uint64_t *base, int words) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(base), 0, words * 8,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint64_t region_word(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 16 /* sc1 */);
+    return ((uint64_t)v.y << 32) | v.x;
+}
+
+// Completes a first round w of loads of words idx[i] (i < n) of region r:
+// if any lane of the wave still has a stale word, DEPTH re-poll rounds go
+// out a short sleep apart, each asking only for the words still stale;
+// then each returning round (oldest first) is merged and sent again for
+// what is still missing. The wait after the last word lands is one memory
+// latency plus part of a round gap, not a full round trip per retry.
+// Bounded: past SPIN_LIMIT passes the error word is set and the stale
+// values are returned.
+constexpr int POLL_GAP = 6;  // s_sleep units (64 clocks) between re-poll rounds
+
+template <int N, int DEPTH>
+__device__ __forceinline__ void poll_complete(uint32_t *err, __amdgpu_buffer_rsrc_t r,
+                                              const int (&idx)[N], int n, uint32_t epoch,
+                                              uint64_t (&w)[N], uint32_t (&v)[N]) {
+    // valid entries form a prefix; the others count as done
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (i >= n) w[i] = tagged(0u, epoch);
+    if (__builtin_amdgcn_ballot_w64(!all_have_epoch<N>(w, epoch)) != 0) {
+        uint64_t q[DEPTH][N];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                q[d][i] = region_word(r, has_epoch(w[i], epoch) ? POLL_OOB : 8 * idx[i]);
+            if (d + 1 < DEPTH) __builtin_amdgcn_s_sleep(POLL_GAP);
+        }
+        for (uint32_t spin = 0;; ++spin) {
+            bool fin = false;  // wave-uniform
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                if (!fin) {
+#pragma unroll
+                    for (int i = 0; i < N; ++i)
+                        if (!has_epoch(w[i], epoch)) w[i] = q[d][i];
+                    fin = __builtin_amdgcn_ballot_w64(!all_have_epoch<N>(w, epoch)) == 0;
+                    if (!fin)
+#pragma unroll
+                        for (int i = 0; i < N; ++i)
+                            q[d][i] = region_word(r, has_epoch(w[i], epoch) ? POLL_OOB
+                                                                            : 8 * idx[i]);
+                }
+            }
+            if (fin) break;
+            if (spin >= SPIN_LIMIT) {
+                st_dev(err, 1u);
+                break;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (uint32_t)w[i];
+}
+
+// the wave's earlier LDS stores are seen by its later LDS loads in other
+// lanes: a wave's LDS operations execute in order, and this keeps the
+// compiler from moving memory operations across it (a memory fence here
+// would also wait for every global load the wave has in flight)
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_wave_barrier(); }
+
+__device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
+    const uint32_t as[4] = {a.x, a.y, a.z, a.w}, bs[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc = fmaf(bf16_lo(as[k]), bf16_lo(bs[k]), acc);
+        acc = fmaf(bf16_hi(as[k]), bf16_hi(bs[k]), acc);
+    }
+    return acc;
+}
+
 // ------------------------------------------------------------- phase A
 
 // Router logits come first and alone: each workgroup's four waves share one
@@ -210,18 +274,35 @@ struct RouterRegs {
 };
 
 // chunk c = lane + 64 (wave + 4 i) of row e of the router and of row t of x
+// (x from global memory, or from the renormalised rows in LDS when RN)
 template <int NQ>
-__device__ __forceinline__ void router_load(const FusedArgs &a, int r, RouterRegs<NQ> &rr) {
-    const int t = r / a.E, e = r % a.E, nc8 = a.H / 8;
+__device__ __forceinline__ void router_load_w(const FusedArgs &a, int r, RouterRegs<NQ> &rr) {
+    const int e = r % a.E, nc8 = a.H / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint16_t *wr = a.router_w + (int64_t)e * a.H, *xr = a.x + (int64_t)t * a.H;
+    const uint16_t *wr = a.router_w + (int64_t)e * a.H;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int c = lane + WAVE * (wave + 4 * i);
-        const bool ok = c < nc8;
-        rr.w[i] = ok ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
-        rr.x[i] = ok ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        rr.w[i] = c < nc8 ? ld16(wr + c * 8) : make_uint4(0, 0, 0, 0);
     }
+}
+template <int NQ, bool RN>
+__device__ __forceinline__ void router_load_x(const FusedArgs &a, int r, const uint16_t *xs,
+                                              RouterRegs<NQ> &rr) {
+    const int t = r / a.E, nc8 = a.H / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t *xr = (RN ? xs : a.x) + (int64_t)t * a.H;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int c = lane + WAVE * (wave + 4 * i);
+        rr.x[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+template <int NQ, bool RN>
+__device__ __forceinline__ void router_load(const FusedArgs &a, int r, const uint16_t *xs,
+                                            RouterRegs<NQ> &rr) {
+    router_load_w<NQ>(a, r, rr);
+    router_load_x<NQ, RN>(a, r, xs, rr);
 }
 
 // Logit r = (t, e): exact fp64 sum of bf16 products (each wave's partial in
@@ -254,97 +335,139 @@ __device__ __forceinline__ void router_logit(const FusedArgs &a, int r, const Ro
         const int t = r / a.E, e = r % a.E;
         const double acc = ((red[0] + red[1]) + red[2]) + red[3];
         float l = (float)acc;
-        if (!(a.flags & K_LOGITS_FP32)) l = __uint_as_float(f32_to_bf16(l) << 16);
+        if (!(a.flags & K_LOGITS_FP32)) l = bf16_round(l);
         if (a.bias) l = l + a.bias[e];
         st_dev(a.logits + (int64_t)(lane * a.T + t) * a.E + e, tagged(__float_as_uint(l), epoch));
     }
 }
 
-// NB = 16-byte chunks of a bf16 H-row per lane (H / 512, rounded up). An
-// item is one shared-expert row or the shared gate of one row of x; all of
-// an item's loads are issued before any of its arithmetic, and the kernel
-// can do other work between the two.
-template <int NB>
-struct ItemARegs {
-    uint4 x[NB], w0[NB], w1[NB];
-};
-
-__device__ __forceinline__ float dot8_bf16_regs(uint4 a, uint4 b, float acc) {
-    const uint32_t as[4] = {a.x, a.y, a.z, a.w}, bs[4] = {b.x, b.y, b.z, b.w};
+// x (bf16) and its 1x128 e4m3 groups into LDS, with the arithmetic of the
+// quantiser: chunk c of 8 values, 16 lanes per 128-column group
+__device__ __forceinline__ void quant_chunk_to_lds(uint4 v, int c, uint8_t *q, float *s) {
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        acc = fmaf(bf16_lo(as[k]), bf16_lo(bs[k]), acc);
-        acc = fmaf(bf16_hi(as[k]), bf16_hi(bs[k]), acc);
-    }
-    return acc;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = group16_max(amax);
+    const float sc = group_scale(amax);
+    uint2 out;
+    out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+    out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+    *reinterpret_cast<uint2 *>(q + c * 8) = out;
+    if ((c & 15) == 0) s[c >> 4] = sc;
 }
 
-// item `it`: [0, T*Is) shared rows (t, n); then T shared gates
-// the item's weight rows (they do not depend on x)
-template <int NB>
-__device__ __forceinline__ void itemA_load_w(const FusedArgs &a, int it, int lane,
-                                             ItemARegs<NB> &r) {
-    const int n_sh = a.T * a.Is, nc8 = a.H / 8;
-    const uint16_t *w0, *w1 = nullptr;
-    if (it < n_sh) {
-        const int n = it % a.Is;
-        w0 = a.sh_gate + (int64_t)n * a.H;
-        w1 = a.sh_up + (int64_t)n * a.H;
-    } else {
-        w0 = a.sh_gate_w;
-    }
+// one row: the workgroup's router loads hold all of x (lane chunk
+// c = lane + 64 (wave + 4 i), whole 16-lane groups)
+template <int NQ>
+__device__ __forceinline__ void x_stage_router(const RouterRegs<NQ> &rr, int H, uint16_t *xs,
+                                               uint8_t *q, float *s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = lane + WAVE * i;
-        const bool ok = c < nc8;
-        r.w0[i] = ok ? ld16(w0 + c * 8) : make_uint4(0, 0, 0, 0);
-        r.w1[i] = ok && w1 ? ld16(w1 + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-}
-
-// the item's row of x (global memory, or LDS in a layer stack)
-template <int NB>
-__device__ __forceinline__ void itemA_load_x(const FusedArgs &a, int it, int lane,
-                                             ItemARegs<NB> &r) {
-    const int n_sh = a.T * a.Is, nc8 = a.H / 8;
-    const int t = it < n_sh ? it / a.Is : it - n_sh;
-    const uint16_t *xr = a.x + (int64_t)t * a.H;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = lane + WAVE * i;
-        r.x[i] = c < nc8 ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-}
-
-template <int NB>
-__device__ __forceinline__ void itemA_compute(const FusedArgs &a, int it, int lane,
-                                              const ItemARegs<NB> &r, uint32_t epoch) {
-    const int n_sh = a.T * a.Is;
-    if (it < n_sh) {
-        // shared-expert row n of row t: hs = bf16(silu(g) * u)
-        const int t = it / a.Is, n = it % a.Is;
-        float g = 0.0f, u = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            g = dot8_bf16_regs(r.x[i], r.w0[i], g);
-            u = dot8_bf16_regs(r.x[i], r.w1[i], u);
+    for (int i = 0; i < NQ; ++i) {
+        const int c = lane + WAVE * (wave + 4 * i);
+        if (c < H / 8) {
+            st16(xs + c * 8, rr.x[i]);
+            quant_chunk_to_lds(rr.x[i], c, q, s);
         }
-        g = wave_allsum(g);
-        u = wave_allsum(u);
-        if (lane < REPL)
-            st_dev(a.hs + (int64_t)(lane * a.T + t) * a.Is + n,
-                   tagged(f32_to_bf16(silu(g) * u), epoch));
-    } else {
-        // shared gate of row t
-        const int t = it - n_sh;
-        float z = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) z = dot8_bf16_regs(r.x[i], r.w0[i], z);
-        z = wave_allsum(z);
-        if (lane < REPL)
-            st_dev(a.gamma + lane * a.T + t,
-                   tagged(__float_as_uint(1.0f / (1.0f + expf(-z))), epoch));
     }
+}
+
+// every row, thread tid owning chunks tid + 256 k (x from global memory, or
+// already in LDS when RN)
+template <bool RN>
+__device__ __forceinline__ void x_stage_rows(const uint16_t *x, int T, int H, uint16_t *xs,
+                                             uint8_t *q, float *s) {
+    const int n = T * H / 8;
+    for (int c = threadIdx.x; c < n; c += blockDim.x) {
+        const uint4 v = RN ? ld16(xs + c * 8) : ld16(x + (int64_t)c * 8);
+        if (!RN) st16(xs + c * 8, v);
+        quant_chunk_to_lds(v, c, q, s);
+    }
+}
+
+// Shared expert gate/up. One item: columns n0 = 2s and n0 + 1 of the gate
+// and up matrices for every row (T <= 4), all of H, by one wave, with the
+// grouped kernel's arithmetic: per 128-column K step, four chained bf16
+// MFMAs from zero (MFMA i takes elements [32 kq + 8 i, +8) of lane
+// (l16, kq)); the steps' partials added in fp64 in ascending order;
+// hs = bf16(silu(gs) * us). One chain covers four K steps: B column l16 is
+// weight row (l16 & 3) = gate n0, gate n0 + 1, up n0, up n0 + 1 at step
+// 4g + (l16 >> 2); A row l16 is x row (l16 & 3) at the same step; the
+// diagonal 4x4 blocks (row block = column block) are kept.
+constexpr int SH_GROUPS = 4;  // chains (four K steps each) per batch of loads
+
+__device__ __forceinline__ void s_item(const FusedArgs &a, int s, const uint16_t *xs, float *q,
+                                       uint32_t epoch) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const int H = a.H, KB = H / GROUP, T = a.T, Is = a.Is;
+    const int n0 = 2 * s, cid = l16 & 3, qb = l16 >> 2;
+    const uint16_t *wrow =
+        (cid < 2 ? a.sh_gate : a.sh_up) + (int64_t)(n0 + (cid & 1)) * H + 32 * kq;
+    const uint16_t *xrow = xs + min(cid, T - 1) * H + 32 * kq;
+    const int NG = (KB + 3) / 4;
+    for (int g0 = 0; g0 < NG; g0 += SH_GROUPS) {
+        uint4 w[SH_GROUPS][4];
+#pragma unroll
+        for (int gg = 0; gg < SH_GROUPS; ++gg) {
+            const int kb = min(4 * (g0 + gg) + qb, KB - 1);  // steps past H reload the last
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[gg][i] = ld16(wrow + kb * GROUP + 8 * i);
+        }
+#pragma unroll
+        for (int gg = 0; gg < SH_GROUPS; ++gg) {
+            const int g = g0 + gg;
+            if (g < NG) {  // wave-uniform
+                const int kb = min(4 * g + qb, KB - 1);
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc = mfma_bf16_k32(as_v8bf(ld16(xrow + kb * GROUP + 8 * i)),
+                                        as_v8bf(w[gg][i]), acc);
+                // element r of lane (l16, kq): row 4 kq + r = x row r at step
+                // 4g + kq; column l16 = weight row cid at step 4g + qb
+                const int kbv = 4 * g + kq;
+                if (kq == qb && kbv < KB)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (r < T) q[kbv * 16 + r * 4 + cid] = acc[r];
+            }
+        }
+    }
+    wave_lds_sync();
+    uint32_t hv = 0;
+    if (lane < 2 * T) {
+        const int t = lane >> 1, nl = lane & 1;
+        double dg = 0.0, du = 0.0;
+        for (int kb = 0; kb < KB; ++kb) {
+            dg += (double)q[kb * 16 + t * 4 + nl];
+            du += (double)q[kb * 16 + t * 4 + 2 + nl];
+        }
+        hv = f32_to_bf16(silu((float)dg) * (float)du);
+    }
+    // copy lane / (2T) of value (t, nl) = lane % (2T)
+    const int nv = 2 * T;
+    const uint32_t v = (uint32_t)__shfl((int)hv, lane % nv);
+    if (lane < REPL * nv) {
+        const int r = lane / nv, vi = lane % nv, t = vi >> 1, nl = vi & 1;
+        st_dev(a.hs + ((int64_t)r * T + t) * Is + n0 + nl, tagged(v, epoch));
+    }
+    wave_lds_sync();  // q is rewritten by the wave's next item
+}
+
+// shared gate of row t: gamma = 1 / (1 + exp(-(x . wg))), the dot product in
+// the top-K kernels' order (lane chunks c = lane + 64 i, fp32 fma chains,
+// then the wave sum)
+__device__ __forceinline__ void g_item(const FusedArgs &a, int t, const uint16_t *xs,
+                                       uint32_t epoch) {
+    const int lane = threadIdx.x & 63, nc8 = a.H / 8;
+    float z = 0.0f;
+    for (int c = lane; c < nc8; c += WAVE)
+        z = dot8_bf16_regs(ld16(xs + t * a.H + c * 8), ld16(a.sh_gate_w + c * 8), z);
+    z = wave_allsum(z);
+    if (lane < REPL)
+        st_dev(a.gamma + lane * a.T + t, tagged(__float_as_uint(1.0f / (1.0f + expf(-z))), epoch));
 }
 
 // ------------------------------------------------------------- phase B
@@ -358,7 +481,9 @@ __device__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, 
     for (int i = 0; i < NL; ++i) idx[i] = lane + WAVE * i;
     const int n = min(NL, max(0, (E - lane + WAVE - 1) / WAVE));
     uint32_t bits[NL];
-    poll_words_staggered<NL>(err, lr, idx, n, epoch, bits);
+    uint64_t w[NL];
+    poll_issue<NL>(lr, idx, n, epoch, w);
+    poll_complete<NL, (NL <= 4 ? 3 : 1)>(err, handoff_region(lr, E), idx, n, epoch, w, bits);
     if (packed) {
         uint32_t k[NL];
 #pragma unroll
@@ -385,66 +510,121 @@ __device__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch, ui
     else topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed);
 }
 
-// routed rows n0..n0+GU_ROWS-1 of pair p: h = silu(g) * u (fp32); loads first
-template <int NC>
+// Routed gate/up. One item: columns n0..n0+3 of the gate and up matrices of
+// pair p's expert, all of H, by one wave, with the grouped kernel's
+// arithmetic: per 128x128 weight block one FP8 MFMA from zero, folded in
+// ascending K order as acc = fmaf(sx * s_w, P, acc), then h = silu(g) * u.
+// One MFMA covers two K blocks: B column l16 is weight row (l16 & 7) (gate
+// n0..n0+3, then up n0..n0+3) at block j (l16 < 8) or KH + j (l16 >= 8), A
+// row l16 is the pair's row of qx at the same block, and the two diagonal
+// 8x8 blocks are kept. Lanes 0-7 (D row 0) fold the first KH blocks and hand
+// their sums to lanes 40-47 (D row 8, columns 8-15), which fold the rest.
+constexpr int GU_STEP = 8;  // MFMAs (block pairs) per batch of loads
+
 struct GateUpRegs {
-    uint4 g[NC][GU_ROWS], u[NC][GU_ROWS];
-    float sg[NC], su[NC];  // block scales of each chunk's 128-column block
+    uint4 w[GU_STEP][2];
+    float sw[GU_STEP];  // weight block scale of each lane's column and block
 };
 
-template <int NC>
-__device__ __forceinline__ void gateup_load(const FusedArgs &a, int n0, int e, int lane,
-                                            GateUpRegs<NC> &r) {
-    const int H = a.H, I = a.I, nchunk = H / 16;
-    const uint8_t *wg = a.w_gate + ((int64_t)e * I + n0) * H;
-    const uint8_t *wu = a.w_up + ((int64_t)e * I + n0) * H;
-    const int KB = H / GROUP;
-    const float *sg = a.s_gate + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
-    const float *su = a.s_up + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
-    // branch-free: chunks past the row reload its last chunk (the compute
-    // skips them), so the loads form one straight run
+__device__ __forceinline__ void gateup_load(const FusedArgs &a, int e, int n0, int j0,
+                                            GateUpRegs &r) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const int H = a.H, I = a.I, KB = H / GROUP, KH = (KB + 1) / 2;
+    const int r8 = l16 & 7, hb = l16 >> 3;
+    const bool up = r8 >= 4;
+    const uint8_t *row = (up ? a.w_up : a.w_gate) + ((int64_t)e * I + n0 + (r8 & 3)) * H + 32 * kq;
+    const float *srow = (up ? a.s_up : a.s_gate) + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+    // branch-free: blocks past the end reload the last one (dropped later)
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int c = min(lane + WAVE * i, nchunk - 1);
-        r.sg[i] = sg[c / 8];
-        r.su[i] = su[c / 8];
+    for (int u = 0; u < GU_STEP; ++u) {
+        const int kb = min(hb * KH + j0 + u, KB - 1);
+        r.w[u][0] = ld16(row + kb * GROUP);
+        r.w[u][1] = ld16(row + kb * GROUP + 16);
+        r.sw[u] = srow[kb];
+    }
+}
+
+// the MFMAs of one batch: lanes 0-7 fold their first-half blocks into acc,
+// lanes 40-47 keep (scale, product) of the second-half blocks in sp[j][c]
+__device__ __forceinline__ void gateup_mfma(const FusedArgs &a, int t, int j0,
+                                            const GateUpRegs &r, const uint8_t *qx,
+                                            const float *sx, float2 *sp, float &acc) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2, hb = l16 >> 3;
+    const uint8_t *qa = qx + t * H + 32 * kq;
 #pragma unroll
-        for (int q = 0; q < GU_ROWS; ++q) {
-            r.g[i][q] = ld16(wg + (int64_t)q * H + c * 16);
-            r.u[i][q] = ld16(wu + (int64_t)q * H + c * 16);
+    for (int u = 0; u < GU_STEP; ++u) {
+        const int j = j0 + u;
+        if (j < KH) {  // wave-uniform
+            const int kb = min(hb * KH + j, KB - 1);  // A row l16 and B column l16 share it
+            const v8i av = as_v8i(ld16(qa + kb * GROUP), ld16(qa + kb * GROUP + 16));
+            const v4f d = mfma_fp8_k128(av, as_v8i(r.w[u][0], r.w[u][1]));
+            const float sc = sx[t * KB + kb] * r.sw[u];
+            if (lane < 8) acc = fmaf(sc, d[0], acc);
+            else if (lane >= 40 && lane < 48 && KH + j < KB) sp[j * 8 + lane - 40] = make_float2(sc, d[0]);
         }
     }
 }
 
-template <int NC>
-__device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0, int e,
-                                               const uint8_t *qx, const float *sx, int lane,
-                                               const GateUpRegs<NC> &r, uint32_t epoch) {
-    const int I = a.I, nchunk = a.H / 16;
-    float accg[GU_ROWS] = {}, accu[GU_ROWS] = {};
+// The rest of the item once its first batch is in. With one batch
+// (H <= 2048) every block's (scale, product) stays in registers: lanes 0-7
+// fold the first half, lanes 40-47 take over their sums and fold the second
+// half, with no LDS and no wait beyond the item's own loads. Larger H takes
+// further batches and keeps the second half's pairs in LDS (sp).
+__device__ __forceinline__ void gateup_finish(const FusedArgs &a, int p, int n0, int e,
+                                              const GateUpRegs &r0, const uint8_t *qx,
+                                              const float *sx, float2 *sp, uint32_t epoch) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2, t = p / a.K, hb = l16 >> 3;
+    const int src = (lane >= 40 && lane < 48) ? lane - 40 : lane;
+    float g;
+    if (KH <= GU_STEP) {
+        const uint8_t *qa = qx + t * H + 32 * kq;
+        float sc[GU_STEP], pv[GU_STEP];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int c = lane + WAVE * i;
-        if (c < nchunk) {
-            float xq[16];
-            decode16(*reinterpret_cast<const uint4 *>(qx + c * 16), xq);
-            const float s = sx[c / 8];
-#pragma unroll
-            for (int q = 0; q < GU_ROWS; ++q) {
-                accg[q] = fmaf(s * r.sg[i], dot16_fp8(xq, r.g[i][q]), accg[q]);
-                accu[q] = fmaf(s * r.su[i], dot16_fp8(xq, r.u[i][q]), accu[q]);
+        for (int u = 0; u < GU_STEP; ++u) {
+            sc[u] = 0.0f;
+            pv[u] = 0.0f;
+            if (u < KH) {  // wave-uniform
+                const int kb = min(hb * KH + u, KB - 1);  // A row l16 and B column l16 share it
+                const v8i av = as_v8i(ld16(qa + kb * GROUP), ld16(qa + kb * GROUP + 16));
+                const v4f d = mfma_fp8_k128(av, as_v8i(r0.w[u][0], r0.w[u][1]));
+                sc[u] = sx[t * KB + kb] * r0.sw[u];
+                pv[u] = d[0];
             }
         }
-    }
-    float hv = 0.0f;
+        float acc = 0.0f;  // lanes 0-7: blocks 0..KH-1
 #pragma unroll
-    for (int q = 0; q < GU_ROWS; ++q) {
-        const float g = wave_allsum(accg[q]), u = wave_allsum(accu[q]);
-        if (lane % GU_ROWS == q) hv = silu(g) * u;
+        for (int u = 0; u < GU_STEP; ++u)
+            if (u < KH) acc = fmaf(sc[u], pv[u], acc);
+        g = __shfl(acc, src);  // lanes 40-47: blocks KH..KB-1
+#pragma unroll
+        for (int u = 0; u < GU_STEP; ++u)
+            if (KH + u < KB) g = fmaf(sc[u], pv[u], g);
+    } else {
+        float acc = 0.0f;
+        gateup_mfma(a, t, 0, r0, qx, sx, sp, acc);
+        for (int j0 = GU_STEP; j0 < KH; j0 += GU_STEP) {
+            GateUpRegs r;
+            gateup_load(a, e, n0, j0, r);
+            gateup_mfma(a, t, j0, r, qx, sx, sp, acc);
+        }
+        g = __shfl(acc, src);
+        wave_lds_sync();
+        if (lane >= 40 && lane < 48)
+            for (int j = 0; j < KB - KH; ++j) {
+                const float2 v = sp[j * 8 + lane - 40];
+                g = fmaf(v.x, v.y, g);
+            }
+        wave_lds_sync();  // sp is rewritten by the wave's next item
     }
-    if (lane < GU_ROWS * REPL)
-        st_dev(a.h + ((int64_t)(lane / GU_ROWS) * a.T * a.K + p) * I + n0 + lane % GU_ROWS,
-               tagged(__float_as_uint(hv), epoch));
+    const int F = KB > KH ? 40 : 0;  // lanes F..F+3: gate sums, F+4..F+7: up sums
+    const float u = __shfl(g, min(lane + 4, 63));
+    const float hv = silu(g) * u;
+    const float hl = __shfl(hv, F + (lane & 3));
+    if (lane < 4 * REPL)
+        st_dev(a.h + ((int64_t)(lane >> 2) * a.T * a.K + p) * a.I + n0 + (lane & 3),
+               tagged(__float_as_uint(hl), epoch));
 }
 
 // ------------------------------------------------------------- phase C
@@ -452,52 +632,49 @@ __device__ __forceinline__ void gateup_compute(const FusedArgs &a, int p, int n0
 // A phase-C unit is a block of MB output rows m0..m0+MB-1 of one row t of x:
 // the routed down rows of all K slots, the shared down rows and the combine.
 //
-// The routed part runs on the FP8 matrix cores. A 16x16x128 MFMA takes as A
-// the rows (slot j, row m) of two slots, 2 x MB = 16 rows of 128 codes of
-// one K block, and as B the same K block of h for all 16 slot columns (the
-// same B for every tile); only the products of slot j's rows with slot j's
-// column are kept. That is 8x the matrix work needed, on matrix cores that
-// are idle here, instead of several hundred dependent vector instructions
-// per wave with no other wave on the SIMD to hide their latency. Every MFMA
-// starts from zero and covers exactly one 128x128 weight block, so the lane
-// folds (h scale x weight block scale) into its fp32 sum per K block.
+// Routed: a 16x16x128 MFMA takes as A the rows (slot j, row m) of two slots,
+// 2 x MB = 16 rows of 128 codes of one K block, and as B the same K block of
+// h for all 16 slot columns; only the products of slot j's rows with slot
+// j's column are kept (an output element depends only on its own A row and B
+// column). The lane folds (h scale x weight block scale) into its fp32 sum
+// per K block, in ascending order, as the grouped down kernel does; e_j is
+// then rounded to bf16, the grouped path's staging precision.
 //
-// Operand layouts of v_mfma_scale_f32_16x16x128_f8f6f4, lane = 16 kq + l16:
-// A row l16 and B column l16 hold bytes [32 kq, 32 kq + 32) of the K block;
-// D element i of a lane is row 4 kq + i, column l16.
-constexpr int MB = 8;      // output rows per phase-C unit
-constexpr int SD_CH = 2;   // shared down-row chunks (8 bf16) per thread held in registers
+// Shared: the grouped combine kernel's chain of bf16 MFMAs over Is (per
+// 128-column block, MFMA i takes elements [32 kq + 8 i, +8)), accumulated in
+// the MFMA from zero in ascending order; B column l16 is shared down row
+// m0 + (l16 & 7), every A row is hs of row t.
+constexpr int SDB = 4;  // 128-column blocks of a shared down row loaded ahead (one per wave)
 
 template <int KBR, int TPW>
 struct DownRegs {
     uint4 w[TPW][KBR][2];  // A operands: tile, K block, two 16-byte halves
     float sd[TPW][KBR];    // weight block scale of this lane's D rows
-    uint4 s[SD_CH];        // shared down row chunks
+    uint4 s[4];            // shared down operands of block `wave`
 };
 
-__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
+constexpr int CHAIN_WAVE = 3;  // the wave that runs the shared down chain
 
-// 16x16 output, K = 128 e4m3 per operand; E8M0 scales 127 = x1.
-__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
-}
-
-// shared down rows of unit (t, m0): thread -> row m0 + tid / 32, 8-value
-// chunks tid % 32 + 32 i
+// Shared down operands of rows m0..m0+MB-1: wave w loads block w (every
+// wave the same loads, so no wave's wait counts depend on a branch; blocks
+// past Is reload the last one), staged in LDS for the chain wave.
 template <int KBR, int TPW>
 __device__ __forceinline__ void down_load_shared(const FusedArgs &a, int m0,
                                                  DownRegs<KBR, TPW> &r) {
-    const int l32 = threadIdx.x & 31, nch = a.Is / 8;
-    const uint16_t *srow = a.sh_down + (int64_t)(m0 + (threadIdx.x >> 5)) * a.Is;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, kq = lane >> 4;
+    const int Is = a.Is, SB = Is / GROUP;
+    const uint16_t *row = a.sh_down + (int64_t)(m0 + (l16 & 7)) * Is + 32 * kq;
+    const int bc = min(wave, SB - 1);
 #pragma unroll
-    for (int i = 0; i < SD_CH; ++i)  // branch-free (chunks past the row are skipped later)
-        r.s[i] = ld16(srow + min(l32 + 32 * i, nch - 1) * 8);
+    for (int i = 0; i < 4; ++i) r.s[i] = ld16(row + bc * GROUP + 8 * i);
+}
+
+// sdo: LDS [SDB][4][64] uint4
+template <int KBR, int TPW>
+__device__ __forceinline__ void down_stage_shared(const DownRegs<KBR, TPW> &r, uint4 *sdo) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdo[(wave * 4 + i) * 64 + lane] = r.s[i];
 }
 
 // Routed A operands and block scales of unit (t, m0) for this wave's tiles,
@@ -527,36 +704,44 @@ __device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int 
     }
 }
 
+// shared down of rows m0 + c, c < 8, in lanes c (D row 0, element 0); the
+// first SDB blocks' operands from LDS (sdo), later ones from memory
+__device__ __forceinline__ float shared_down_chain(const FusedArgs &a, int t, int m0,
+                                                   const uint4 *sdo, const uint16_t *hs_l) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const int Is = a.Is, SB = Is / GROUP;
+    const uint16_t *ha = hs_l + t * Is + 32 * kq;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < SDB; ++b)
+        if (b < SB)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc = mfma_bf16_k32(as_v8bf(ld16(ha + b * GROUP + 8 * i)),
+                                    as_v8bf(sdo[(b * 4 + i) * 64 + lane]), acc);
+    const uint16_t *row = a.sh_down + (int64_t)(m0 + (l16 & 7)) * Is + 32 * kq;
+    for (int b = SDB; b < SB; ++b)  // blocks past the ones loaded ahead
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = mfma_bf16_k32(as_v8bf(ld16(ha + b * GROUP + 8 * i)),
+                                as_v8bf(ld16(row + b * GROUP + 8 * i)), acc);
+    return acc[0];
+}
+
 // The unit's output: every routed slot's e_j (MFMA), the gated shared row
 // and the combine y = bf16(sum_j w_j e_j + gamma s), slots in order. ej and
-// gsl are LDS scratch ([K][MB] and [MB] fp32); hs and gamma were staged in
-// LDS. Every thread of the workgroup calls this (it has barriers).
+// ss are LDS scratch ([K][MB] and [MB] fp32); hs and gamma were staged in
+// LDS; with chain false the shared rows' s is already in ss. Every thread of
+// the workgroup calls this (it has barriers).
 template <int KBR, int TPW>
 __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
                                           const DownRegs<KBR, TPW> &r, const uint8_t *qh,
                                           const float *shs, const int32_t *ids,
                                           const float *wts, const uint16_t *hs_l,
-                                          const float *gam_l, float *ej, float *gsl,
-                                          uint32_t epoch) {
+                                          const float *gam_l, float *ej, float *ss,
+                                          uint4 *sdo, bool chain) {
     const int H = a.H, I = a.I, K = a.K, IB = I / GROUP, Is = a.Is;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kq = lane >> 4;
-
-    // gamma * (shared down row . hs[t]): 32 lanes per row
-    if (Is > 0) {
-        const uint16_t *hr = hs_l + t * Is;
-        const uint16_t *srow = a.sh_down + (int64_t)(m0 + (tid >> 5)) * Is;
-        const int l32 = tid & 31, nch = Is / 8;
-        float sacc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < SD_CH; ++i) {
-            const int c = l32 + 32 * i;
-            if (c < nch) sacc += dot8_bf16_regs(ld16(hr + c * 8), r.s[i], 0.0f);
-        }
-        for (int c = l32 + 32 * SD_CH; c < nch; c += 32)  // rows past the register copy
-            sacc += dot8_bf16_regs(ld16(hr + c * 8), ld16(srow + c * 8), 0.0f);
-        sacc = group32_sum(sacc);
-        if (l32 == 0) gsl[tid >> 5] = gam_l[t] * sacc;
-    }
 
     // routed slots: tile tau = wave + 4u holds slots 2 tau, 2 tau + 1
     const int ntiles = (K + 1) / 2;
@@ -601,116 +786,62 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
         // the lane whose column is that slot holds the product wanted
         if (js < K && l16 == js)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ej[js * MB + 4 * (kq & 1) + i] = acc[u][i];
+            for (int i = 0; i < 4; ++i) ej[js * MB + 4 * (kq & 1) + i] = bf16_round(acc[u][i]);
+    }
+    if (Is > 0 && chain) {  // else computed before the h handoff
+        down_stage_shared<KBR, TPW>(r, sdo);
+        __syncthreads();
+        if (wave == CHAIN_WAVE) {
+            const float s = shared_down_chain(a, t, m0, sdo, hs_l);
+            if (lane < MB) ss[lane] = s;
+        }
     }
     __syncthreads();
 
-    // combine: slots in order, then the shared term; 8 copies for a stack
-    if (tid < MB * REPL) {
-        const int mm = tid & (MB - 1);
+    // combine: slots in order, then the shared term
+    if (tid < MB) {
         float yacc = 0.0f;
-        for (int j = 0; j < K; ++j) yacc = fmaf(wts[t * K + j], ej[j * MB + mm], yacc);
-        if (Is > 0) yacc += gsl[mm];
-        const uint32_t yb = f32_to_bf16(yacc);
-        if (tid < MB && a.y) a.y[(int64_t)t * H + m0 + mm] = (uint16_t)yb;
-        if (a.ytag) st_dev(a.ytag + ((int64_t)(tid / MB) * a.T + t) * H + m0 + mm, tagged(yb, epoch));
+        for (int j = 0; j < K; ++j) yacc = fmaf(wts[t * K + j], ej[j * MB + tid], yacc);
+        if (Is > 0) yacc = fmaf(gam_l[t], ss[tid], yacc);
+        const uint16_t yb = (uint16_t)f32_to_bf16(yacc);
+        a.y[(int64_t)t * H + m0 + tid] = yb;
+        if (a.y2) a.y2[(int64_t)t * H + m0 + tid] = yb;
     }
-    __syncthreads();  // ej and gsl are reused by the next unit
+    __syncthreads();  // ej and ss are reused by the next unit
 }
 
 // ---------------------------------------------------------------- kernel
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, hs, gam, ej, gsl, rl, xs, red, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
-__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is,
-                                            bool stack = false) {
+__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is) {
     LdsPlan L;
-    const int P = T * K;
+    const int P = T * K, KB = H / GROUP, KH = (KB + 1) / 2;
     L.qx = 0;
     L.sx = L.qx + al16i(T * H);
-    L.qh = L.sx + al16i(T * (H / GROUP) * 4);
+    L.qh = L.sx + al16i(T * KB * 4);
     L.shs = L.qh + al16i(P * I);
     L.ids = L.shs + al16i(P * (I / GROUP) * 4);
     L.wts = L.ids + al16i(P * 4);
     L.hs = L.wts + al16i(P * 4);
     L.gam = L.hs + al16i(T * Is * 2);
-    L.ej = L.gam + al16i(T * 4);                     // phase-C unit: e_j of its rows
-    L.gsl = L.ej + al16i(K * MB * 4);                // phase-C unit: gated shared rows
-    L.rl = L.gsl + al16i(MB * 4);                    // router: 2 x 4 fp64 wave partials
-    L.xs = L.rl + 64;                                // stacks: the renormalised rows
-    L.red = L.xs + (stack ? al16i(T * H * 2) : 0);   // stacks: 4 fp64 partial sums
-    L.total = L.red + (stack ? 32 : 0);
+    L.ej = L.gam + al16i(T * 4);          // phase-C unit: e_j of its rows
+    L.ss = L.ej + al16i(K * MB * 4);      // phase-C unit: shared down of its rows
+    L.rl = L.ss + al16i(MB * 4);          // router: 2 x 4 fp64 wave partials
+    L.xs = L.rl + 64;                     // x rows, bf16
+    L.red = L.xs + al16i(T * H * 2);      // renormalisation: 4 fp64 partial sums
+    L.sq = L.red + 32;                    // shared gate/up partials, per wave [KB][16]
+    L.sp = L.sq + 4 * al16i(KB * 16 * 4); // routed gate/up second halves, per wave [KH][8]
+    L.sdo = L.sp + 4 * al16i(KH * 8 * 8); // shared down operands [SDB][4][64] uint4
+    L.total = L.sdo + (Is > 0 ? SDB * 4 * 64 * 16 : 0);
     return L;
 }
 
-bool decode_fits(int T, int H, int K, int I, int Is, bool stack) {
-    return T >= 1 && T <= DECODE_MAX_ROWS && lds_plan(T, H, K, I, Is, stack).total <= 150 * 1024;
-}
-
-// 1x128 quantisation of 8 values per lane (16 lanes per group) into LDS
-__device__ __forceinline__ void quant8_to_lds(const float (&f)[8], int g, int sub, uint8_t *q,
-                                              float *s) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = group16_max(amax);
-    const float sc = group_scale(amax);
-    uint2 out;
-    out.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
-    out.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
-    *reinterpret_cast<uint2 *>(q + g * GROUP + sub * 8) = out;
-    if (sub == 0) s[g] = sc;
-}
-
-// x (bf16, [T][H]) -> LDS codes and scales. Thread tid owns the 8-value
-// chunks tid + 256 k (16 lanes per 128-group); the first XQ of them are
-// loaded into registers at kernel start (x_load) and quantised later
-// (x_quant), so the quantisation waits on no memory.
-constexpr int XQ = 4;
-struct XRegs {
-    uint4 v[XQ];
-};
-
-__device__ __forceinline__ void x_load(const uint16_t *x, int n_chunks, XRegs &r) {
-#pragma unroll
-    for (int k = 0; k < XQ; ++k) {
-        const int c = threadIdx.x + blockDim.x * k;
-        r.v[k] = c < n_chunks ? ld16(x + (int64_t)c * 8) : make_uint4(0, 0, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void quant_chunk_to_lds(uint4 v, int c, uint8_t *q, float *s) {
-    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    quant8_to_lds(f, c >> 4, c & 15, q, s);
-}
-
-// x from a workgroup's router loads (one row): lane chunk c = lane + 64
-// (wave + 4 i), 16 lanes per 128-group
-template <int NQ>
-__device__ __forceinline__ void x_quant_router(const RouterRegs<NQ> &rr, int H, uint8_t *q,
-                                               float *s) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const int c = lane + WAVE * (wave + 4 * i);
-        if (c < H / 8) quant_chunk_to_lds(rr.x[i], c, q, s);  // whole 16-lane groups
-    }
-}
-
-// chunks beyond the register copy (more than XQ per thread) are loaded here
-__device__ __forceinline__ void x_quant(const uint16_t *x, int n_chunks, const XRegs &r,
-                                        uint8_t *q, float *s) {
-#pragma unroll
-    for (int k = 0; k < XQ; ++k) {
-        const int c = threadIdx.x + blockDim.x * k;
-        if (c < n_chunks) quant_chunk_to_lds(r.v[k], c, q, s);
-    }
-    for (int c = threadIdx.x + blockDim.x * XQ; c < n_chunks; c += blockDim.x)
-        quant_chunk_to_lds(ld16(x + (int64_t)c * 8), c, q, s);
+bool decode_fits(int T, int H, int K, int I, int Is) {
+    return T >= 1 && T <= DECODE_MAX_ROWS && lds_plan(T, H, K, I, Is).total <= 150 * 1024;
 }
 
 // h groups each 16-lane team stages per round of loads
@@ -739,10 +870,9 @@ __device__ __forceinline__ void quant8_strided_to_lds(const float (&f)[8], int g
 // Phase C inputs from this workgroup's copy, waiting for each word's epoch:
 // h (fp32, re-quantised 1x128 into LDS codes and scales), hs (bf16) and
 // gamma into LDS. stage_c_issue sends the first loads of hs, gamma and of the
-// first round of h; the caller can issue other loads (the routed down rows)
-// before stage_c_finish waits on them: loads return in issue order, so the
-// handoff words come back first and a workgroup pays one handoff round trip
-// here, not one per kind of value.
+// first round of h, in that order (a wave's loads return in issue order);
+// stage_c_finish_shared waits for hs and gamma alone, stage_c_finish_h for
+// h, so the shared down product can run in between.
 struct StageC {
     int sidx[8], gidx[1], hidx[8 * STAGE_HG];
     int n_s0, n_g, nk0;
@@ -785,33 +915,20 @@ __device__ __forceinline__ void stage_c_issue(const uint64_t *h, const uint64_t 
     c.gidx[0] = rp * T + tid;
     c.n_g = Is > 0 && tid < T ? 1 : 0;
     c.nk0 = stage_h_round(0, P * (I / GROUP), c.hidx);
-    poll_issue<8 * STAGE_HG>(h + (int64_t)rp * P * I, c.hidx, 8 * c.nk0, epoch, c.hw);
+    // hs and gamma first: they were written in phase A, and waiting for
+    // them must not also wait for the h words behind them
     poll_issue<8>(hs + (int64_t)rp * T * Is, c.sidx, c.n_s0, epoch, c.sw);
     poll_issue<1>(gamma, c.gidx, c.n_g, epoch, c.gw);
+    poll_issue<8 * STAGE_HG>(h + (int64_t)rp * P * I, c.hidx, 8 * c.nk0, epoch, c.hw);
 }
 
-__device__ __forceinline__ void stage_c_finish(const uint64_t *h, const uint64_t *hs,
-                                               const uint64_t *gamma, int T, int P, int I, int Is,
-                                               uint32_t epoch, uint32_t *err, StageC &c,
-                                               uint8_t *qh, float *shs, uint16_t *hs_l,
-                                               float *gam_l) {
-    const int rp = blockIdx.x % REPL, tid = threadIdx.x, nth = blockDim.x, teams = nth >> 4;
-    const uint64_t *hsrc = h + (int64_t)rp * P * I;
+__device__ __forceinline__ void stage_c_finish_shared(const uint64_t *hs, const uint64_t *gamma,
+                                                      int T, int Is, uint32_t epoch,
+                                                      uint32_t *err, StageC &c, uint16_t *hs_l,
+                                                      float *gam_l) {
+    const int rp = blockIdx.x % REPL, tid = threadIdx.x, nth = blockDim.x;
     const uint64_t *ssrc = hs + (int64_t)rp * T * Is;
-    const int n_groups = P * (I / GROUP), n_hs = T * Is;
-    {
-        uint32_t bits[8 * STAGE_HG];
-        poll_finish<8 * STAGE_HG>(err, hsrc, c.hidx, 8 * c.nk0, epoch, c.hw, bits);
-        stage_h_quant(0, c.nk0, bits, qh, shs);
-    }
-    for (int base = STAGE_HG * teams; base < n_groups; base += STAGE_HG * teams) {
-        int idx[8 * STAGE_HG];
-        const int nk = stage_h_round(base, n_groups, idx);
-        uint32_t bits[8 * STAGE_HG];
-        poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
-        stage_h_quant(base, nk, bits, qh, shs);
-    }
-    // hs: the first round, then any further rounds
+    const int n_hs = T * Is;
     {
         uint32_t bits[8];
         poll_finish<8>(err, ssrc, c.sidx, c.n_s0, epoch, c.sw, bits);
@@ -819,7 +936,12 @@ __device__ __forceinline__ void stage_c_finish(const uint64_t *h, const uint64_t
         for (int i = 0; i < 8; ++i)
             if (i < c.n_s0) hs_l[c.sidx[i]] = (uint16_t)bits[i];
     }
-    for (int b = nth * 8; b < n_hs; b += nth * 8) {
+    if (c.n_g) {
+        uint32_t bits[1];
+        poll_finish<1>(err, gamma, c.gidx, 1, epoch, c.gw, bits);
+        gam_l[tid] = __uint_as_float(bits[0]);
+    }
+    for (int b = nth * 8; b < n_hs; b += nth * 8) {  // further rounds of hs (Is > 512 rows)
         int idx[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) idx[i] = b + tid + nth * i;
@@ -830,61 +952,59 @@ __device__ __forceinline__ void stage_c_finish(const uint64_t *h, const uint64_t
         for (int i = 0; i < 8; ++i)
             if (i < n) hs_l[idx[i]] = (uint16_t)bits[i];
     }
-    if (c.n_g) {
-        uint32_t bits[1];
-        poll_finish<1>(err, gamma, c.gidx, 1, epoch, c.gw, bits);
-        gam_l[tid] = __uint_as_float(bits[0]);
+}
+
+__device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P, int I,
+                                                 uint32_t epoch, uint32_t *err, StageC &c,
+                                                 uint8_t *qh, float *shs) {
+    const int rp = blockIdx.x % REPL, teams = blockDim.x >> 4;
+    const uint64_t *hsrc = h + (int64_t)rp * P * I;
+    const int n_groups = P * (I / GROUP);
+    {
+        uint32_t bits[8 * STAGE_HG];
+        poll_complete<8 * STAGE_HG, 2>(err, handoff_region(hsrc, P * I), c.hidx, 8 * c.nk0, epoch,
+                                       c.hw, bits);
+        stage_h_quant(0, c.nk0, bits, qh, shs);
+    }
+    for (int base = STAGE_HG * teams; base < n_groups; base += STAGE_HG * teams) {
+        int idx[8 * STAGE_HG];
+        const int nk = stage_h_round(base, n_groups, idx);
+        uint32_t bits[8 * STAGE_HG];
+        poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
+        stage_h_quant(base, nk, bits, qh, shs);
     }
 }
 
-// Layer stacks: x_l = renorm(y_{l-1}) for every row, from this workgroup's
-// copy of the tagged y words, into LDS (bf16), with the arithmetic of the
-// stand-alone renormalisation kernel (same thread mapping and sum order).
-__device__ __forceinline__ void renorm_rows_to_lds(const uint64_t *ytag, int T, int H, float eps,
-                                   uint32_t epoch, uint32_t *err, uint16_t *xs, double *red) {
-    const int rp = blockIdx.x % REPL, tid = threadIdx.x, nc = H / 8;
+// Renormalising prologue: x_t = bf16(y_prev_t * rms scale) into LDS, every
+// workgroup for every row, with the stand-alone renormalisation's arithmetic
+// (renorm_row_scale, renorm_chunk). y_prev was written by an earlier launch.
+__device__ __forceinline__ void renorm_rows_to_lds(const uint16_t *y, int T, int H, float eps,
+                                                   uint16_t *xs, double *red) {
+    const int tid = threadIdx.x, nc = H / 8;
     for (int t = 0; t < T; ++t) {
-        const uint64_t *src = ytag + ((int64_t)rp * T + t) * H;
-        float v[RENORM_CHUNKS][8];
-        double acc = 0.0;
+        uint4 v[RENORM_CHUNKS];
 #pragma unroll
         for (int i = 0; i < RENORM_CHUNKS; ++i) {
             const int c = tid + 256 * i;
-            int idx[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) idx[k] = c * 8 + k;
-            uint32_t bits[8];
-            poll_words<8>(err, src, idx, c < nc ? 8 : 0, epoch, bits);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[i][k] = c < nc ? bf16_to_f32((uint16_t)bits[k]) : 0.0f;
-            acc = sumsq8(v[i], acc);
+            v[i] = c < nc ? ld16(y + (int64_t)t * H + c * 8) : make_uint4(0, 0, 0, 0);
         }
-        acc = wave_allsum_d(acc);
-        if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = acc;
-        __syncthreads();
-        const double sum = ((red[0] + red[1]) + red[2]) + red[3];
-        const float r = rms_scale(sum, H, eps);
+        const float r = renorm_row_scale(v, H, eps, red);
 #pragma unroll
         for (int i = 0; i < RENORM_CHUNKS; ++i) {
             const int c = tid + 256 * i;
-            if (c < nc) {
-                uint32_t o[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    o[k] = f32_to_bf16(v[i][2 * k] * r) | (f32_to_bf16(v[i][2 * k + 1] * r) << 16);
-                st16(xs + (int64_t)t * H + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
-            }
+            if (c < nc) st16(xs + t * H + c * 8, renorm_chunk(v[i], r));
         }
         __syncthreads();  // red is reused by the next row
     }
 }
 
-// STACK: a0.n_layers layers in sequence, one launch; otherwise one layer
-template <int NC, int KBR, int TPW, bool STACK>
-__global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
+// RN: the renormalising variant (x from y_prev in the prologue)
+template <int NQ, int KBR, int TPW, bool RN>
+__global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int T = a0.T, H = a0.H, K = a0.K, I = a0.I, E = a0.E, P = T * K;
-    const LdsPlan L = lds_plan(T, H, K, I, a0.Is, STACK);
+    const int T = a.T, H = a.H, K = a.K, I = a.I, E = a.E, P = T * K, Is = a.Is;
+    const int KB = H / GROUP, KH = (KB + 1) / 2;
+    const LdsPlan L = lds_plan(T, H, K, I, Is);
     uint8_t *qx = lds + L.qx;                                 // [T][H]
     float *sx = reinterpret_cast<float *>(lds + L.sx);        // [T][H/128]
     uint8_t *qh = lds + L.qh;                                 // [P][I]
@@ -894,19 +1014,22 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Is]
     float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
     float *ej = reinterpret_cast<float *>(lds + L.ej);          // [K][MB]
-    float *gsl = reinterpret_cast<float *>(lds + L.gsl);        // [MB]
+    float *ss = reinterpret_cast<float *>(lds + L.ss);          // [MB]
     double *rl = reinterpret_cast<double *>(lds + L.rl);        // [2][4]
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds + L.xs);    // [T][H]
+    uint4 *sdo = reinterpret_cast<uint4 *>(lds + L.sdo);        // [SDB][4][64]
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nw = a0.nwg * 4;
-    constexpr int NB = 2 * NC;        // bf16 H-row chunks per lane
-    constexpr int NQ = (NB + 3) / 4;  // the same per lane of a wave quarter
-    const int gw = wave * a0.nwg + blockIdx.x;  // workgroup-major wave index
+    const int wave = threadIdx.x >> 6;
+    const int nw = a.nwg * 4;
+    const int gw = wave * a.nwg + blockIdx.x;  // workgroup-major wave index
+    float *sq = reinterpret_cast<float *>(lds + L.sq + wave * al16i(KB * 16 * 4));
+    float2 *sp = reinterpret_cast<float2 *>(lds + L.sp + wave * al16i(KH * 8 * 8));
     // The counter's load goes out first but is waited for only after the
     // first weight loads have been issued: it is a full device-coherent round
     // trip, and nothing before the first tagged store needs the epoch.
-    uint32_t *counter = a0.sync + SYNC_FLAGS + blockIdx.x;
+    uint32_t *counter = a.sync + SYNC_FLAGS + blockIdx.x;
     const uint32_t cnt = ld_dev(counter);
+    uint32_t *err = a.sync + ERR_WORD;
 
     // phase-C units (t, MB-row block), workgroup-major; a workgroup past the
     // last unit loads the last unit's rows (unused), so its loads need no
@@ -914,215 +1037,157 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a0) {
     const int units = T * (H / MB);
     const int u_first = min((int)blockIdx.x, units - 1);
     const int t_first = u_first / (H / MB), m_first = (u_first % (H / MB)) * MB;
-    const int n_layers = STACK ? a0.n_layers : 1;
 
-    for (int l = 0; l < n_layers; ++l) {
-        FusedArgs a = a0;
-        if constexpr (STACK) {
-            const LayerPtrs lw = a0.layers[l];
-            a.router_w = lw.router_w;
-            a.bias = lw.bias;
-            a.w_gate = lw.w_gate;
-            a.s_gate = lw.s_gate;
-            a.w_up = lw.w_up;
-            a.s_up = lw.s_up;
-            a.w_down = lw.w_down;
-            a.s_down = lw.s_down;
-            a.sh_gate = lw.sh_gate;
-            a.sh_up = lw.sh_up;
-            a.sh_down = lw.sh_down;
-            a.sh_gate_w = lw.sh_gate_w;
-            // consecutive layers use alternate halves of every handoff region
-            const int64_t par = l & 1;
-            a.logits = a0.logits + par * REPL * T * E;
-            a.gamma = a0.gamma + par * REPL * T;
-            a.hs = a0.hs + par * REPL * T * a0.Is;
-            a.h = a0.h + par * REPL * P * I;
-            a.y = l == n_layers - 1 ? a0.y : (a0.ys ? a0.ys + (int64_t)l * T * H : nullptr);
-            a.ytag = l < n_layers - 1 ? a0.ytag + par * REPL * T * H : nullptr;
-            if (l > 0) a.x = reinterpret_cast<const uint16_t *>(lds + L.xs);
+    // A1: router logits, one per workgroup at a time (four waves each),
+    // before any other load; then x into LDS. In a stack's later layer the
+    // router rows go out first and the previous layer's output is
+    // renormalised into LDS while they are in flight.
+    const int n_logits = T * E;
+    uint32_t epoch;
+    {
+        RouterRegs<NQ> rr;
+        if constexpr (RN) {
+            if ((int)blockIdx.x < n_logits) router_load_w<NQ>(a, blockIdx.x, rr);
+            renorm_rows_to_lds(a.y_prev, T, H, a.eps, xs, reinterpret_cast<double *>(lds + L.red));
+            if ((int)blockIdx.x < n_logits) router_load_x<NQ, RN>(a, blockIdx.x, xs, rr);
+        } else {
+            if ((int)blockIdx.x < n_logits) router_load<NQ, RN>(a, blockIdx.x, xs, rr);
         }
-        DownRegs<KBR, TPW> dr;
+        epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt));
+        int round = 0;
+        for (int r = blockIdx.x; r < n_logits; r += a.nwg, ++round) {
+            if (round > 0) router_load<NQ, RN>(a, r, xs, rr);
+            router_logit<NQ>(a, r, rr, rl + 4 * (round & 1), epoch);
+        }
+        if (!RN && T == 1 && (int)blockIdx.x < n_logits) x_stage_router<NQ>(rr, H, xs, qx, sx);
+        else x_stage_rows<RN>(a.x, T, H, xs, qx, sx);
+    }
+    __syncthreads();  // xs, qx, sx ready
 
-        // A1: router logits, one per workgroup at a time (four waves each),
-        // before any other load; in a stack, once the previous layer's output
-        // is in and renormalised.
-        const int n_logits = T * E;
-        uint32_t epoch;
-        {
-            RouterRegs<NQ> rr;
-            if constexpr (STACK) {
-                epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt)) + 4u * (uint32_t)l;
-                if (l > 0) {
-                    renorm_rows_to_lds(a0.ytag + (int64_t)((l - 1) & 1) * REPL * T * H, T, H,
-                                       a0.eps, epoch - 4u, a0.sync + ERR_WORD,
-                                       reinterpret_cast<uint16_t *>(lds + L.xs),
-                                       reinterpret_cast<double *>(lds + L.red));
-                }
-            }
-            if ((int)blockIdx.x < n_logits) router_load<NQ>(a, blockIdx.x, rr);
-            if constexpr (!STACK) epoch = __builtin_amdgcn_readfirstlane(call_epoch(cnt));
-            int round = 0;
-            for (int r = blockIdx.x; r < n_logits; r += a0.nwg, ++round) {
-                if (round > 0) router_load<NQ>(a, r, rr);
-                router_logit<NQ>(a, r, rr, rl + 4 * (round & 1), epoch);
-            }
-            // one row: the workgroup's router loads hold all of x, which is
-            // quantised (1x128) into LDS from them, needed from phase B on
-            if (T == 1 && (int)blockIdx.x < n_logits) x_quant_router<NQ>(rr, H, qx, sx);
+    // A2: the shared expert's gate/up columns and the shared gate, on waves
+    // 1-3 (wave 0 runs the top-K next, and a wave with loads in flight would
+    // wait for them before its first poll)
+    if (wave > 0 && Is > 0) {
+        const int n_s = Is / 2, n_items = n_s + T;
+        for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
+            if (it < n_s) s_item(a, it, xs, sq, epoch);
+            else g_item(a, it - n_s, xs, epoch);
         }
+    }
 
-        // A2: shared-expert gate/up rows and the shared gate, one item per
-        // wave (waves 1-3 first: wave 0 runs the top-K next, and a wave with
-        // loads in flight would wait for them before its first poll).
-        const int n_items = a.Is > 0 ? T * a.Is + T : 0;
-        const int ia = (gw + nw - a0.nwg) % nw;  // this wave's first item
-        {
-            ItemARegs<NB> ir;
-            if (ia < n_items) {
-                itemA_load_w<NB>(a, ia, lane, ir);
-                itemA_load_x<NB>(a, ia, lane, ir);
-                itemA_compute<NB>(a, ia, lane, ir, epoch);
-            }
-        }
-        if (T > 1 || (int)blockIdx.x >= n_logits) {
-            XRegs xr;
-            x_load(a.x, T * H / 8, xr);
-            x_quant(a.x, T * H / 8, xr, qx, sx);  // needed from phase B on
-        }
-        for (int it = ia + nw; it < n_items; it += nw) {
-            ItemARegs<NB> ir;
-            itemA_load_w<NB>(a, it, lane, ir);
-            itemA_load_x<NB>(a, it, lane, ir);
-            itemA_compute<NB>(a, it, lane, ir, epoch);
-        }
-
-        // B: top-K per row (one wave per row) once its logits exist, then the
-        // routed gate/up rows
-        for (int t = wave; t < T; t += 4)
-            topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch,
-                        a.sync + ERR_WORD, lane, ids + t * K, wts + t * K,
-                        !a.bias && !(a.flags & K_LOGITS_FP32));
-        __syncthreads();
-        // The first unit's shared and routed down rows are issued right after
-        // this wave's first gate/up rows: they stream in behind them while the
-        // gate/up arithmetic and the h handoff run, and the gate/up wait is
-        // for its own rows only (straight-line loads, scheduling barrier).
-        const int per_pair = I / GU_ROWS;
-        {
-            const int it = min(gw, P * per_pair - 1);  // waves past the last item load it (unused)
-            const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
-            GateUpRegs<NC> gr;
-            gateup_load<NC>(a, n0, ids[p], lane, gr);
-            if (a.Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
-            down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
-            __builtin_amdgcn_sched_barrier(0);
-            if (gw < P * per_pair)
-                gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr,
-                                   epoch);
-        }
-        for (int it = gw + nw; it < P * per_pair; it += nw) {
-            const int p = it / per_pair, n0 = (it % per_pair) * GU_ROWS, t = p / K;
-            GateUpRegs<NC> gr;
-            gateup_load<NC>(a, n0, ids[p], lane, gr);
-            gateup_compute<NC>(a, p, n0, ids[p], qx + t * H, sx + t * (H / GROUP), lane, gr,
-                               epoch);
-        }
-
-        // C: h (re-quantised), hs and gamma into LDS once they exist, then
-        // whole output rows with the combine.
-        StageC sc;
-        stage_c_issue(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, sc);
+    // B: top-K per row (one wave per row) once its logits exist, then the
+    // routed gate/up items
+    for (int t = wave; t < T; t += 4)
+        topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
+                    threadIdx.x & 63, ids + t * K, wts + t * K,
+                    !a.bias && !(a.flags & K_LOGITS_FP32));
+    __syncthreads();
+    // The first unit's routed and shared down rows are issued right after
+    // this wave's first gate/up rows: they stream in behind them while the
+    // gate/up arithmetic and the h handoff run, and the gate/up wait is for
+    // its own rows only (straight-line loads, scheduling barrier).
+    const int per_pair = I / 4, n_items = P * per_pair;
+    DownRegs<KBR, TPW> dr;
+    {
+        const int it = min(gw, n_items - 1);  // waves past the last item load it (unused)
+        const int p = it / per_pair, n0 = (it % per_pair) * 4;
+        GateUpRegs gr;
+        gateup_load(a, ids[p], n0, 0, gr);
+        down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
+        if (Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         __builtin_amdgcn_sched_barrier(0);
-        stage_c_finish(a.h, a.hs, a.gamma, T, P, I, a.Is, epoch, a.sync + ERR_WORD, sc, qh, shs,
-                       hs_l, gam_l);
-        __syncthreads();
-        for (int u = blockIdx.x; u < units; u += a0.nwg) {
-            const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
-            if (u != (int)blockIdx.x) {
-                if (a.Is > 0) down_load_shared<KBR, TPW>(a, m0, dr);
-                down_load_routed<KBR, TPW>(a, t, m0, ids, dr);
-            }
-            down_unit<KBR, TPW>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, gsl, epoch);
+        if (gw < n_items) gateup_finish(a, p, n0, ids[p], gr, qx, sx, sp, epoch);
+    }
+    for (int it = gw + nw; it < n_items; it += nw) {
+        const int p = it / per_pair, n0 = (it % per_pair) * 4;
+        GateUpRegs gr;
+        gateup_load(a, ids[p], n0, 0, gr);
+        gateup_finish(a, p, n0, ids[p], gr, qx, sx, sp, epoch);
+    }
+
+    // C: hs and gamma (ready since phase A) into LDS, the first unit's
+    // shared down rows while h is still on its way, then h (re-quantised)
+    // into LDS once it exists, and whole output rows with the combine.
+    StageC sc;
+    stage_c_issue(a.h, a.hs, a.gamma, T, P, I, Is, epoch, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_c_finish_shared(a.hs, a.gamma, T, Is, epoch, err, sc, hs_l, gam_l);
+    if (Is > 0) down_stage_shared<KBR, TPW>(dr, sdo);
+    __syncthreads();
+    if (Is > 0 && wave == CHAIN_WAVE && (int)blockIdx.x < units) {
+        const float s = shared_down_chain(a, t_first, m_first, sdo, hs_l);
+        if ((threadIdx.x & 63) < MB) ss[threadIdx.x & 63] = s;
+    }
+    stage_c_finish_h(a.h, T, P, I, epoch, err, sc, qh, shs);
+    __syncthreads();
+    for (int u = blockIdx.x; u < units; u += a.nwg) {
+        const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
+        const bool first = u == (int)blockIdx.x;
+        if (!first) {
+            down_load_routed<KBR, TPW>(a, t, m0, ids, dr);
+            if (Is > 0) down_load_shared<KBR, TPW>(a, m0, dr);
         }
-        __syncthreads();  // LDS is reused by the next layer
+        down_unit<KBR, TPW>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, ss, sdo, !first);
     }
     // every wave has read the counter: advance it for the next call
-    if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 4u * (uint32_t)(n_layers - 1) + 1u);
+    if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 1u);
 }
 
-// KBR: K blocks of a down row held in registers (I / 128 up to 8); TPW:
-// MFMA tiles (slot pairs) per wave (K up to 8: one, up to 16: two)
-template <int NC, int TPW, bool STACK>
+// NQ: router chunks per lane (H / 2048, rounded up to 1 or 4); KBR: K blocks
+// of a down row held in registers (I / 128 up to 4; more are loaded in the
+// loop); TPW: MFMA tiles (slot pairs) per wave (K up to 8: one, up to 16:
+// two)
+template <int NQ, int TPW, bool RN>
 static hipError_t launch_t(const FusedArgs &a, size_t lds, hipStream_t st) {
     const dim3 grid(a.nwg), block(256);
     const int ib = a.I / GROUP;
 #define MOE_DECODE(KBRV) \
-    hipLaunchKernelGGL((decode_fused_kernel<NC, KBRV, TPW, STACK>), grid, block, lds, st, a)
+    hipLaunchKernelGGL((decode_fused_kernel<NQ, KBRV, TPW, RN>), grid, block, lds, st, a)
     if (ib <= 1) MOE_DECODE(1);
     else if (ib <= 2) MOE_DECODE(2);
-    else if (ib <= 4) MOE_DECODE(4);
-    else MOE_DECODE(8);
+    else MOE_DECODE(4);
 #undef MOE_DECODE
     return hipGetLastError();
 }
 
-template <int NC, bool STACK>
-static hipError_t launch_nc(const FusedArgs &a, size_t lds, hipStream_t st) {
-    if (a.K <= 8) return launch_t<NC, 1, STACK>(a, lds, st);
-    return launch_t<NC, 2, STACK>(a, lds, st);
+template <int NQ, bool RN>
+static hipError_t launch_nq(const FusedArgs &a, size_t lds, hipStream_t st) {
+    if (a.K <= 8) return launch_t<NQ, 1, RN>(a, lds, st);
+    return launch_t<NQ, 2, RN>(a, lds, st);
 }
 
-template <int NC, int KBR, int TPW, bool STACK>
+template <int NQ, int KBR, int TPW, bool RN>
 static void set_lds_limit() {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_fused_kernel<NC, KBR, TPW, STACK>),
+        reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
-template <int NC, int TPW, bool STACK>
-static void set_lds_limits_t() {
-    set_lds_limit<NC, 1, TPW, STACK>();
-    set_lds_limit<NC, 2, TPW, STACK>();
-    set_lds_limit<NC, 4, TPW, STACK>();
-    set_lds_limit<NC, 8, TPW, STACK>();
-}
-
-template <int NC, bool STACK>
+template <int NQ, bool RN>
 static void set_lds_limits() {
-    set_lds_limits_t<NC, 1, STACK>();
-    set_lds_limits_t<NC, 2, STACK>();
+    set_lds_limit<NQ, 1, 1, RN>();
+    set_lds_limit<NQ, 2, 1, RN>();
+    set_lds_limit<NQ, 4, 1, RN>();
+    set_lds_limit<NQ, 1, 2, RN>();
+    set_lds_limit<NQ, 2, 2, RN>();
+    set_lds_limit<NQ, 4, 2, RN>();
 }
 
-template <bool STACK>
-static hipError_t launch_decode(const FusedArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I, a.Is, STACK).total;
+hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {
+    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I, a.Is).total;
     if (lds > 64 * 1024) {
         static const bool once = [] {
-            set_lds_limits<1, STACK>();
-            set_lds_limits<2, STACK>();
-            set_lds_limits<4, STACK>();
-            set_lds_limits<8, STACK>();
+            set_lds_limits<1, false>();
+            set_lds_limits<4, false>();
+            set_lds_limits<1, true>();
+            set_lds_limits<4, true>();
             return true;
         }();
         (void)once;
     }
-    const int nc = (a.H / 16 + WAVE - 1) / WAVE;
-    if (nc <= 1) return launch_nc<1, STACK>(a, lds, st);
-    if (nc <= 2) return launch_nc<2, STACK>(a, lds, st);
-    if (nc <= 4) return launch_nc<4, STACK>(a, lds, st);
-    return launch_nc<8, STACK>(a, lds, st);
-}
-
-hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {
-    return launch_decode<false>(a, st);
-}
-
-// The one-launch layer stack is switched off: its first run took a memory
-// aperture fault whose cause has not been found, so the STACK variant of the
-// kernel is not instantiated and this refuses every call.
-hipError_t launch_decode_stack(const FusedArgs &, hipStream_t) {
-    return hipErrorNotSupported;
+    const bool rn = a.y_prev != nullptr;
+    if (a.H <= 2048) return rn ? launch_nq<1, true>(a, lds, st) : launch_nq<1, false>(a, lds, st);
+    return rn ? launch_nq<4, true>(a, lds, st) : launch_nq<4, false>(a, lds, st);
 }
 
 }  // namespace moe

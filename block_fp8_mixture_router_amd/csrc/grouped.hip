@@ -270,21 +270,6 @@ hipError_t launch_shared_tiles(int T, int32_t *perm, int32_t *tiles, int32_t *n_
     return hipGetLastError();
 }
 
-// ------------------------------------------------------- FP8 MFMA helpers
-
-__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
-
-// 16x16 output, K = 128 e4m3 per operand; E8M0 scales 127 = x1.
-__device__ __forceinline__ v4f mfma_fp8_k128(v8i a, v8i b) {
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
-}
-
 // ----------------------------------------------------------- gate / up
 // grid.x = max_tiles * (I / 128). Wave w owns output columns
 // [nb*128 + 32w, +32): two 16-column MFMA tiles for gate and two for up.
@@ -570,14 +555,6 @@ hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st) {
     else
         hipLaunchKernelGGL(grouped_down_kernel<1>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
-}
-
-// ------------------------------------------------- bf16 MFMA helpers
-
-__device__ __forceinline__ v8bf as_v8bf(uint4 v) { return __builtin_bit_cast(v8bf, v); }
-
-__device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------- shared gate / up

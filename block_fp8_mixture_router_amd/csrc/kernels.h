@@ -14,8 +14,7 @@ constexpr uint32_t K_LOGITS_FP32 = 1u << 1;
 hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, float *s,
                             hipStream_t st);
 
-// ---- renorm.hip (row RMS normalisation between stacked layers)
-constexpr int RENORM_CHUNKS = 4;  // 16-byte chunks per thread of 256: H <= 8192
+// ---- renorm.hip (row RMS normalisation between stacked layers; H <= 8192)
 hipError_t launch_rms_renorm(const uint16_t *y, int T, int H, float eps, uint16_t *x,
                              hipStream_t st);
 
@@ -47,20 +46,7 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *
                              float *gamma, bool packed, uint8_t *qx, float *sx,
                              hipStream_t st);
 
-// ---- decode.hip (row-at-a-time path: one persistent kernel per call)
-// one layer's weight pointers, laid out as moe_weights
-struct LayerPtrs {
-    const uint16_t *router_w;
-    const float *bias;
-    const uint8_t *w_gate;
-    const float *s_gate;
-    const uint8_t *w_up;
-    const float *s_up;
-    const uint8_t *w_down;
-    const float *s_down;
-    const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
-    const float *sh_s_gate, *sh_s_up, *sh_s_down;  // block-FP8 shared variant (unused here)
-};
+// ---- decode.hip (row-at-a-time path: one persistent kernel per layer)
 struct FusedArgs {
     int T, H, E, K, I, Is;
     uint32_t flags;
@@ -76,23 +62,23 @@ struct FusedArgs {
     uint64_t *gamma;   // [R][T] fp32
     uint64_t *hs;      // [R][T, Is] bf16 shared-expert SwiGLU output
     uint64_t *h;       // [R][T*K, I] fp32 routed SwiGLU output
-    uint32_t *sync;    // [32] spin-out flag, [SYNC_FLAGS + b] workgroup b's call counter
-    uint16_t *y;      // [T, H]
-    int nwg;          // workgroups = compute units (all co-resident)
-    // layer stacks: n_layers layers of this shape, x_{l+1} = renorm(y_l, eps)
-    const LayerPtrs *layers;  // device array [n_layers]
-    int n_layers;
+    uint32_t *sync;    // [ERR_WORD] spin-out flag, [SYNC_FLAGS + b] workgroup b's call counter
+    uint16_t *y;       // [T, H]
+    uint16_t *y2;      // [T, H] a second copy of y, or null
+    int nwg;           // workgroups = compute units (all co-resident)
+    // renormalising variant (the layers of a stack after the first): the
+    // layer's input is x = bf16(y_prev * rms scale), computed by every
+    // workgroup in the kernel's prologue (x is then unused)
+    const uint16_t *y_prev;  // [T, H], or null for the plain layer
     float eps;
-    uint64_t *ytag;   // [2][R][T, H] tagged bf16 outputs handed to the next layer
-    uint16_t *ys;     // [n_layers][T, H] every layer's output, or NULL
 };
-constexpr int DECODE_MAX_ROWS = 16;
+constexpr int DECODE_MAX_ROWS = 4;
 constexpr int DECODE_REPLICAS = 8;
 constexpr int SYNC_FLAGS = 64;
 constexpr int SYNC_WORDS = SYNC_FLAGS + 1024;  // up to 1024 workgroups
-bool decode_fits(int T, int H, int K, int I, int Is, bool stack = false);
+constexpr int SYNC_ERR_WORD = 32;              // the spin-out word
+bool decode_fits(int T, int H, int K, int I, int Is);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
-hipError_t launch_decode_stack(const FusedArgs &a, hipStream_t st);
 
 // ---- grouped.hip (expert-grouped MFMA path)
 struct GroupedArgs {

@@ -6,9 +6,9 @@
 // normalisation, with no learned gain:
 //   ms = fp32(sum of exact squares, in fp64, / H); r = 1 / sqrt(ms + eps);
 //   x  = bf16(y * r).
-// One workgroup per row: each thread loads up to four 16-byte chunks,
-// squares and sums them in fp64, a DPP wave sum and a fixed-order sum of the
-// four wave totals give the row sum. Reads and writes 2H bytes per row.
+// One workgroup per row, with the arithmetic of renorm_row_scale and
+// renorm_chunk (common.h), which the one-row layer kernel's renormalising
+// prologue also uses. Reads and writes 2H bytes per row.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,31 +26,14 @@ __global__ __launch_bounds__(256) void rms_renorm_kernel(const uint16_t *__restr
         const int c = threadIdx.x + 256 * i;
         v[i] = c < nc ? ld16(yr + c * 8) : make_uint4(0, 0, 0, 0);
     }
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 0; i < RENORM_CHUNKS; ++i) {
-        const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
-                            bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
-        acc = sumsq8(f, acc);  // chunks past H are zero and add nothing
-    }
-    acc = wave_allsum_d(acc);
-    if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = acc;
-    __syncthreads();  // every load of this row is done before any store (x may alias y)
-    const double sum = ((part[0] + part[1]) + part[2]) + part[3];
-    const float r = rms_scale(sum, H, eps);
+    // the barrier inside also orders every load of this row before any
+    // store (x may alias y)
+    const float r = renorm_row_scale(v, H, eps, part);
     uint16_t *xr = x + row * H;
 #pragma unroll
     for (int i = 0; i < RENORM_CHUNKS; ++i) {
         const int c = threadIdx.x + 256 * i;
-        if (c >= nc) continue;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float a = bf16_lo(w[k]) * r, b = bf16_hi(w[k]) * r;
-            o[k] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
-        }
-        st16(xr + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
+        if (c < nc) st16(xr + c * 8, renorm_chunk(v[i], r));
     }
 }
 

@@ -124,12 +124,19 @@ def test_renorm_refusals():
     assert L.moe_rms_renorm(Y, 4, 2048, ctypes.c_float(1e-6), Y, None) == -5  # no device
 
 
+def _fake_layers(n):
+    return (moe.Weights * n)(*[_fake_weights(0x10000000 + 0x4000000 * l) for l in range(n)])
+
+
 def test_stack_refusals():
+    """moe_forward_stack takes a host array of weight structs and checks every
+    layer's pointers on the host before anything is enqueued."""
     L = moe.lib()
     c = _cfg()
     cb = ctypes.byref(c)
     n = moe.workspace_bytes(c, 1)
-    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    TB = _fake_layers(40)
+    X, Y, WS = 0x20000000, 0x30000000, 0x40000000
     f = lambda *a: L.moe_forward_stack(*a)  # noqa: E731
     eps = ctypes.c_float(1e-6)
     assert f(cb, TB, 40, X, 1, eps, Y, None, WS, n, None) == -5      # no device
@@ -145,6 +152,26 @@ def test_stack_refusals():
     assert f(cb, TB, 40, X, 1, eps, X, None, WS, n, None) == -5      # y aliases x
     forced = _cfg(flags=moe.FORCE_GROUPED)
     assert f(ctypes.byref(forced), TB, 40, X, 1, eps, Y, None, WS, n, None) == -5
+    # every layer is checked: a missing or misaligned pointer in layer 17
+    bad = _fake_layers(40)
+    bad[17].w_up = None
+    assert f(cb, bad, 40, X, 1, eps, Y, None, WS, n, None) == -1
+    bad = _fake_layers(40)
+    bad[39].router_w = bad[39].router_w + 8
+    assert f(cb, bad, 40, X, 1, eps, Y, None, WS, n, None) == -3
+    # more rows than the one-row path takes
+    n5 = moe.workspace_bytes(c, 5)
+    assert f(cb, TB, 40, X, 5, eps, Y, None, WS, n5, None) == -5
+
+
+def test_decode_regions_do_not_move_with_rows():
+    """The one-row path's handoff regions are sized by the config alone, so
+    for T = 1..4 the workspace needed differs only by the grouped regions,
+    which all lie after them."""
+    c = _cfg()
+    g = _cfg(flags=moe.FORCE_GROUPED)
+    for T in range(1, 8):
+        assert moe.workspace_bytes(c, T) == moe.workspace_bytes(g, T)
 
 
 def test_supported_is_false_without_gpu():
@@ -192,11 +219,19 @@ def test_no_act_quant_flag():
     workspace, and is refused with the decode path forced or in a stack."""
     c, n = _cfg(), _cfg(flags=moe.NO_ACT_QUANT)
     s = inputs.DECODE
-    for T in (1, 1024):
-        extra = (T * s.top_k * s.inter * 2 + 255) // 256 * 256
-        assert moe.workspace_bytes(n, T) == moe.workspace_bytes(c, T) + extra
+
+    def extra(T):
+        return (T * s.top_k * s.inter * 2 + 255) // 256 * 256
+
+    # growth with rows is the plain layout's plus the bf16 h region; the
+    # control never takes the one-row path, so it has no handoff regions
+    grow_n = moe.workspace_bytes(n, 1024) - moe.workspace_bytes(n, 1)
+    grow_c = moe.workspace_bytes(c, 1024) - moe.workspace_bytes(c, 1)
+    assert grow_n == grow_c + extra(1024) - extra(1)
+    assert moe.workspace_bytes(n, 1) < moe.workspace_bytes(c, 1)
     L = moe.lib()
-    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    TB = _fake_layers(40)
+    X, Y, WS = 0x20000000, 0x30000000, 0x40000000
     eps = ctypes.c_float(1e-6)
     nb = moe.workspace_bytes(n, 1)
     assert L.moe_forward_stack(ctypes.byref(n), TB, 40, X, 1, eps, Y, None, WS, nb, None) == -5
@@ -213,7 +248,8 @@ def test_shared_fp8_flag():
     assert moe.workspace_bytes(f, 1024) > moe.workspace_bytes(c, 1024)
     assert moe.workspace_bytes(_cfg(flags=moe.SHARED_FP8 | moe.NO_ACT_QUANT), 1) == 0
     L = moe.lib()
-    TB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    TB = _fake_layers(40)
+    X, Y, WS = 0x20000000, 0x30000000, 0x40000000
     eps = ctypes.c_float(1e-6)
     nf = moe.workspace_bytes(f, 1)
     assert L.moe_forward_stack(ctypes.byref(f), TB, 40, X, 1, eps, Y, None, WS, nf, None) == -5

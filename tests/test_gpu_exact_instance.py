@@ -71,13 +71,13 @@ def _check(name, T, flags=0):
 
 
 @pytest.mark.parametrize("T,flags", [(1, 0), (3, 0), (5, 0), (70, 0), (1, moe.FORCE_GROUPED),
-                                     (9, moe.FORCE_GEMV), (16, moe.FORCE_GEMV)])
+                                     (2, moe.FORCE_GEMV), (4, moe.FORCE_GEMV)])
 def test_exact_tiny(T, flags):
     _check("tiny", T, flags)
 
 
 @pytest.mark.parametrize("T,flags", [(1, 0), (2, 0), (4, 0), (1, moe.FORCE_GROUPED),
-                                     (8, moe.FORCE_GEMV), (37, 0), (300, 0), (1023, 0),
+                                     (3, moe.FORCE_GEMV), (37, 0), (300, 0), (1023, 0),
                                      (1024, 0)])
 def test_exact_decode_shape(T, flags):
     """Up to the 1024-row chunk in the launch configuration the bench times

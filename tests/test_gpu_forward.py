@@ -41,12 +41,12 @@ CASES = [
     ("TINY", 5, 0, False),
     ("TINY", 70, 0, False),
     ("TINY", 1, moe.FORCE_GROUPED, False),
-    ("TINY", 9, moe.FORCE_GEMV, False),
+    ("TINY", 4, moe.FORCE_GEMV, False),
     ("DECODE", 1, 0, False),
     ("DECODE", 2, 0, False),
     ("DECODE", 4, 0, False),
     ("DECODE", 1, moe.FORCE_GROUPED, False),
-    ("DECODE", 7, moe.FORCE_GEMV, False),
+    ("DECODE", 3, moe.FORCE_GEMV, False),
     ("DECODE", 37, 0, False),
 ]
 
@@ -199,3 +199,34 @@ def test_forward_sort_capacity_edges(T):
     _check(shape, host, xh, y, rows=rows)
     y300 = run_forward(shape, dev, x[:300].contiguous())
     assert torch.equal(y[:300].view(torch.int16), y300.view(torch.int16))
+
+
+def test_force_gemv_beyond_four_rows_is_refused():
+    """The one-row path takes at most four rows; forcing it on five is
+    refused before anything is enqueued."""
+    shape, dev, _ = layer("DECODE", 0, False)
+    x, _ = x_rows(shape, 5, seed=9)
+    with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
+        run_forward(shape, dev, x, moe.FORCE_GEMV)
+
+
+def test_workspace_regions_do_not_move_with_rows():
+    """Grouped calls at few rows and one-row calls share a fresh zero-filled
+    workspace: a grouped call's plain data never lands where a later one-row
+    call polls for tagged words, so every output equals its lone call's."""
+    shape, dev, _ = layer("DECODE", 0, False)
+    cfg = moe.config(shape)
+    sequences = [
+        [(1, moe.FORCE_GROUPED), (4, 0)],
+        [(5, 0), (4, moe.FORCE_GEMV)],
+        [(2, moe.FORCE_GROUPED), (3, 0), (1, 0), (16, 0), (2, 0)],
+    ]
+    for seq in sequences:
+        say(f"workspace sequence {seq}")
+        ws = moe.alloc_workspace(cfg, max(T for T, _ in seq))
+        for i, (T, flags) in enumerate(seq):
+            x, _ = x_rows(shape, T, seed=60 + i)
+            want = run_forward(shape, dev, x, flags)
+            got = run_forward(shape, dev, x, flags, workspace=ws)
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (seq, i)
+        assert int(ws[128:132].view(torch.int32).item()) == 0

@@ -1,9 +1,9 @@
 """The 40-layer decode stack on the GPU: the row renormalisation between
 layers (bit-exact against the oracle); a chain of decode layers,
 teacher-forced against the oracle layer by layer (each oracle layer gets the
-GPU's input to that layer), eager and as a captured graph; and the one-launch
-stack (moe_forward_stack), which must equal that chain bit for bit (switched
-off: those tests are skipped, and the entry point must refuse)."""
+GPU's input to that layer), eager and as a captured graph; and
+moe_forward_stack, one launch per layer with the renormalisation folded into
+each later layer's prologue, which must equal that chain bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -16,10 +16,6 @@ from tests.gpu_common import OUT_TOL, bits, need_gpu, rel_rows, say
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
-STACK_OFF = pytest.mark.skip(
-    reason="moe_forward_stack is switched off: its one-launch kernel took a GPU memory "
-           "aperture fault on the first case (DECODE T=1 L=6) and the cause has not been "
-           "found; the entry point refuses every call until it is")
 
 
 @pytest.fixture(autouse=True)
@@ -129,34 +125,33 @@ def _chain_outputs(shape, layers, wstructs, x0, eps=EPS):
     return [bits(y.cpu()) for y in ys]
 
 
-@STACK_OFF
 @pytest.mark.parametrize("shape_name,T,L", [("DECODE", 1, 6), ("DECODE", 2, 3), ("TINY", 1, 5),
-                                            ("TINY", 4, 4), ("DECODE", 1, 1)])
+                                            ("TINY", 4, 4), ("DECODE", 1, 1), ("DECODE", 4, 2)])
 def test_forward_stack_equals_chain(shape_name, T, L):
     shape = getattr(inputs, shape_name)
-    say(f"stack kernel {shape_name} T={T} L={L}")
+    say(f"stack {shape_name} T={T} L={L}")
     layers = [inputs.make_layer(shape, seed=1, layer=200 + l, device="cuda") for l in range(L)]
     wstructs = [moe.weights_struct(lw) for lw in layers]
     x0 = inputs.make_x(shape, T, seed=43, device="cuda")
     want = _chain_outputs(shape, layers, wstructs, x0)
     cfg = moe.config(shape)
-    table = moe.layer_table(layers)
+    arr = moe.weights_array(layers)
     ws = moe.alloc_workspace(cfg, T)
     ys = torch.empty(L, T, shape.hidden, dtype=torch.bfloat16, device="cuda")
     for rep in range(3):  # repeated calls on one workspace (epochs advance)
-        y = moe.forward_stack(cfg, table, L, x0, ys=ys, eps=EPS, workspace=ws)
+        ys.fill_(float("nan"))
+        y = moe.forward_stack(cfg, arr, x0, ys=ys, eps=EPS, workspace=ws)
         torch.cuda.synchronize()
         for l in range(L):
             assert np.array_equal(bits(ys[l].cpu()), want[l]), (rep, l)
         assert np.array_equal(bits(y.cpu()), want[-1])
     assert int(ws[128:132].view(torch.int32).item()) == 0
-    # the last output alone, no per-layer outputs
-    y2 = moe.forward_stack(cfg, table, L, x0, eps=EPS, workspace=ws)
+    # the last output alone, no per-layer outputs (the workspace's buffers)
+    y2 = moe.forward_stack(cfg, arr, x0, eps=EPS, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(bits(y2.cpu()), want[-1])
 
 
-@STACK_OFF
 def test_forward_stack_graph_replays():
     shape, L = inputs.DECODE, 4
     layers = [inputs.make_layer(shape, seed=2, layer=300 + l, device="cuda") for l in range(L)]
@@ -164,32 +159,34 @@ def test_forward_stack_graph_replays():
     x0 = inputs.make_x(shape, 1, seed=44, device="cuda")
     want = _chain_outputs(shape, layers, wstructs, x0)
     cfg = moe.config(shape)
-    table = moe.layer_table(layers)
+    arr = moe.weights_array(layers)
     ws = moe.alloc_workspace(cfg, 1)
     y = torch.empty_like(x0)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        moe.forward_stack(cfg, table, L, x0, y=y, eps=EPS, workspace=ws, stream=stream)
+        moe.forward_stack(cfg, arr, x0, y=y, eps=EPS, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
-        moe.forward_stack(cfg, table, L, x0, y=y, eps=EPS, workspace=ws, stream=stream)
+        moe.forward_stack(cfg, arr, x0, y=y, eps=EPS, workspace=ws, stream=stream)
     for rep in range(3):
         y.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(y.cpu()), want[-1]), rep
+        # eager work on the same workspace between replays
+        moe.forward(cfg, layers[0], x0, workspace=ws, wstruct=wstructs[0])
+        torch.cuda.synchronize()
 
 
-def test_forward_stack_refuses_while_switched_off():
+def test_forward_stack_refuses_more_than_four_rows():
     shape = inputs.TINY
     layers = [inputs.make_layer(shape, seed=3, layer=l, device="cuda") for l in range(2)]
     cfg = moe.config(shape)
-    table = moe.layer_table(layers)
-    x0 = inputs.make_x(shape, 1, seed=45, device="cuda")
-    ws = moe.alloc_workspace(cfg, 1)
+    x0 = inputs.make_x(shape, 5, seed=45, device="cuda")
+    ws = moe.alloc_workspace(cfg, 5)
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
-        moe.forward_stack(cfg, table, 2, x0, eps=EPS, workspace=ws)
+        moe.forward_stack(cfg, layers, x0, eps=EPS, workspace=ws)
     torch.cuda.synchronize()
