@@ -23,6 +23,8 @@
 //    columns (one group) to e4m3 before anything leaves the CU.
 //  - No floating-point atomics anywhere: every sum has a fixed order, so
 //    results are bitwise deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,6 +32,22 @@ namespace moe {
 
 constexpr int GR = GROUP_ROWS;   // 64 rows per tile
 constexpr int APAD = 16;         // LDS row padding (bytes) against bank conflicts
+
+// Runs step(kb, slot, refill) for kb = 0 .. KB - 1 over a ring of PD slots.
+// The main loop refills every slot it consumes, so each of its iterations
+// issues the same loads and the compiler's wait counts stay exact (a load
+// issued on one path only makes it wait for every load in flight at the
+// loop head); the last PD steps, peeled, issue none. `refill` is a
+// compile-time constant. KB is a positive multiple of PD.
+template <int PD, typename F>
+__device__ __forceinline__ void ring_loop(int KB, F &step) {
+    int kb0 = 0;
+    for (; kb0 + PD < KB; kb0 += PD)
+#pragma unroll
+        for (int d = 0; d < PD; ++d) step(kb0 + d, d, std::true_type{});
+#pragma unroll
+    for (int d = 0; d < PD; ++d) step(kb0 + d, d, std::false_type{});
+}
 
 int grouped_max_tiles(int T, int K, int E) {
     const int64_t P = (int64_t)T * K;
@@ -345,47 +363,45 @@ __device__ void grouped_gateup_block(const GroupedArgs &a, int blk) {
     }
     __syncthreads();  // toks / sxs ready
 
-    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
-        const bool more = kb0 + PD < KB;  // uniform: the main loop or the last group
+    // one K step from ring slot d; with `more` it refills the slot with
+    // step kb + PD
+    auto step = [&](int kb, int d, auto more) {
+        uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
+        *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+        *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+        if constexpr (decltype(more)::value) load_a(kb + PD, av[d]);
+        __syncthreads();
+        const float sgk = sgr[kb], suk = sur[kb];
+        v8i cg[2], cu[2];
 #pragma unroll
-        for (int d = 0; d < PD; ++d) {
-            const int kb = kb0 + d;
-            uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
-            *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
-            *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
-            if (more) load_a(kb + PD, av[d]);
-            __syncthreads();
-            const float sgk = sgr[kb], suk = sur[kb];
-            v8i cg[2], cu[2];
+        for (int ct = 0; ct < 2; ++ct) {
+            cg[ct] = as_v8i(bg[d][ct][0], bg[d][ct][1]);
+            cu[ct] = as_v8i(bu[d][ct][0], bu[d][ct][1]);
+        }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                cg[ct] = as_v8i(bg[d][ct][0], bg[d][ct][1]);
-                cu[ct] = as_v8i(bu[d][ct][0], bu[d][ct][1]);
-            }
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt < nrt) {
+                const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
+                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                      *reinterpret_cast<const uint4 *>(ar + 16));
+                float sxr[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (rt < nrt) {
-                    const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
-                    const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
-                                          *reinterpret_cast<const uint4 *>(ar + 16));
-                    float sxr[4];
+                for (int i = 0; i < 4; ++i) sxr[i] = sxs[rt * 16 + 4 * kq + i][kb];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sxr[i] = sxs[rt * 16 + 4 * kq + i][kb];
+                for (int ct = 0; ct < 2; ++ct) {
+                    const v4f pg = mfma_fp8_k128(af, cg[ct]);
+                    const v4f pu = mfma_fp8_k128(af, cu[ct]);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const v4f pg = mfma_fp8_k128(af, cg[ct]);
-                        const v4f pu = mfma_fp8_k128(af, cu[ct]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            accg[rt][ct][i] = fmaf(sxr[i] * sgk, pg[i], accg[rt][ct][i]);
-                            accu[rt][ct][i] = fmaf(sxr[i] * suk, pu[i], accu[rt][ct][i]);
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        accg[rt][ct][i] = fmaf(sxr[i] * sgk, pg[i], accg[rt][ct][i]);
+                        accu[rt][ct][i] = fmaf(sxr[i] * suk, pu[i], accu[rt][ct][i]);
                     }
                 }
             }
-            if (more) load_b(kb + PD, bg[d], bu[d]);
         }
-    }
+        if constexpr (decltype(more)::value) load_b(kb + PD, bg[d], bu[d]);
+    };
+    ring_loop<PD>(KB, step);
 
     // epilogue: h = silu(g) * u, per-row amax over the 128 columns, e4m3
     float hv[4][2][4];
@@ -493,41 +509,39 @@ __global__ __launch_bounds__(256, 2) void grouped_down_kernel(GroupedArgs a) {
     }
     __syncthreads();  // shs and pairs ready
 
-    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
-        const bool more = kb0 + PD < KB;
+    // one K step from ring slot d; with `more` it refills the slot with
+    // step kb + PD
+    auto step = [&](int kb, int d, auto more) {
+        uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
+        *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+        *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+        if constexpr (decltype(more)::value) load_a(kb + PD, av[d]);
+        __syncthreads();
+        const float sdk = sdr[kb];
+        v8i cd[2];
 #pragma unroll
-        for (int d = 0; d < PD; ++d) {
-            const int kb = kb0 + d;
-            uint8_t(*Ab)[GROUP + APAD] = As[kb & 1];
-            *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
-            *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
-            if (more) load_a(kb + PD, av[d]);
-            __syncthreads();
-            const float sdk = sdr[kb];
-            v8i cd[2];
+        for (int ct = 0; ct < 2; ++ct) cd[ct] = as_v8i(bd[d][ct][0], bd[d][ct][1]);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) cd[ct] = as_v8i(bd[d][ct][0], bd[d][ct][1]);
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt < nrt) {
+                const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
+                const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
+                                      *reinterpret_cast<const uint4 *>(ar + 16));
+                float shr[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (rt < nrt) {
-                    const uint8_t *ar = &Ab[rt * 16 + l16][32 * kq];
-                    const v8i af = as_v8i(*reinterpret_cast<const uint4 *>(ar),
-                                          *reinterpret_cast<const uint4 *>(ar + 16));
-                    float shr[4];
+                for (int i = 0; i < 4; ++i) shr[i] = shs[rt * 16 + 4 * kq + i][kb];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) shr[i] = shs[rt * 16 + 4 * kq + i][kb];
+                for (int ct = 0; ct < 2; ++ct) {
+                    const v4f p = mfma_fp8_k128(af, cd[ct]);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const v4f p = mfma_fp8_k128(af, cd[ct]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[rt][ct][i] = fmaf(shr[i] * sdk, p[i], acc[rt][ct][i]);
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        acc[rt][ct][i] = fmaf(shr[i] * sdk, p[i], acc[rt][ct][i]);
                 }
             }
-            if (more) load_b(kb + PD, bd[d]);
         }
-    }
+        if constexpr (decltype(more)::value) load_b(kb + PD, bd[d]);
+    };
+    ring_loop<PD>(KB, step);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -548,9 +562,8 @@ __global__ __launch_bounds__(256, 2) void grouped_down_kernel(GroupedArgs a) {
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.max_tiles * (a.H / GROUP)));
     const int kb = a.I / GROUP;
-    if (kb % 4 == 0)
-        hipLaunchKernelGGL(grouped_down_kernel<4>, grid, dim3(256), 0, st, a);
-    else if (kb % 2 == 0)
+    // a ring two blocks deep keeps three workgroups per CU (four deep, two)
+    if (kb % 2 == 0)
         hipLaunchKernelGGL(grouped_down_kernel<2>, grid, dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL(grouped_down_kernel<1>, grid, dim3(256), 0, st, a);
@@ -609,39 +622,37 @@ __device__ void shared_gateup_block(const GroupedArgs &a, int blk) {
     };
 #pragma unroll
     for (int d = 0; d < PD; ++d) load(d, bg[d], bu[d], av[d]);
-    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
-        const bool more = kb0 + PD < KB;
+    // one K step from ring slot d; with `more` it refills the slot with
+    // step kb + PD
+    auto step = [&](int kb, int d, auto more) {
+        {
+            uint8_t(*Ab)[GROUP * 2 + APAD] = Ash[kb & 1];
 #pragma unroll
-        for (int d = 0; d < PD; ++d) {
-            const int kb = kb0 + d;
-            {
-                uint8_t(*Ab)[GROUP * 2 + APAD] = Ash[kb & 1];
-#pragma unroll
-                for (int r = 0; r < ARR; ++r) {
-                    *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol]) = av[d][r][0];
-                    *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol + 16]) = av[d][r][1];
-                }
-                __syncthreads();
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) {
-                    const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
-                    v4f pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
-                        pg = mfma_bf16_k32(af, as_v8bf(bg[d][i]), pg);
-                        pu = mfma_bf16_k32(af, as_v8bf(bu[d][i]), pu);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        dg[rt][i] += (double)pg[i];
-                        du[rt][i] += (double)pu[i];
-                    }
-                }
-                if (more) load(kb + PD, bg[d], bu[d], av[d]);
+            for (int r = 0; r < ARR; ++r) {
+                *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol]) = av[d][r][0];
+                *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol + 16]) = av[d][r][1];
             }
+            __syncthreads();
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
+                v4f pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+                    pg = mfma_bf16_k32(af, as_v8bf(bg[d][i]), pg);
+                    pu = mfma_bf16_k32(af, as_v8bf(bu[d][i]), pu);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dg[rt][i] += (double)pg[i];
+                    du[rt][i] += (double)pu[i];
+                }
+            }
+            if constexpr (decltype(more)::value) load(kb + PD, bg[d], bu[d], av[d]);
         }
-    }
+    };
+    ring_loop<PD>(KB, step);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -734,31 +745,29 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
         };
 #pragma unroll
         for (int d = 0; d < PD; ++d) load(d, b[d], av[d]);
-        for (int kb0 = 0; kb0 < KB; kb0 += PD) {
-            const bool more = kb0 + PD < KB;
+        // one K step from ring slot d; with `more` it refills the slot with
+        // step kb + PD
+        auto step = [&](int kb, int d, auto more) {
+            {
+                uint8_t(*Ab)[GROUP * 2 + APAD] = As[kb & 1];
+                *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
+                *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
+                __syncthreads();
 #pragma unroll
-            for (int d = 0; d < PD; ++d) {
-                const int kb = kb0 + d;
-                {
-                    uint8_t(*Ab)[GROUP * 2 + APAD] = As[kb & 1];
-                    *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
-                    *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
-                    __syncthreads();
+                for (int rt = 0; rt < 2; ++rt) {
+                    const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) {
-                        const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
+                    for (int i = 0; i < 4; ++i) {
+                        const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
-#pragma unroll
-                            for (int ct = 0; ct < 2; ++ct)
-                                acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[d][ct][i]), acc[rt][ct]);
-                        }
+                        for (int ct = 0; ct < 2; ++ct)
+                            acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[d][ct][i]), acc[rt][ct]);
                     }
-                    if (more) load(kb + PD, b[d], av[d]);
                 }
+                if constexpr (decltype(more)::value) load(kb + PD, b[d], av[d]);
             }
-        }
+        };
+        ring_loop<PD>(KB, step);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
