@@ -104,7 +104,7 @@ int decode_rows_max(const moe_config *c) {
 
 struct Layout {
     size_t sync, dlogits, dgamma, dhs, dh, ybuf, logits, absums, ids, wts, gamma, hs, qx, sx,
-        offsets, perm, tiles, n_tiles, qh, sh, stage, hb, sperm, stiles, sntiles, sqh, ssh, es;
+        offsets, perm, tiles, n_tiles, qh, sh, stage, hb, sperm, stiles, sntiles, sqh, ssh, so;
     size_t total;
     int max_tiles;
 };
@@ -152,14 +152,16 @@ Layout layout_of(const moe_config *c, int T) {
     // bf16 h of the no-activation-quantisation control
     L.hb = take((c->flags & MOE_NO_ACT_QUANT) ? t * K * I * 2 : 0);
     // the block-FP8 shared expert as one more grouped expert over all rows:
-    // its pair list and tiles, its h codes and scales, and its output
+    // its pair list and tiles, its h codes and scales
     const bool sfp8 = (c->flags & MOE_SHARED_FP8) && Is > 0;
     L.sperm = take(sfp8 ? t * 4 : 0);
     L.stiles = take(sfp8 ? (t + GROUP_ROWS - 1) / GROUP_ROWS * 16 : 0);
     L.sntiles = take(sfp8 ? 4 : 0);
     L.sqh = take(sfp8 ? t * Is : 0);
     L.ssh = take(sfp8 ? t * (Is / 128) * 4 : 0);
-    L.es = take(sfp8 ? t * H * 2 : 0);
+    // the shared expert's output s for the combine: fp32 from the bf16
+    // expert, bf16 (in the first half) from the block-FP8 one
+    L.so = take(Is > 0 ? t * H * 4 : 0);
     L.total = off;
     return L;
 }
@@ -401,6 +403,7 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     g.hs = at<uint16_t>(workspace, L.hs);
     g.stage = at<uint16_t>(workspace, L.stage);
     g.hb = noq ? at<uint16_t>(workspace, L.hb) : nullptr;
+    g.ss = (shared && !sfp8) ? at<float>(workspace, L.so) : nullptr;
     g.y = static_cast<uint16_t *>(y);
     const uint16_t *rw = static_cast<const uint16_t *>(w->router_w);
     const uint16_t *gw = shared ? static_cast<const uint16_t *>(w->sh_gate_w) : nullptr;
@@ -422,12 +425,13 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     GroupedArgs gr = g;
     if (sfp8) gr.Is = 0;
     if (noq) {
-        // the bf16 shared expert's tiles alone (the launch holds no routed
-        // tiles when max_tiles is 0), then the control's routed products
+        // the bf16 shared expert's tiles alone (the launches hold no routed
+        // tiles when max_tiles is 0) around the control's routed products
         GroupedArgs gs = gr;
         gs.max_tiles = 0;
         MOE_TRY(launch_expert_gateup(gs, st));
         MOE_TRY(launch_grouped_noq(gr, st));
+        MOE_TRY(launch_grouped_down(gs, st));
     } else {
         MOE_TRY(launch_expert_gateup(gr, st));
         MOE_TRY(launch_grouped_down(gr, st));
@@ -451,13 +455,13 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
         gs.max_tiles = (T + GROUP_ROWS - 1) / GROUP_ROWS;
         gs.qh = at<uint8_t>(workspace, L.sqh);
         gs.sh = at<float>(workspace, L.ssh);
-        gs.stage = at<uint16_t>(workspace, L.es);
+        gs.stage = at<uint16_t>(workspace, L.so);
         MOE_TRY(launch_shared_tiles(T, gs.perm, gs.tiles, gs.n_tiles, st));
         MOE_TRY(launch_expert_gateup(gs, st));
         MOE_TRY(launch_grouped_down(gs, st));
         gr.es = gs.stage;
     }
-    MOE_TRY(launch_shared_down_combine(gr, st));
+    MOE_TRY(launch_combine(gr, st));
     return MOE_OK;
 }
 

@@ -454,14 +454,21 @@ __device__ void grouped_gateup_block(const GroupedArgs &a, int blk) {
 // (row, slot) pair's own row of the stage buffer. Up to four K steps
 // (the whole K = I = 512 extent) are kept in flight.
 
+struct DownSmem {
+    uint8_t As[2][GR][GROUP + APAD];
+    float shs[GR][32];
+    int pairs[GR];
+    uint16_t Ys[GR][GROUP + 8];
+};
+
 template <int PD>
-__global__ __launch_bounds__(256, 2) void grouped_down_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[2][GR][GROUP + APAD];
-    __shared__ float shs[GR][32];
-    __shared__ int pairs[GR];
-    __shared__ __align__(16) uint16_t Ys[GR][GROUP + 8];
+__device__ void grouped_down_block(const GroupedArgs &a, int blk, DownSmem &sm) {
+    auto &As = sm.As;
+    auto &shs = sm.shs;
+    auto &pairs = sm.pairs;
+    auto &Ys = sm.Ys;
     const int mbs = a.H / GROUP;
-    const int tile = blockIdx.x / mbs, mb = blockIdx.x % mbs;
+    const int tile = blk / mbs, mb = blk % mbs;
     if (tile >= *a.n_tiles) return;
     const int e = a.tiles[4 * tile], r0 = a.tiles[4 * tile + 1], nr = a.tiles[4 * tile + 2];
     const int H = a.H, I = a.I, KB = I / GROUP;
@@ -559,14 +566,129 @@ __global__ __launch_bounds__(256, 2) void grouped_down_kernel(GroupedArgs a) {
     }
 }
 
+// ------------------------------------------------------ shared down
+// Tile: SDR = 64 rows x 128 columns mb of H; wave w owns columns
+// mb*128 + 32w .. +32 (two 16-column MFMA tiles) for all rows. Per
+// 128-element step of Is, each lane reads 64 contiguous bytes of its weight
+// row and splits them over four bf16 MFMAs (MFMA i takes elements
+// [32 kq + 8 i, +8) of lane (l16, kq)); the hs rows go through a
+// double-buffered LDS tile with the same split. The MFMAs of a tile form
+// one chain over Is in ascending order (the one-row kernel runs the same
+// chain), and s leaves in fp32 for the combine.
+constexpr int SDR = 64;
+
+struct SharedDownSmem {
+    uint8_t As[2][SDR][GROUP * 2 + APAD];
+};
+
+template <int PD>
+__device__ void shared_down_block(const GroupedArgs &a, int blk, SharedDownSmem &sm) {
+    constexpr int NRT = SDR / 16, ARR = SDR / 32;
+    auto &As = sm.As;
+    const int mbs = a.H / GROUP;
+    const int t0 = (blk / mbs) * SDR, mb = blk % mbs;
+    const int H = a.H, Is = a.Is, KB = Is / GROUP;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int arow = tid >> 3, acol = (tid & 7) * 32;  // bytes
+    const uint8_t *aptr[ARR];
+#pragma unroll
+    for (int r = 0; r < ARR; ++r) {
+        const int at = min(t0 + arow + 32 * r, a.T - 1);  // rows past T read a valid row
+        aptr[r] = reinterpret_cast<const uint8_t *>(a.hs + (int64_t)at * Is) + acol;
+    }
+    const uint8_t *wp[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int m = mb * GROUP + 32 * wave + 16 * ct + l16;
+        wp[ct] = reinterpret_cast<const uint8_t *>(a.sh_down + (int64_t)m * Is) + 64 * kq;
+    }
+    v4f acc[NRT][2];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+    uint4 b[PD][2][4], av[PD][ARR][2];
+    auto load = [&](int kb, uint4 (&bb)[2][4], uint4 (&x)[ARR][2]) {
+        const int off = kb * GROUP * 2;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bb[ct][i] = ld16(wp[ct] + off + 16 * i);
+#pragma unroll
+        for (int r = 0; r < ARR; ++r) {
+            x[r][0] = ld16(aptr[r] + off);
+            x[r][1] = ld16(aptr[r] + off + 16);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < PD; ++d) load(d, b[d], av[d]);
+    // one K step from ring slot d; with `more` it refills the slot with
+    // step kb + PD
+    auto step = [&](int kb, int d, auto more) {
+        uint8_t(*Ab)[GROUP * 2 + APAD] = As[kb & 1];
+#pragma unroll
+        for (int r = 0; r < ARR; ++r) {
+            *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol]) = av[d][r][0];
+            *reinterpret_cast<uint4 *>(&Ab[arow + 32 * r][acol + 16]) = av[d][r][1];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[d][ct][i]), acc[rt][ct]);
+            }
+        }
+        if constexpr (decltype(more)::value) load(kb + PD, b[d], av[d]);
+    };
+    ring_loop<PD>(KB, step);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + rt * 16 + 4 * kq + i;
+            if (t < a.T)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    a.ss[(int64_t)t * H + mb * GROUP + 32 * wave + 16 * ct + l16] = acc[rt][ct][i];
+        }
+}
+
+// One launch for both down products: the bf16 shared expert's tiles first
+// (they need only hs and the shared weights), then the routed tiles. The
+// two kinds of tile share one LDS buffer.
+template <int PD, int SPD>
+__global__ __launch_bounds__(256, 2) void expert_down_kernel(GroupedArgs a, int n_shared) {
+    __shared__ __align__(16) uint8_t smem[sizeof(DownSmem) > sizeof(SharedDownSmem)
+                                             ? sizeof(DownSmem)
+                                             : sizeof(SharedDownSmem)];
+    if ((int)blockIdx.x < n_shared) {
+        shared_down_block<SPD>(a, blockIdx.x, *reinterpret_cast<SharedDownSmem *>(smem));
+        return;
+    }
+    grouped_down_block<PD>(a, blockIdx.x - n_shared, *reinterpret_cast<DownSmem *>(smem));
+}
+
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(a.max_tiles * (a.H / GROUP)));
-    const int kb = a.I / GROUP;
-    // a ring two blocks deep keeps three workgroups per CU (four deep, two)
-    if (kb % 2 == 0)
-        hipLaunchKernelGGL(grouped_down_kernel<2>, grid, dim3(256), 0, st, a);
+    const int n_shared = a.Is > 0 ? ((a.T + SDR - 1) / SDR) * (a.H / GROUP) : 0;
+    const dim3 grid((unsigned)(n_shared + a.max_tiles * (a.H / GROUP)));
+    if (grid.x == 0) return hipSuccess;
+    const int kb = a.I / GROUP, skb = a.Is / GROUP;
+    // a ring two blocks deep keeps three workgroups per CU (four deep, two);
+    // Is = 0 (no shared tiles) counts as even
+    if (kb % 2 == 0 && skb % 2 == 0)
+        hipLaunchKernelGGL((expert_down_kernel<2, 2>), grid, dim3(256), 0, st, a, n_shared);
+    else if (kb % 2 == 0)
+        hipLaunchKernelGGL((expert_down_kernel<2, 1>), grid, dim3(256), 0, st, a, n_shared);
+    else if (skb % 2 == 0)
+        hipLaunchKernelGGL((expert_down_kernel<1, 2>), grid, dim3(256), 0, st, a, n_shared);
     else
-        hipLaunchKernelGGL(grouped_down_kernel<1>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_down_kernel<1, 1>), grid, dim3(256), 0, st, a, n_shared);
     return hipGetLastError();
 }
 
@@ -692,90 +814,37 @@ hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// ------------------------------------------- shared down + combine
+// ---------------------------------------------------------- combine
 // Tile: 32 rows x 128 columns of H; grid (ceil(T/32), H/128). Each thread
-// first issues the loads of the staged e_j it will combine (two 8-column
-// items, K slots each), then the shared expert's down product runs on
-// bf16 MFMA into LDS, then each thread produces 8 contiguous outputs
-// y = bf16(sum_j w_j e_j + gamma s) from its 16-byte loads, slots in order.
+// owns two items (row, 8 contiguous columns): it issues the 16-byte loads
+// of the item's staged e_j (K slots) and shared output s (fp32 from the
+// bf16 shared expert, bf16 from the block-FP8 one), then produces
+// y = bf16(sum_j w_j e_j + gamma s), slots in order.
 
-template <int KMAX, int PD>
-__global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a) {
-    __shared__ __align__(16) uint8_t As[2][SR][GROUP * 2 + APAD];
-    __shared__ __align__(16) float Ss[SR][GROUP + 4];
-    const int H = a.H, Is = a.Is, K = a.K;
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_kernel(GroupedArgs a) {
+    const int H = a.H, K = a.K;
     const int t0 = blockIdx.x * SR, mb = blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int l16 = lane & 15, kq = lane >> 4;
-    // the combine items of this thread: (row, 8-column chunk) = idx, idx + 256
-    uint4 ev[2][KMAX];
+    const int tid = threadIdx.x;
+    // every load first (rows past T read row T - 1, slots past K slot K - 1;
+    // neither is used), then the arithmetic
+    uint4 ev[2][KMAX], sv[2][2];
+    float wv[2][KMAX], gv[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int idx = tid + 256 * it;
         const int t = min(t0 + (idx >> 4), a.T - 1), c = idx & 15;
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-            if (j < K) ev[it][j] = ld16(a.stage + ((int64_t)t * K + j) * H + mb * GROUP + c * 8);
-    }
-    if (Is > 0) {
-        const int arow = tid >> 3, acol = (tid & 7) * 32;
-        const int at = min(t0 + arow, a.T - 1);
-        const uint8_t *aptr = reinterpret_cast<const uint8_t *>(a.hs + (int64_t)at * Is) + acol;
-        const uint8_t *wp[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int m = mb * GROUP + 32 * wave + 16 * ct + l16;
-            wp[ct] = reinterpret_cast<const uint8_t *>(a.sh_down + (int64_t)m * Is) + 64 * kq;
+        for (int j = 0; j < KMAX; ++j) {
+            const int jj = j < K ? j : K - 1;
+            ev[it][j] = ld16(a.stage + ((int64_t)t * K + jj) * H + mb * GROUP + c * 8);
+            wv[it][j] = a.wts[(int64_t)t * K + jj];
         }
-        v4f acc[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-        const int KB = Is / GROUP;
-        uint4 b[PD][2][4], av[PD][2];
-        auto load = [&](int kb, uint4 (&bb)[2][4], uint4 (&x)[2]) {
-            const int off = kb * GROUP * 2;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) bb[ct][i] = ld16(wp[ct] + off + 16 * i);
-            x[0] = ld16(aptr + off);
-            x[1] = ld16(aptr + off + 16);
-        };
-#pragma unroll
-        for (int d = 0; d < PD; ++d) load(d, b[d], av[d]);
-        // one K step from ring slot d; with `more` it refills the slot with
-        // step kb + PD
-        auto step = [&](int kb, int d, auto more) {
-            {
-                uint8_t(*Ab)[GROUP * 2 + APAD] = As[kb & 1];
-                *reinterpret_cast<uint4 *>(&Ab[arow][acol]) = av[d][0];
-                *reinterpret_cast<uint4 *>(&Ab[arow][acol + 16]) = av[d][1];
-                __syncthreads();
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const uint8_t *ar = &Ab[rt * 16 + l16][64 * kq];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const v8bf af = as_v8bf(*reinterpret_cast<const uint4 *>(ar + 16 * i));
-#pragma unroll
-                        for (int ct = 0; ct < 2; ++ct)
-                            acc[rt][ct] = mfma_bf16_k32(af, as_v8bf(b[d][ct][i]), acc[rt][ct]);
-                    }
-                }
-                if constexpr (decltype(more)::value) load(kb + PD, b[d], av[d]);
-            }
-        };
-        ring_loop<PD>(KB, step);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Ss[rt * 16 + 4 * kq + i][32 * wave + 16 * ct + l16] = acc[rt][ct][i];
-        __syncthreads();
+        const float *sp = a.ss ? a.ss + (int64_t)t * H + mb * GROUP + c * 8 : nullptr;
+        const uint16_t *ep = a.es ? a.es + (int64_t)t * H + mb * GROUP + c * 8 : nullptr;
+        sv[it][0] = sp ? ld16(sp) : ep ? ld16(ep) : make_uint4(0, 0, 0, 0);
+        sv[it][1] = sp ? ld16(sp + 4) : make_uint4(0, 0, 0, 0);
+        gv[it] = a.gamma[t];
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -787,7 +856,7 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (j < K) {
-                const float w = a.wts[(int64_t)t * K + j];
+                const float w = wv[it][j];
                 const uint32_t vs[4] = {ev[it][j].x, ev[it][j].y, ev[it][j].z, ev[it][j].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -795,13 +864,15 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
                     acc8[2 * i + 1] = fmaf(w, bf16_hi(vs[i]), acc8[2 * i + 1]);
                 }
             }
-        if (Is > 0) {
-            const float g = a.gamma[t];
+        if (a.ss) {  // the bf16 shared expert's fp32 output
+            const float g = gv[it];
+            const uint32_t u[8] = {sv[it][0].x, sv[it][0].y, sv[it][0].z, sv[it][0].w,
+                                   sv[it][1].x, sv[it][1].y, sv[it][1].z, sv[it][1].w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc8[i] = fmaf(g, Ss[row][c * 8 + i], acc8[i]);
+            for (int i = 0; i < 8; ++i) acc8[i] = fmaf(g, __uint_as_float(u[i]), acc8[i]);
         } else if (a.es) {  // the block-FP8 shared expert's staged output
-            const float g = a.gamma[t];
-            const uint4 v = ld16(a.es + (int64_t)t * H + mb * GROUP + c * 8);
+            const float g = gv[it];
+            const uint4 v = sv[it][0];
             const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -818,19 +889,14 @@ __global__ __launch_bounds__(256) void shared_down_combine_kernel(GroupedArgs a)
     }
 }
 
-hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st) {
+hipError_t launch_combine(const GroupedArgs &a, hipStream_t st) {
     const dim3 grid((a.T + SR - 1) / SR, a.H / GROUP);
-    const bool even = (a.Is / GROUP) % 2 == 0;  // Is = 0 counts as even
-    if (a.K <= 4) {
-        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<4, 2>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((shared_down_combine_kernel<4, 1>), grid, dim3(256), 0, st, a);
-    } else if (a.K <= 8) {
-        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<8, 2>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((shared_down_combine_kernel<8, 1>), grid, dim3(256), 0, st, a);
-    } else {
-        if (even) hipLaunchKernelGGL((shared_down_combine_kernel<16, 2>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((shared_down_combine_kernel<16, 1>), grid, dim3(256), 0, st, a);
-    }
+    if (a.K <= 4)
+        hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, st, a);
+    else if (a.K <= 8)
+        hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

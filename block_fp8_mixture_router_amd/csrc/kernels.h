@@ -103,6 +103,7 @@ struct GroupedArgs {
     uint16_t *stage;     // [T*K, H] bf16 expert outputs e_j, pair order
     uint16_t *hb;        // [T*K, I] bf16 h, sorted order (no-quantisation control only)
     const uint16_t *es;  // [T, H] bf16 block-FP8 shared expert output, or null
+    float *ss;           // [T, H] fp32 bf16 shared expert's down output, or null
     uint16_t *y;         // [T, H]
 };
 constexpr int GROUP_ROWS = 64;  // rows (token, slot) per MFMA work tile
@@ -111,9 +112,11 @@ hipError_t launch_group_sort(const GroupedArgs &a, hipStream_t st);
 // the shared expert's gate/up (when Is > 0) and the routed experts' gate/up,
 // one launch
 hipError_t launch_expert_gateup(const GroupedArgs &a, hipStream_t st);
+// the shared expert's down (when Is > 0, into ss) and the routed experts'
+// down (into stage), one launch
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t st);
-
-hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t st);
+// y = sum_j w_j e_j + gamma s, from stage and ss (or es)
+hipError_t launch_combine(const GroupedArgs &a, hipStream_t st);
 // the no-activation-quantisation control: routed gate/up and down on bf16
 // activations and decoded e4m3 weights (writes hb, then stage)
 hipError_t launch_grouped_noq(const GroupedArgs &a, hipStream_t st);
