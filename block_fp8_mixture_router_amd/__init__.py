@@ -25,7 +25,7 @@ FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
            "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant",
-           "moe_bf16_gemv")
+           "moe_bf16_gemv", "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +70,8 @@ def lib():
         L.moe_quant_act.restype = ctypes.c_int
         L.moe_forward.argtypes = [vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [vp, vp, vp, i32, vp, vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_rms_renorm.restype = ctypes.c_int
         L.moe_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
@@ -225,6 +227,19 @@ def weights_struct(lw) -> Weights:
     """Weights struct from an object with the tensor attributes of
     inputs.LayerWeights (all on the device)."""
     return Weights(**{k: _ptr(getattr(lw, k, None)) for k, _ in Weights._fields_})
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20  # MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def forward_noalloc(cfg: Config, lw, x, y, stream=None, wstruct=None):
+    """Whole layer through moe_forward_noalloc (the library's own workspace):
+    y bf16 [T, H], allocated by the caller."""
+    T = x.shape[0]
+    ws = wstruct if wstruct is not None else weights_struct(lw)
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(cfg), ctypes.byref(ws), _ptr(x), T, _ptr(y), _stream(stream)))
+    return y
 
 
 def forward(cfg: Config, lw, x, y=None, workspace=None, stream=None, wstruct=None):

@@ -343,22 +343,40 @@ moe_status check_weights(const moe_config *cfg, const moe_weights *w) {
 }
 }  // namespace
 
-moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int32_t T,
-                       void *y, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace moe {
+// moe_forward's host-side checks, in its order; with own_workspace the
+// workspace pointer and size are the library's (not checked here)
+moe_status forward_checks(const moe_config *cfg, const moe_weights *w, const void *x, int32_t T,
+                          const void *y, const void *workspace, size_t workspace_bytes,
+                          bool own_workspace) {
     moe_status s = check_cfg(cfg);
     if (s != MOE_OK) return s;
     if (T < 0 || T > MAX_ROWS) return MOE_E_SHAPE;
     if (T == 0) return MOE_OK;
-    if (!w || !x || !y || !workspace) return MOE_E_NULL;
+    if (!w || !x || !y || (!own_workspace && !workspace)) return MOE_E_NULL;
     if ((s = check_weights(cfg, w)) != MOE_OK) return s;
     if (!al16(x) || !al16(y)) return MOE_E_ALIGN;
-    const bool shared = cfg->shared_inter > 0;
-    const bool sfp8 = shared && (cfg->flags & MOE_SHARED_FP8);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
-    const Layout L = layout_of(cfg, T);
-    if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
+    if (!own_workspace) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MOE_E_ALIGN;
+        if (workspace_bytes < layout_of(cfg, T).total) return MOE_E_WORKSPACE;
+    }
     if (x == y) return MOE_E_UNSUPPORTED;
     if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int32_t T,
+                       void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status s = forward_checks(cfg, w, x, T, y, workspace, workspace_bytes, false);
+    if (s != MOE_OK || T == 0) return s;
+    const bool shared = cfg->shared_inter > 0;
+    const bool sfp8 = shared && (cfg->flags & MOE_SHARED_FP8);
+    const Layout L = layout_of(cfg, T);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int H = cfg->hidden, E = cfg->n_experts, K = cfg->top_k;

@@ -180,6 +180,31 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* Size of the device array moe_forward_noalloc uses as its workspace. */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, arithmetic and results as moe_forward, minus
+ * the workspace: the library's own device array of
+ * MOE_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU serves instead, held from the
+ * library's load until the process ends. The call allocates nothing and
+ * calls no allocating routine.
+ * Refused with MOE_E_WORKSPACE (nothing enqueued) when
+ * moe_workspace_bytes(cfg, T) exceeds that size (with H 2048, 256 experts
+ * top-8 and I = Is = 512: beyond 639 rows); every other check and status is
+ * moe_forward's.
+ * The array starts zero-filled; a call whose config differs from the
+ * previous call's on the same GPU first clears it with a kernel on `stream`.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU race (whatever their
+ * streams), so order them, e.g. on one stream. The decode path's error word
+ * lives in the array and cannot be read by the caller.
+ */
+moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                               int32_t T, void *y, void *stream);
+
 /*
  * A stack of n_layers layers of one shape, run on the same rows in sequence
  * in ONE launch (the per-frame backbone: PR #925 backbone commit summaries;

@@ -295,3 +295,22 @@ def test_flag_values_match_the_header():
     body = re.search(r"typedef struct \{(.*?)\} moe_weights;", src, re.S).group(1)
     names = re.findall(r"\*\s*(\w+);", body)
     assert names == [n for n, _ in moe.Weights._fields_]
+
+
+def test_noalloc_refusals_without_a_device():
+    """moe_forward_noalloc refuses, before touching any device, a call whose
+    workspace would not fit its 32 MiB array, and otherwise reports what
+    moe_forward reports (here: no gfx950 device)."""
+    L = moe.lib()
+    c = _cfg()
+    w = _fake_weights()
+    X, Y = 0x20000000, 0x30000000
+    assert moe.workspace_bytes(c, 600) <= moe.NOALLOC_WORKSPACE_BYTES
+    assert moe.workspace_bytes(c, 1024) > moe.NOALLOC_WORKSPACE_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X, 1024, Y, None) == -4
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X, 0, Y, None) == 0
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X, -1, Y, None) == -2
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), None, 1, Y, None) == -1
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X + 8, 1, Y, None) == -3
+    assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X, 1, Y, None) == -5
+    assert L.moe_forward_noalloc(None, ctypes.byref(w), X, 1, Y, None) == -1
