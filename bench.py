@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import sys
 import time
@@ -118,8 +119,10 @@ def copy_calibration(nbytes=256 << 20, reps=10):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
-def graph_time(step_fn, n_steps, warmup, stream):
-    """Capture n_steps calls in one graph; returns seconds for one replay."""
+def graph_time(step_fn, n_steps, warmup, stream, replays=5):
+    """Capture n_steps calls in one graph, replay it `replays` times (each
+    replay timed by HIP events on the stream); returns (median seconds per
+    replay, the graph, every replay's seconds)."""
     torch.cuda.synchronize()  # inputs were prepared on the default stream
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -131,38 +134,95 @@ def graph_time(step_fn, n_steps, warmup, stream):
             step_fn(i)
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
+    times = []
+    for _ in range(replays):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
         torch.cuda.synchronize()
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3, g
+        times.append(start.elapsed_time(end) / 1e3)
+    return statistics.median(times), g, times
 
 
-def cpu_baseline(shape, host_layer, target_s=10.0):
-    """The oracle, as it stands, on batches of 256 decode rows until about
-    target_s seconds of wall time have passed."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, host_layers, reps=5):
+    """The oracle, as it stands, timed on the host cores: the decode row
+    (config 1, also the 40-layer stack's per-layer step), and rows of the
+    uniform and skewed 1024-row chunks (configs 2 and 3), at every thread
+    the oracle gets by default and at one thread. Each figure is the median
+    of `reps` timed calls on a bounded sample of rows (the oracle's time is
+    linear in rows: every (row, slot) pair and every row is computed on its
+    own), scaled to the config's unit."""
     import oracle
-    batch = 256
-    x = inputs.make_x(shape, batch, seed=99)
-    oracle.forward(shape, host_layer, x[:1])  # warm
-    rows, took = 0, 0.0
-    while took < target_s:
-        t0 = time.perf_counter()
-        oracle.forward(shape, host_layer, x)
-        took += time.perf_counter() - t0
-        rows += batch
-    per_row = took / rows
+    nproc = oracle.num_threads()
+    layer = host_layers[0]
+    x_dec = inputs.make_x(shape, 256, seed=99)
+    x_chunk = inputs.make_x(shape, 1024, seed=1)
+    import dataclasses
+    skewed = dataclasses.replace(layer, router_bias=inputs.skew_bias(shape.n_experts))
+    oracle.forward(shape, layer, x_dec[:1])  # warm
+
+    def med_per_row(lw, x, rows):
+        per = []
+        for r in range(reps):
+            xs = x[(r * rows) % x.shape[0]:][:rows]
+            t0 = time.perf_counter()
+            oracle.forward(shape, lw, xs)
+            per.append((time.perf_counter() - t0) / xs.shape[0])
+        return statistics.median(per)
+
+    figures = {}
+    for threads in (nproc, 1):
+        oracle.set_num_threads(threads)
+        rows = 256 if threads > 1 else 8
+        dec = med_per_row(layer, x_dec, rows)
+        uni = med_per_row(layer, x_chunk, rows)
+        skw = med_per_row(skewed, x_chunk, rows)
+        # one row per call, layer after layer: the stack's per-layer step
+        # (the renormalisation between layers costs microseconds)
+        per = []
+        for r in range(reps):
+            t0 = time.perf_counter()
+            oracle.forward(shape, host_layers[r % len(host_layers)], x_dec[r:r + 1])
+            per.append(time.perf_counter() - t0)
+        one = statistics.median(per)
+        figures[f"threads{threads}"] = {
+            "decode_1row_us_per_row_batched": round(dec * 1e6, 1),
+            "decode_1row_tbs_batched": round(decode_bytes(shape) / dec / 1e12, 6),
+            "stack40_decode_us_per_layer": round(one * 1e6, 1),
+            "chunk1024_uniform_ms_per_chunk": round(uni * 1024 * 1e3, 1),
+            "chunk1024_skewed_ms_per_chunk": round(skw * 1024 * 1e3, 1),
+            "chunk1024_uniform_fp8_tflops": round(fp8_flops(shape, 1024) / (uni * 1024) / 1e12,
+                                                  6),
+            "rows_per_sample": rows,
+        }
+    oracle.set_num_threads(nproc)
+    head = figures[f"threads{nproc}"]
     return {
-        "value": decode_bytes(shape) / per_row / 1e12,
+        "value": head["decode_1row_tbs_batched"],
         "unit": "TB/s",
-        "us_per_layer": per_row * 1e6,
-        "cores": oracle.num_threads(),
+        "us_per_layer": head["decode_1row_us_per_row_batched"],
+        "cores": nproc,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"{rows} rows of the decode layer in oracle calls of {batch} rows "
-                  f"({took:.1f} s wall); per-row time taken as the layer time",
+        "sample": f"median of {reps} oracle calls per figure: {figures[f'threads{nproc}']['rows_per_sample']}"
+                  f" rows per call at {nproc} threads, 8 at 1 thread (decode rows; rows of "
+                  "the uniform and skewed 1024-row chunks, scaled to 1024 rows); the stack "
+                  "figure is one-row calls on successive layers; value = the decode layer's "
+                  "bytes over the per-row time of batched decode rows",
+        "figures": figures,
     }
 
 
@@ -227,12 +287,15 @@ def main():
     }
     if not args.no_decode:
         print(f"[bench] decode: {args.steps} steps", file=sys.stderr, flush=True)
-        secs, _ = graph_time(step, args.steps, args.warmup, stream)
+        secs, _, reps = graph_time(step, args.steps, args.warmup, stream)
         us = secs / args.steps * 1e6
         gbs = nbytes / (us * 1e-6) / 1e9
         rec["value"] = round(gbs / 1e3, 4)
         rec["ms_per_step"] = secs / args.steps * 1e3
         rec["us_per_layer"] = round(us, 3)
+        rec["decode_replays_us_per_layer"] = [round(t / args.steps * 1e6, 3) for t in reps]
+        rec["decode_timing"] = (f"median of {len(reps)} replays of one graph of {args.steps} "
+                                "layer calls on 40 rotated layers")
         # the decode layer is one kernel launch: time those launches live
         k_avg, k_min = kernel_time_live(step, args.live_launches, stream)
         kgbs = nbytes / k_avg / 1e9
@@ -258,7 +321,7 @@ def main():
 
         n1 = max(L, args.steps // 8)
         print(f"[bench] one row, grouped kernels: {n1} steps", file=sys.stderr, flush=True)
-        g1secs, _ = graph_time(gstep1, n1, L, stream)
+        g1secs, _, _ = graph_time(gstep1, n1, L, stream)
         rec["row1_grouped_invariant"] = {"us_per_layer": round(g1secs / n1 * 1e6, 3),
                                          "note": "one row on the grouped kernels "
                                                  "(chunk-invariant bytes)"}
@@ -290,7 +353,7 @@ def main():
                 moe.forward(cfg, lw, xc, y=yc, workspace=ws, wstruct=wsr, stream=stream)
 
             print(f"[bench] {name}: {args.chunk_steps} steps", file=sys.stderr, flush=True)
-            csecs, _ = graph_time(cstep, args.chunk_steps, 2, stream)
+            csecs, _, _ = graph_time(cstep, args.chunk_steps, 2, stream)
             cus = csecs / args.chunk_steps * 1e6
             fl = fp8_flops(shape, 1024)
             cb = decode_bytes(shape, rows=1024, experts_touched=touched)
@@ -314,7 +377,7 @@ def main():
                 moe.forward(cfg_nq, lw, xc, y=yc, workspace=ws_nq, wstruct=wsr, stream=stream)
 
             print(f"[bench] control: {args.chunk_steps} steps", file=sys.stderr, flush=True)
-            nsecs, _ = graph_time(nstep, args.chunk_steps, 2, stream)
+            nsecs, _, _ = graph_time(nstep, args.chunk_steps, 2, stream)
             chunk["chunk1024_uniform_no_act_quant"] = {
                 "us_per_chunk": round(nsecs / args.chunk_steps * 1e6, 2),
                 "note": "fidelity control: bf16 activations, decoded e4m3 weights"}
@@ -333,7 +396,7 @@ def main():
                 moe.forward(cfg_sf, lw, xc, y=yc, workspace=ws_sf, wstruct=wsr, stream=stream)
 
             print(f"[bench] shared fp8: {args.chunk_steps} steps", file=sys.stderr, flush=True)
-            fsecs, _ = graph_time(fstep, args.chunk_steps, 2, stream)
+            fsecs, _, _ = graph_time(fstep, args.chunk_steps, 2, stream)
             chunk["chunk1024_uniform_shared_fp8"] = {
                 "us_per_chunk": round(fsecs / args.chunk_steps * 1e6, 2),
                 "note": "variant: block-FP8 shared expert run as a grouped expert"}
@@ -353,7 +416,7 @@ def main():
 
         print(f"[bench] stack of {L} layers: {args.stack_passes} passes", file=sys.stderr,
               flush=True)
-        ssecs, _ = graph_time(spass, args.stack_passes, 2, stream)
+        ssecs, _, _ = graph_time(spass, args.stack_passes, 2, stream)
         sus = ssecs / args.stack_passes * 1e6
         rec["stack"] = {"workload": f"stack{L}_decode", "layers": L,
                         "us_per_pass": round(sus, 2), "us_per_layer": round(sus / L, 3),
@@ -384,7 +447,7 @@ def main():
                                       scales=so, stream=stream)
 
             n = 800 if rows == 1 else 200
-            asecs, _ = graph_time(astep, n, 8, stream)
+            asecs, _, _ = graph_time(astep, n, 8, stream)
             aus = asecs / n * 1e6
             abytes = rows * (4 * H + 4 * H + H + (H // 128) * 4) + 2 * H
             an[f"rows{rows}"] = {"us": round(aus, 3), "bytes": abytes,
@@ -408,7 +471,7 @@ def main():
                 moe.bf16_gemv(Ws[i % len(Ws)], xg, y=yg, stream=stream)
 
             n = 4 * ncopy
-            gsecs, _ = graph_time(gstep, n, ncopy, stream)
+            gsecs, _, _ = graph_time(gstep, n, ncopy, stream)
             gus = gsecs / n * 1e6
             gbytes = N * K * 2 + K * 2 + N * 2
             tbs = gbytes / (gus * 1e-6) / 1e12
@@ -419,7 +482,7 @@ def main():
         rec["bf16_gemv"] = gv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(shape, layers[0].to("cpu"))
+        rec["cpu_baseline"] = cpu_baseline(shape, [layers[l].to("cpu") for l in range(min(5, L))])
     rec["source_hash"] = source_hash()
     print(json.dumps(rec), flush=True)
 

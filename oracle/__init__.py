@@ -78,6 +78,8 @@ def lib():
         L.oracle_add_rmsnorm_quant.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp, vp,
                                                vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -235,6 +237,12 @@ def forward(shape, weights, x, flags: int = 0, shared: Optional[bool] = None):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Worker threads of later oracle calls (timing only; results do not
+    depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def bf16_bits_to_f32(bits) -> np.ndarray:

@@ -442,3 +442,11 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

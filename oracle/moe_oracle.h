@@ -102,6 +102,8 @@ void oracle_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const uint16_t *x
 
 /* Threads the OpenMP runtime will use (for the baseline record). */
 int oracle_num_threads(void);
+/* sets the worker threads of later calls (n >= 1); no effect without OpenMP */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
