@@ -25,7 +25,7 @@ FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
            "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant",
-           "moe_bf16_gemv", "moe_forward_noalloc")
+           "moe_bf16_gemv", "moe_forward_noalloc", "moe_decode_status")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward_noalloc.argtypes = [vp, vp, vp, i32, vp, vp]
         L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_decode_status.argtypes = [vp, vp, i32, vp]
+        L.moe_decode_status.restype = ctypes.c_int
         L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_rms_renorm.restype = ctypes.c_int
         L.moe_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
@@ -227,6 +229,21 @@ def weights_struct(lw) -> Weights:
     """Weights struct from an object with the tensor attributes of
     inputs.LayerWeights (all on the device)."""
     return Weights(**{k: _ptr(getattr(lw, k, None)) for k, _ in Weights._fields_})
+
+
+def decode_status(workspace, clear: bool = False, stream=None) -> int:
+    """The decode path's spin-out word of `workspace` (0: every bounded wait
+    was met), read on `stream` after the work enqueued there; with clear,
+    also zeroes it."""
+    import torch
+    out = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    _check("moe_decode_status", lib().moe_decode_status(_ptr(workspace), _ptr(out),
+                                                         int(bool(clear)), _stream(stream)))
+    if stream is not None:
+        stream.synchronize()
+    else:
+        torch.cuda.synchronize(workspace.device)
+    return int(out.item())
 
 
 NOALLOC_WORKSPACE_BYTES = 32 << 20  # MOE_NOALLOC_WORKSPACE_BYTES

@@ -203,6 +203,18 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
     return MOE_OK;
 }
 
+moe_status moe_decode_status(void *workspace, uint32_t *status, int32_t clear, void *stream) {
+    if (!workspace || !status) return MOE_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+        (reinterpret_cast<uintptr_t>(status) & 3u))
+        return MOE_E_ALIGN;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    // the sync region opens every layout, at offset 0
+    MOE_TRY(launch_decode_status(static_cast<uint32_t *>(workspace), status, clear != 0,
+                                 static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 moe_status moe_rms_renorm(const void *y, int32_t T, int32_t H, float eps, void *x,
                           void *stream) {
     if (T < 0 || T > MAX_ROWS || H < 128 || H > 8192 || H % 128) return MOE_E_SHAPE;

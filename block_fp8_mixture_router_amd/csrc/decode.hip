@@ -49,7 +49,8 @@
 // workspace started out filled with one repeated byte. Epochs are odd, below
 // 2^30 and differ from the counter they come from, so neither such a fill nor
 // words left by an earlier call can satisfy a wait. Waits are bounded: after
-// SPIN_LIMIT unsuccessful poll rounds (workgroups not all resident) the
+// SPIN_LIMIT = 2^17 unsuccessful poll rounds (about 0.1-0.3 s: a round is
+// one device-coherent load round trip; workgroups not all resident) the
 // spin-out word is set and the kernel still finishes.
 #include "common.h"
 #include "kernels.h"
@@ -58,7 +59,7 @@
 namespace moe {
 
 constexpr int REPL = DECODE_REPLICAS;   // copies of every cross-workgroup value
-constexpr uint32_t SPIN_LIMIT = 1u << 17;  // poll rounds before giving up (0.1-0.3 s)
+constexpr uint32_t SPIN_LIMIT = 1u << 17;  // poll rounds before giving up (about 0.1-0.3 s)
 constexpr int ERR_WORD = SYNC_ERR_WORD;
 constexpr int MB = 8;  // output rows per phase-C unit
 
@@ -1141,17 +1142,30 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
 // of a down row held in registers (I / 128 up to 4; more are loaded in the
 // loop); TPW: MFMA tiles (slot pairs) per wave (K up to 8: one, up to 16:
 // two)
+// Every workgroup waits for values other workgroups produce, so all of the
+// grid (one workgroup per CU) must be resident at once: the launch is
+// refused unless one workgroup with the largest LDS plan the decode path
+// takes fits on a CU (checked once per kernel variant).
+template <int NQ, int KBR, int TPW, bool RN>
+static hipError_t launch_v(const FusedArgs &a, size_t lds, hipStream_t st) {
+    static const hipError_t fits = [] {
+        int n = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN>), 256,
+            150 * 1024);
+        return e != hipSuccess ? e : n >= 1 ? hipSuccess : hipErrorInvalidConfiguration;
+    }();
+    if (fits != hipSuccess) return fits;
+    hipLaunchKernelGGL((decode_fused_kernel<NQ, KBR, TPW, RN>), dim3(a.nwg), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
 template <int NQ, int TPW, bool RN>
 static hipError_t launch_t(const FusedArgs &a, size_t lds, hipStream_t st) {
-    const dim3 grid(a.nwg), block(256);
     const int ib = a.I / GROUP;
-#define MOE_DECODE(KBRV) \
-    hipLaunchKernelGGL((decode_fused_kernel<NQ, KBRV, TPW, RN>), grid, block, lds, st, a)
-    if (ib <= 1) MOE_DECODE(1);
-    else if (ib <= 2) MOE_DECODE(2);
-    else MOE_DECODE(4);
-#undef MOE_DECODE
-    return hipGetLastError();
+    if (ib <= 1) return launch_v<NQ, 1, TPW, RN>(a, lds, st);
+    if (ib <= 2) return launch_v<NQ, 2, TPW, RN>(a, lds, st);
+    return launch_v<NQ, 4, TPW, RN>(a, lds, st);
 }
 
 template <int NQ, bool RN>
@@ -1175,6 +1189,17 @@ static void set_lds_limits() {
     set_lds_limit<NQ, 1, 2, RN>();
     set_lds_limit<NQ, 2, 2, RN>();
     set_lds_limit<NQ, 4, 2, RN>();
+}
+
+// copies the spin-out word to *out and, with clear, zeroes it (one thread)
+__global__ void decode_status_kernel(uint32_t *sync, uint32_t *out, int clear) {
+    out[0] = ld_dev(sync + ERR_WORD);
+    if (clear) st_dev(sync + ERR_WORD, 0u);
+}
+
+hipError_t launch_decode_status(uint32_t *sync, uint32_t *out, int clear, hipStream_t st) {
+    hipLaunchKernelGGL(decode_status_kernel, dim3(1), dim3(1), 0, st, sync, out, clear);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {

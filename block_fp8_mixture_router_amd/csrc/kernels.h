@@ -79,6 +79,8 @@ constexpr int SYNC_WORDS = SYNC_FLAGS + 1024;  // up to 1024 workgroups
 constexpr int SYNC_ERR_WORD = 32;              // the spin-out word
 bool decode_fits(int T, int H, int K, int I, int Is);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
+// the decode path's spin-out word (workspace sync word SYNC_ERR_WORD) -> out
+hipError_t launch_decode_status(uint32_t *sync, uint32_t *out, int clear, hipStream_t st);
 
 // ---- grouped.hip (expert-grouped MFMA path)
 struct GroupedArgs {

@@ -171,14 +171,32 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
  * no clearing. The decode path (T <= 4 by default) keeps per-workgroup call
  * counters and epoch-tagged handoff words in it between calls, so two calls
  * that overlap in time must not share a workspace; calls ordered on one
- * stream may. If the decode kernel's workgroups cannot all be resident at
- * once within about 0.1 s, its bounded waits give up, the output is
- * undefined, and the 32-bit word at byte offset 128 of the workspace is set
- * to nonzero (it is never cleared by the library).
+ * stream may. The decode kernel runs one workgroup per CU and every
+ * workgroup waits for values the others produce, so all of them must be
+ * resident at once: the launch is refused (MOE_E_LAUNCH) on a device where
+ * one of its workgroups does not fit on a CU, and concurrent work that holds
+ * CUs (another decode call included) can keep some from starting. Its waits
+ * are bounded: after 2^17 poll rounds (about 0.1-0.3 s) a waiting
+ * workgroup gives up, the output is undefined, and the workspace's spin-out
+ * word is set; moe_decode_status reads (and clears) it. moe_forward still
+ * returns MOE_OK, since the outcome is known only on the device.
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * The decode path's spin-out word: copies it from `workspace` (as passed to
+ * moe_forward, moe_forward_stack) into status[0] on `stream`, after the work
+ * already enqueued there, and zeroes it if `clear` is nonzero. 0 means every
+ * bounded wait of every decode launch since the last clear was met; nonzero
+ * means one gave up and those launches' outputs are undefined. status: a
+ * device uint32, 4-byte aligned. The residency rule this watches is part of
+ * the pages' persistent-kernel design for the one-row chain (PR #927 "drama:
+ * the backbone chain launches with programmatic dependent launch", "What this
+ * changes"); the call itself has no counterpart on the pages.
+ */
+moe_status moe_decode_status(void *workspace, uint32_t *status, int32_t clear, void *stream);
 
 /* Size of the device array moe_forward_noalloc uses as its workspace. */
 #define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)

@@ -314,3 +314,15 @@ def test_noalloc_refusals_without_a_device():
     assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X + 8, 1, Y, None) == -3
     assert L.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), X, 1, Y, None) == -5
     assert L.moe_forward_noalloc(None, ctypes.byref(w), X, 1, Y, None) == -1
+
+
+def test_decode_status_refusals_without_a_device():
+    """moe_decode_status checks its pointers on the host; a valid call needs a
+    gfx950 device."""
+    L = moe.lib()
+    WS, OUT = 0x40000000, 0x50000000
+    assert L.moe_decode_status(None, OUT, 0, None) == -1
+    assert L.moe_decode_status(WS, None, 0, None) == -1
+    assert L.moe_decode_status(WS + 16, OUT, 0, None) == -3
+    assert L.moe_decode_status(WS, OUT + 2, 1, None) == -3
+    assert L.moe_decode_status(WS, OUT, 1, None) == -5

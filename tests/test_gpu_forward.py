@@ -82,12 +82,12 @@ def test_forward_deterministic_and_poison_proof():
         y1 = run_forward(shape, dev, x, flags)
         ws = moe.alloc_workspace(moe.config(shape, flags), T)
         ws.fill_(0xFF)
-        ws[128:132].zero_()  # the decode kernel's handoff error word (set on a spin-out)
+        moe.decode_status(ws, clear=True)  # zero the decode kernel's spin-out word
         y2 = run_forward(shape, dev, x, flags, workspace=ws)
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
         y3 = run_forward(shape, dev, x, flags, workspace=ws)
         assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
-        assert int(ws[128:132].view(torch.int32).item()) == 0
+        assert moe.decode_status(ws) == 0
 
 
 def test_workspace_fills_and_path_mixing():
@@ -102,11 +102,11 @@ def test_workspace_fills_and_path_mixing():
         say(f"workspace fill {fill:#04x}")
         ws = moe.alloc_workspace(cfg, 300)
         ws.fill_(fill)
-        ws[128:132].zero_()  # the decode kernel's spin-out word
+        moe.decode_status(ws, clear=True)  # zero the decode kernel's spin-out word
         for xx, ref in ((x1, ref1), (x3, ref3), (x1, ref1), (x1, ref1), (x3, ref3), (x1, ref1)):
             y = run_forward(shape, dev, xx, workspace=ws)
             assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
-        assert int(ws[128:132].view(torch.int32).item()) == 0
+        assert moe.decode_status(ws) == 0
 
 
 def test_grouped_rows_independent_of_order():
@@ -229,4 +229,23 @@ def test_workspace_regions_do_not_move_with_rows():
             want = run_forward(shape, dev, x, flags)
             got = run_forward(shape, dev, x, flags, workspace=ws)
             assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (seq, i)
-        assert int(ws[128:132].view(torch.int32).item()) == 0
+        assert moe.decode_status(ws) == 0
+
+
+def test_decode_status_reads_and_clears():
+    """moe_decode_status returns the spin-out word as it stands and zeroes it
+    on request (the word is set here from the host, as a spin-out would)."""
+    shape, dev, host = layer("DECODE", 0, False)
+    cfg = moe.config(shape)
+    ws = moe.alloc_workspace(cfg, 1)
+    ws.zero_()
+    x, _ = x_rows(shape, 1, seed=31)
+    run_forward(shape, dev, x, workspace=ws)
+    assert moe.decode_status(ws) == 0
+    ws[128:132].view(torch.int32).fill_(7)
+    assert moe.decode_status(ws) == 7
+    assert moe.decode_status(ws, clear=True) == 7
+    assert moe.decode_status(ws) == 0
+    y = run_forward(shape, dev, x, workspace=ws)
+    assert torch.equal(y.view(torch.int16), run_forward(shape, dev, x).view(torch.int16))
+    assert moe.decode_status(ws) == 0
