@@ -25,7 +25,7 @@ FORCE_GROUPED = 1 << 9
 
 EXPORTS = ("moe_supported", "moe_workspace_bytes", "moe_route", "moe_quant_act",
            "moe_forward", "moe_rms_renorm", "moe_forward_stack", "moe_add_rmsnorm_quant",
-           "moe_bf16_gemv", "moe_forward_noalloc", "moe_decode_status")
+           "moe_bf16_gemv", "moe_forward_noalloc", "moe_decode_status", "moe_e4m3_encode")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,8 @@ def lib():
         L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_decode_status.argtypes = [vp, vp, i32, vp]
         L.moe_decode_status.restype = ctypes.c_int
+        L.moe_e4m3_encode.argtypes = [vp, ctypes.c_int64, vp, vp]
+        L.moe_e4m3_encode.restype = ctypes.c_int
         L.moe_rms_renorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_rms_renorm.restype = ctypes.c_int
         L.moe_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
@@ -229,6 +231,16 @@ def weights_struct(lw) -> Weights:
     """Weights struct from an object with the tensor attributes of
     inputs.LayerWeights (all on the device)."""
     return Weights(**{k: _ptr(getattr(lw, k, None)) for k, _ in Weights._fields_})
+
+
+def e4m3_encode(x, q=None, stream=None):
+    """The kernels' fp32 -> e4m3 conversion of fp32 tensor x (any shape):
+    uint8 codes of the same shape."""
+    import torch
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check("moe_e4m3_encode", lib().moe_e4m3_encode(_ptr(x), x.numel(), _ptr(q), _stream(stream)))
+    return q
 
 
 def decode_status(workspace, clear: bool = False, stream=None) -> int:

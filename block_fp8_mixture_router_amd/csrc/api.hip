@@ -203,6 +203,17 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
     return MOE_OK;
 }
 
+moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream) {
+    if (n < 0 || n > ((int64_t)1 << 40)) return MOE_E_SHAPE;
+    if (n == 0) return MOE_OK;
+    if (!x || !q) return MOE_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(q) & 3u))
+        return MOE_E_ALIGN;
+    if (!current_device_ok()) return MOE_E_UNSUPPORTED;
+    MOE_TRY(launch_e4m3_encode(x, n, q, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 moe_status moe_decode_status(void *workspace, uint32_t *status, int32_t clear, void *stream) {
     if (!workspace || !status) return MOE_E_NULL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) ||

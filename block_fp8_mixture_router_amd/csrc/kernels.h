@@ -11,6 +11,8 @@ namespace moe {
 constexpr uint32_t K_LOGITS_FP32 = 1u << 1;
 
 // ---- quant.hip
+// the kernels' fp32 -> e4m3 conversion on n values (x 16-byte aligned)
+hipError_t launch_e4m3_encode(const float *x, int64_t n, uint8_t *q, hipStream_t st);
 hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, float *s,
                             hipStream_t st);
 

@@ -34,6 +34,29 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t *__restri
     if (sub == 0) s[g] = sc;
 }
 
+// The fp32 -> e4m3 conversion every kernel uses (e4m3x4: saturate to +-448,
+// round to nearest even), applied to n values: four per thread, grid-stride.
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float *__restrict__ x, int64_t n,
+                                                          uint8_t *__restrict__ q) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + i);
+            *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x, v.y, v.z, v.w);
+        } else {
+            for (int64_t k = i; k < n; ++k) q[k] = (uint8_t)(e4m3x4(x[k], 0.f, 0.f, 0.f) & 0xFFu);
+        }
+    }
+}
+
+hipError_t launch_e4m3_encode(const float *x, int64_t n, uint8_t *q, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t quads = (n + 3) / 4;
+    const int64_t blocks = (quads + 255) / 256 < 8192 ? (quads + 255) / 256 : 8192;
+    hipLaunchKernelGGL(e4m3_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, q);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const uint16_t *x, int64_t n_groups, uint8_t *q, float *s,
                             hipStream_t st) {
     if (n_groups <= 0) return hipSuccess;

@@ -143,6 +143,17 @@ moe_status moe_quant_act(const void *x, int32_t T, int32_t C, uint8_t *q, float 
                          void *stream);
 
 /*
+ * The fp32 -> e4m3 conversion every kernel of the library uses (the codes of
+ * moe_quant_act, the re-quantised h): saturate to +-448, then round to the
+ * nearest e4m3 value, ties to even; a negative value that rounds to 0 gives
+ * 0x80 (PR #939, "How it fits the engine" > Precision: e4m3 with amax/448
+ * scales). NaN input is outside the contract. Exposed so that the conversion
+ * can be checked on every fp32 value.
+ * x: fp32 [n], 16-byte aligned; q: uint8 [n], 4-byte aligned; 0 <= n <= 2^40.
+ */
+moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
+
+/*
  * The whole layer, without the residual (PR #925 commit summaries: the
  * router, the FP8 experts on FP8 rows with per-row scales, one SwiGLU launch
  * writing routed rows as FP8 and shared rows as bf16, and the combine that

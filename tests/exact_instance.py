@@ -118,9 +118,16 @@ def _columns(H: int, E: int):
     return route, np.array(data)
 
 
-def build(shape: inputs.LayerShape, T: int, seed: int = 0, rows=None) -> ExactInstance:
+def build(shape: inputs.LayerShape, T: int, seed: int = 0, rows=None,
+          act_scales: bool = False) -> ExactInstance:
     """An exact instance with T rows. The expected output is computed for
-    `rows` only (all rows when None); the other rows of y_bits/acc are 0."""
+    `rows` only (all rows when None); the other rows of y_bits/acc are 0.
+
+    With act_scales, group g's 448 column holds 448 * 2^a_g (a_g in 0..2, per
+    group), so x's activation scales are 1, 2 and 4 across the groups and the
+    codes are x / 2^a_g (still exact in e4m3); the gate blocks' scales carry
+    2^-a_g, so the marker rows stay as above. A kernel that takes a group's
+    activation scale from the wrong group then changes bits."""
     H, E, K, I, Is = shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter
     G, NB = H // GROUP, I // GROUP
     assert G & (G - 1) == 0, "the marker construction needs a power-of-two group count"
@@ -131,10 +138,16 @@ def build(shape: inputs.LayerShape, T: int, seed: int = 0, rows=None) -> ExactIn
 
     # ---- x and the routing it encodes
     picks = np.stack([np.sort(rng.choice(E, K, replace=False)) for _ in range(T)])
+    a_g = rng.integers(0, 3, size=G) if act_scales else np.zeros(G, dtype=np.int64)
     x = np.zeros((T, H))
-    x[:, bias_cols] = 448.0
+    x[:, bias_cols] = 448.0 * 2.0 ** a_g
     x[:, one_col] = 64.0
     x[:, data] = rng.integers(-4, 5, size=(T, data.size))
+    if act_scales:
+        # data values in group g are multiples of 2^a_g, so x / 2^a_g stays an
+        # integer and every sum keeps the granularity the bounds above assume
+        step = 2.0 ** a_g[data // GROUP]
+        x[:, data] = np.round(x[:, data] / step) * step
     for t in range(T):
         x[t, np.array(route)[picks[t]]] = 16.0
     assert _bf16_exact(x)
@@ -162,7 +175,7 @@ def build(shape: inputs.LayerShape, T: int, seed: int = 0, rows=None) -> ExactIn
         pattern = np.zeros(G, dtype=np.int64)
     r = rng.permuted(np.broadcast_to(pattern, (E, NB, G)).copy(), axis=2)
     p = p_hi - rng.integers(0, 2, size=(E, NB))
-    sg = 2.0 ** -(p[:, :, None] + r).astype(np.float64)
+    sg = 2.0 ** -(p[:, :, None] + r + a_g[None, None, :]).astype(np.float64)
     su = np.broadcast_to(2.0 ** -rng.integers(7, 9, size=(E, NB, 1)).astype(np.float64),
                          (E, NB, G)).copy()
     wu = np.zeros((E, I, H), dtype=np.int8)

@@ -326,3 +326,15 @@ def test_decode_status_refusals_without_a_device():
     assert L.moe_decode_status(WS + 16, OUT, 0, None) == -3
     assert L.moe_decode_status(WS, OUT + 2, 1, None) == -3
     assert L.moe_decode_status(WS, OUT, 1, None) == -5
+
+
+def test_e4m3_encode_refusals_without_a_device():
+    L = moe.lib()
+    X, Q = 0x20000000, 0x30000000
+    assert L.moe_e4m3_encode(X, 0, Q, None) == 0
+    assert L.moe_e4m3_encode(X, -1, Q, None) == -2
+    assert L.moe_e4m3_encode(None, 4, Q, None) == -1
+    assert L.moe_e4m3_encode(X, 4, None, None) == -1
+    assert L.moe_e4m3_encode(X + 4, 4, Q, None) == -3
+    assert L.moe_e4m3_encode(X, 4, Q + 1, None) == -3
+    assert L.moe_e4m3_encode(X, 4, Q, None) == -5

@@ -39,14 +39,17 @@ SHAPES = {
         np.random.default_rng(0).choice(np.arange(40, 1020), 40, replace=False)]))),
     "decode_noshared": (dataclasses.replace(inputs.DECODE, shared_inter=0, n_experts=64), 40,
                         None),
+    # activation scales 1, 2 and 4 across the groups (non-unit powers of two)
+    "decode_act": (inputs.DECODE, 300, None),
 }
+ACT_SCALES = {"decode_act"}
 
 
 @functools.lru_cache(maxsize=1)
 def _instance(name):
     shape, T, rows = SHAPES[name]
     say(f"building exact instance {name} ({T} rows)")
-    inst = xi.build(shape, T, seed=5, rows=rows)
+    inst = xi.build(shape, T, seed=5, rows=rows, act_scales=name in ACT_SCALES)
     sel = np.arange(T) if rows is None else rows
     return shape, inst, inst.weights.to("cuda"), inst.x.cuda(), sel
 
@@ -83,6 +86,13 @@ def test_exact_decode_shape(T, flags):
     """Up to the 1024-row chunk in the launch configuration the bench times
     (exact expectations for 84 of its rows)."""
     _check("decode", T, flags)
+
+
+@pytest.mark.parametrize("T,flags", [(1, 0), (4, 0), (1, moe.FORCE_GROUPED), (300, 0)])
+def test_exact_decode_shape_activation_scales(T, flags):
+    """Activation scales 1, 2 and 4 across the groups: every path takes each
+    group's own scale."""
+    _check("decode_act", T, flags)
 
 
 @pytest.mark.parametrize("T", [1, 40])

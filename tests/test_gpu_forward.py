@@ -31,6 +31,7 @@ def _check(shape, host, x_host, y_dev, rows=None, tol=OUT_TOL, flags=0, shared=T
     say(f"  relL2 {rel:.2e}  worst row {worst:.2e}")
     assert np.all(np.isfinite(exact.bits_to_f32(yb)))
     assert rel <= tol, (rel, worst)
+    assert worst <= tol, (rel, worst)  # every row on its own, not only the whole
     return rel, worst
 
 

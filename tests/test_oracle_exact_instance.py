@@ -42,3 +42,18 @@ def test_oracle_reproduces_exact_instance(oracle_lib, name, T):
         no_routed = dataclasses.replace(inst.weights, w_down=inst.weights.w_down * 0)
         _, acc_only_shared, _, _ = oracle_lib.forward(shape, no_routed, inst.x)
         assert np.mean(acc_only_shared != acc_sh) > 0.3
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 7), ("decode_E32", 3), ("tiny_I256_K2", 5)])
+def test_oracle_reproduces_exact_instance_with_activation_scales(oracle_lib, name, T):
+    """The same with activation scales of 1, 2 and 4 across the groups, so
+    each group's scale enters its own block products."""
+    shape = SHAPES[name]
+    inst = xi.build(shape, T, seed=13, act_scales=True)
+    g = shape.hidden // 128
+    amax = inst.x.float().numpy()[:, 127::128]
+    assert len(np.unique(amax)) > 1 or g == 1
+    y, acc, ids, w = oracle_lib.forward(shape, inst.weights, inst.x)
+    assert np.array_equal(ids, inst.ids)
+    assert np.array_equal(acc, inst.acc)
+    assert np.array_equal(xi.zero_sign_blind(y), xi.zero_sign_blind(inst.y_bits))
