@@ -66,8 +66,9 @@ typedef enum {
 #define MOE_NO_ACT_QUANT  (1u << 2) /* fidelity control: the routed experts take bf16 x and
                                        bf16 h times the decoded e4m3 weights (no activation
                                        quantisation); moe_forward only, grouped path at any T */
-#define MOE_FORCE_GEMV    (1u << 8) /* run the row-at-a-time decode path (T <= 16; refused
-                                       with MOE_E_UNSUPPORTED where its LDS plan does not fit) */
+#define MOE_FORCE_GEMV    (1u << 8) /* run the one-row decode kernel (T <= 4; refused with
+                                       MOE_E_UNSUPPORTED beyond, where its LDS plan does not
+                                       fit, or with a variant flag) */
 #define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
 
 typedef struct {
@@ -101,11 +102,16 @@ typedef struct {
 } moe_weights;
 
 /* 1 if `device` is a gfx950 GPU this library was built for; 0 otherwise and
- * on any runtime failure (never an error). */
+ * on any runtime failure, never an error (the capability convention of PR
+ * #925's commit summary on the device-global marker test: a failing driver
+ * call is a plain negative). */
 int moe_supported(int device);
 
 /* Bytes of device workspace moe_forward and moe_route need for up to
- * `max_rows` rows of this config; 0 if the config is refused. */
+ * `max_rows` rows of this config; 0 if the config is refused. The library
+ * allocates nothing (PR #925, commit summary of the allocation cap: device
+ * and pinned bytes are bounded by the caller's budget), so the caller sizes
+ * and owns this buffer. */
 size_t moe_workspace_bytes(const moe_config *cfg, int32_t max_rows);
 
 /*
@@ -202,10 +208,11 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
  * already enqueued there, and zeroes it if `clear` is nonzero. 0 means every
  * bounded wait of every decode launch since the last clear was met; nonzero
  * means one gave up and those launches' outputs are undefined. status: a
- * device uint32, 4-byte aligned. The residency rule this watches is part of
- * the pages' persistent-kernel design for the one-row chain (PR #927 "drama:
- * the backbone chain launches with programmatic dependent launch", "What this
- * changes"); the call itself has no counterpart on the pages.
+ * device uint32, 4-byte aligned. The call has no counterpart on the pages;
+ * it serves their rule that a failure is observable before success is
+ * reported (PR #939 "drama3: Fish Audio Drama 3 text to speech on one CUDA
+ * GPU", review thread: the finding on write failures and its fix), which a
+ * launch cannot honour from the host for a wait that gives up on the device.
  */
 moe_status moe_decode_status(void *workspace, uint32_t *status, int32_t clear, void *stream);
 
@@ -236,28 +243,25 @@ moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, cons
 
 /*
  * A stack of n_layers layers of one shape, run on the same rows in sequence
- * in ONE launch (the per-frame backbone: PR #925 backbone commit summaries;
- * each of its 40 layers holds this MoE block, and rows are RMS-normalised
- * before each). With x_0 = x:
+ * (the per-frame backbone: PR #925 backbone commit summaries; each of its
+ * layers holds this MoE block, and rows are RMS-normalised before each).
+ * With x_0 = x:
  *   y_l     = the layer of weights layers[l] applied to x_l (as moe_forward);
  *   x_{l+1} = moe_rms_renorm(y_l, eps).
+ * One decode launch per layer: every layer after the first renormalises its
+ * predecessor's output in its prologue, with moe_rms_renorm's arithmetic.
  * The result equals, bit for bit, moe_forward and moe_rms_renorm called in
- * turn (the decode path) with the same workspace.
- * layers: DEVICE array of n_layers moe_weights structs, 16-byte aligned; the
- *   pointers in it cannot be checked on the host and must satisfy every
- *   rule of moe_forward (shared expert present iff cfg->shared_inter > 0);
+ * turn with the same workspace.
+ * layers: HOST array of n_layers moe_weights structs, each checked as
+ *   moe_forward checks its weights (shared expert present iff
+ *   cfg->shared_inter > 0);
  * x: bf16 [T, H]; y: bf16 [T, H], the last layer's output (must not alias
- * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL;
- * T rows of the decode path only (MOE_E_UNSUPPORTED where its LDS plan does
- * not fit, e.g. beyond 16 rows); cfg->flags may not force a path or set
- * MOE_NO_ACT_QUANT or MOE_SHARED_FP8;
+ * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL (then the
+ * layers' outputs alternate between two rows of the workspace);
+ * T rows of the decode path only (MOE_E_UNSUPPORTED where it does not take
+ * them, beyond 4 rows on the decode-layer shape); cfg->flags may not force a
+ * path or set MOE_NO_ACT_QUANT or MOE_SHARED_FP8;
  * 0 <= n_layers <= 4096; 0 <= eps <= 1; workspace as for moe_forward.
- * STATUS: switched off. The arguments are checked as above (T = 0 or
- * n_layers = 0 still returns MOE_OK); every other valid call returns
- * MOE_E_UNSUPPORTED without touching the device, because the one-launch
- * kernel took a GPU memory fault on its first run and the cause has not
- * been found. Call moe_forward and moe_rms_renorm in turn instead (they can
- * be captured into one graph).
  */
 moe_status moe_forward_stack(const moe_config *cfg, const moe_weights *layers, int32_t n_layers,
                              const void *x, int32_t T, float eps, void *y, void *ys,
