@@ -44,12 +44,14 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0  # dense MFMA, no sparsity
 
 
-def decode_bytes(shape, rows=1, experts_touched=None) -> int:
+def decode_bytes(shape, rows=1, experts_touched=None, shared_fp8=False) -> int:
     """Algorithmic HBM bytes of one layer pass: every touched expert's codes
-    and scales once, shared expert, router, gate vector, x and y."""
+    and scales once, shared expert (bf16, or block-FP8 codes and scales),
+    router, gate vector, x and y."""
     k = shape.top_k * rows if experts_touched is None else experts_touched
     routed = k * shape.expert_bytes()
-    shared = 3 * shape.hidden * shape.shared_inter * 2
+    h, i_s = shape.hidden, shape.shared_inter
+    shared = (3 * h * i_s + 3 * (h // 128) * (i_s // 128) * 4) if shared_fp8 else 3 * h * i_s * 2
     router = shape.n_experts * shape.hidden * 2
     return routed + shared + router + shape.hidden * 2 + rows * shape.hidden * 2 * 2
 
@@ -325,6 +327,41 @@ def main():
         rec["row1_grouped_invariant"] = {"us_per_layer": round(g1secs / n1 * 1e6, 3),
                                          "note": "one row on the grouped kernels "
                                                  "(chunk-invariant bytes)"}
+        # the two switches on the one-row kernel: the block-FP8 shared expert
+        # (on as many rotated layers, its shared matrices block-FP8) and the
+        # no-activation-quantisation control
+        cfg_sf = moe.config(shape, moe.SHARED_FP8)
+        ws_sf = moe.alloc_workspace(cfg_sf, 1)
+        lsf = [inputs.make_layer(shape, seed=0, layer=l, device="cuda", shared_fp8=True)
+               for l in range(L)]
+        wsf = [moe.weights_struct(lw) for lw in lsf]
+        cfg_nq = moe.config(shape, moe.NO_ACT_QUANT)
+        ws_nq = moe.alloc_workspace(cfg_nq, 1)
+
+        def sfstep(i):
+            j = i % L
+            moe.forward(cfg_sf, lsf[j], xs[j:j + 1], y=ys[j:j + 1], workspace=ws_sf,
+                        wstruct=wsf[j], stream=stream)
+
+        def nqstep(i):
+            j = i % L
+            moe.forward(cfg_nq, layers[j], xs[j:j + 1], y=ys[j:j + 1], workspace=ws_nq,
+                        wstruct=wstructs[j], stream=stream)
+
+        n2 = max(L, args.steps // 4)
+        print(f"[bench] one row, switches: {n2} steps each", file=sys.stderr, flush=True)
+        sfsecs, _, _ = graph_time(sfstep, n2, L, stream)
+        sf_us = sfsecs / n2 * 1e6
+        sf_bytes = decode_bytes(shape, shared_fp8=True)
+        rec["decode_1row_shared_fp8"] = {
+            "us_per_layer": round(sf_us, 3), "bytes_per_layer": sf_bytes,
+            "tbs_algorithmic": round(sf_bytes / (sf_us * 1e-6) / 1e12, 4),
+            "note": "block-FP8 shared expert as slot K of the one-row kernel"}
+        nqsecs, _, _ = graph_time(nqstep, n2, L, stream)
+        rec["decode_1row_no_act_quant"] = {
+            "us_per_layer": round(nqsecs / n2 * 1e6, 3),
+            "note": "fidelity control on the one-row kernel (bf16 x and h, decoded e4m3 weights)"}
+        del lsf, wsf, ws_sf, ws_nq
     if not args.no_chunk:
         chunk = {}
         xc = inputs.make_x(shape, 1024, seed=1, device="cuda")

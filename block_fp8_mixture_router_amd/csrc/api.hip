@@ -87,8 +87,12 @@ constexpr int BOUNDED_MIN_ROWS = 16;
 
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-bool is_variant(const moe_config *c) {
-    return (c->flags & (MOE_SHARED_FP8 | MOE_NO_ACT_QUANT)) != 0;
+// what the one-row kernel computes for this config (the block-FP8 shared
+// switch means nothing without a shared expert)
+int decode_var(const moe_config *c) {
+    if ((c->flags & MOE_SHARED_FP8) && c->shared_inter > 0) return DV_SFP8;
+    if (c->flags & MOE_NO_ACT_QUANT) return DV_NOQ;
+    return DV_PLAIN;
 }
 
 // The most rows the one-row path can take for this config (0 if none): it
@@ -96,9 +100,9 @@ bool is_variant(const moe_config *c) {
 // the workspace moves with T (a grouped call's plain data can never sit
 // where a later decode call polls for tagged words).
 int decode_rows_max(const moe_config *c) {
-    if (is_variant(c)) return 0;
     for (int t = DECODE_MAX_ROWS; t >= 1; --t)
-        if (decode_fits(t, c->hidden, c->top_k, c->inter, c->shared_inter)) return t;
+        if (decode_fits(t, c->hidden, c->top_k, c->inter, c->shared_inter, decode_var(c)))
+            return t;
     return 0;
 }
 
@@ -129,10 +133,12 @@ Layout layout_of(const moe_config *c, int T) {
     // other size is non-decreasing in T, so a workspace sized for max_rows
     // serves every T <= max_rows.
     const size_t R = DECODE_REPLICAS, td = (size_t)decode_rows_max(c);
+    const int var = decode_var(c);
+    const size_t KS = td ? (size_t)decode_slots(var, (int)K, (int)I, (int)Is) : 0;
     L.dlogits = take(R * td * E * 8);
     L.dgamma = take(R * td * 8);
-    L.dhs = take(R * td * Is * 8);
-    L.dh = take(R * td * K * I * 8);
+    L.dhs = take(var == DV_SFP8 ? 0 : R * td * Is * 8);
+    L.dh = take(R * td * KS * I * 8);
     L.ybuf = take(2 * td * H * 2);  // a stack's layer outputs, alternating
     L.logits = take(t * E * 4);  // exact logits, or the bounded scores S
     L.absums = take(t * E * 4);  // the bounded scores' sums of |x||w|
@@ -332,6 +338,16 @@ void fill_decode_args(FusedArgs &a, const moe_config *cfg, const moe_weights *w,
     a.sh_up = static_cast<const uint16_t *>(w->sh_up);
     a.sh_down = static_cast<const uint16_t *>(w->sh_down);
     a.sh_gate_w = static_cast<const uint16_t *>(w->sh_gate_w);
+    a.var = decode_var(cfg);
+    a.KS = decode_slots(a.var, a.K, a.I, a.Is);
+    if (a.var == DV_SFP8) {
+        a.sh8_gate = static_cast<const uint8_t *>(w->sh_gate);
+        a.sh8_up = static_cast<const uint8_t *>(w->sh_up);
+        a.sh8_down = static_cast<const uint8_t *>(w->sh_down);
+        a.sh_s_gate = w->sh_s_gate;
+        a.sh_s_up = w->sh_s_up;
+        a.sh_s_down = w->sh_s_down;
+    }
     a.logits = at<uint64_t>(workspace, L.dlogits);
     a.gamma = at<uint64_t>(workspace, L.dgamma);
     a.hs = at<uint64_t>(workspace, L.dhs);
@@ -410,10 +426,9 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
     float *gamma = at<float>(workspace, L.gamma);
     const bool fits = T <= decode_rows_max(cfg);
     const bool noq = (cfg->flags & MOE_NO_ACT_QUANT) != 0;
-    const bool variant = is_variant(cfg);  // grouped kernels only
-    if ((cfg->flags & MOE_FORCE_GEMV) && (!fits || variant)) return MOE_E_UNSUPPORTED;
-    const bool gemv = (cfg->flags & MOE_FORCE_GEMV) ||
-                      (!(cfg->flags & MOE_FORCE_GROUPED) && !variant && fits);
+    if ((cfg->flags & MOE_FORCE_GEMV) && !fits) return MOE_E_UNSUPPORTED;
+    const bool gemv =
+        (cfg->flags & MOE_FORCE_GEMV) || (!(cfg->flags & MOE_FORCE_GROUPED) && fits);
     if (gemv) {
         FusedArgs a{};
         fill_decode_args(a, cfg, w, T, workspace, L);

@@ -57,6 +57,18 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float &a, float &b, fl
     d = hi.y;
 }
 
+// Eight e4m3 codes (a uint2) -> eight bf16 values (exact: every e4m3 value
+// is a bf16 value).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+    float f[8];
+    e4m3x4_to_f32(c.x, f[0], f[1], f[2], f[3]);
+    e4m3x4_to_f32(c.y, f[4], f[5], f[6], f[7]);
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(f[2 * k]) | (f32_to_bf16(f[2 * k + 1]) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Scale of one 128-wide group from its amax: fp32(max(amax, 1e-10) / 448),
 // with a correctly rounded division (the library is built with
 // -fhip-fp32-correctly-rounded-divide-sqrt).

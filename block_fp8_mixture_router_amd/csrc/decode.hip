@@ -527,42 +527,105 @@ struct GateUpRegs {
     float sw[GU_STEP];  // weight block scale of each lane's column and block
 };
 
+// Expert e's gate or up rows and their block scales; with the block-FP8
+// shared expert, e = E is that expert (its matrices have the routed ones'
+// shape, Is = I).
+template <int VAR>
+__device__ __forceinline__ void expert_gu(const FusedArgs &a, int e, bool up, const uint8_t *&w,
+                                          const float *&s) {
+    if (VAR == DV_SFP8 && e == a.E) {
+        w = up ? a.sh8_up : a.sh8_gate;
+        s = up ? a.sh_s_up : a.sh_s_gate;
+    } else {
+        w = (up ? a.w_up : a.w_gate) + (int64_t)e * a.I * a.H;
+        s = (up ? a.s_up : a.s_gate) + (int64_t)e * (a.I / GROUP) * (a.H / GROUP);
+    }
+}
+
+// The lane's bytes of one K block of its weight row: [32 kq, +32) for the
+// FP8 MFMA; with DV_NOQ the four bf16 chain steps' [32 i + 8 kq, +8), i < 4,
+// in that order.
+template <int VAR>
+__device__ __forceinline__ void load_block(const uint8_t *row, int kb, uint4 &w0, uint4 &w1) {
+    const int kq = (threadIdx.x & 63) >> 4;
+    if constexpr (VAR == DV_NOQ) {
+        const uint8_t *b = row + kb * GROUP + 8 * kq;
+        const uint2 c0 = *reinterpret_cast<const uint2 *>(b);
+        const uint2 c1 = *reinterpret_cast<const uint2 *>(b + 32);
+        const uint2 c2 = *reinterpret_cast<const uint2 *>(b + 64);
+        const uint2 c3 = *reinterpret_cast<const uint2 *>(b + 96);
+        w0 = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        w1 = make_uint4(c2.x, c2.y, c3.x, c3.y);
+    } else {
+        const uint8_t *b = row + kb * GROUP + 32 * kq;
+        w0 = ld16(b);
+        w1 = ld16(b + 16);
+    }
+}
+
+template <int VAR>
 __device__ __forceinline__ void gateup_load(const FusedArgs &a, int e, int n0, int j0,
                                             GateUpRegs &r) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
-    const int H = a.H, I = a.I, KB = H / GROUP, KH = (KB + 1) / 2;
+    const int lane = threadIdx.x & 63, l16 = lane & 15;
+    const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2;
     const int r8 = l16 & 7, hb = l16 >> 3;
-    const bool up = r8 >= 4;
-    const uint8_t *row = (up ? a.w_up : a.w_gate) + ((int64_t)e * I + n0 + (r8 & 3)) * H + 32 * kq;
-    const float *srow = (up ? a.s_up : a.s_gate) + ((int64_t)e * (I / GROUP) + n0 / GROUP) * KB;
+    const uint8_t *wb;
+    const float *sb;
+    expert_gu<VAR>(a, e, r8 >= 4, wb, sb);
+    const uint8_t *row = wb + (int64_t)(n0 + (r8 & 3)) * H;
+    const float *srow = sb + (int64_t)(n0 / GROUP) * KB;
     // branch-free: blocks past the end reload the last one (dropped later)
 #pragma unroll
     for (int u = 0; u < GU_STEP; ++u) {
         const int kb = min(hb * KH + j0 + u, KB - 1);
-        r.w[u][0] = ld16(row + kb * GROUP);
-        r.w[u][1] = ld16(row + kb * GROUP + 16);
+        load_block<VAR>(row, kb, r.w[u][0], r.w[u][1]);
         r.sw[u] = srow[kb];
+    }
+}
+
+// One K block kb of row t against the lane's weight row (its bytes w0, w1):
+// the block's product (element 0 of the lane's result) and the scale it is
+// folded with. FP8: one MFMA on the e4m3 groups of x, scale sx x s_w. DV_NOQ:
+// the control's four chained bf16 MFMAs from zero on bf16 x and the decoded
+// codes, scale s_w.
+template <int VAR>
+__device__ __forceinline__ float2 gu_block(int t, int kb, int H, uint4 w0, uint4 w1, float sw,
+                                           const uint8_t *qx, const float *sx,
+                                           const uint16_t *xs) {
+    const int kq = (threadIdx.x & 63) >> 4;
+    if constexpr (VAR == DV_NOQ) {
+        const uint16_t *xa = xs + t * H + kb * GROUP + 8 * kq;
+        const uint2 c[4] = {make_uint2(w0.x, w0.y), make_uint2(w0.z, w0.w),
+                            make_uint2(w1.x, w1.y), make_uint2(w1.z, w1.w)};
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d = mfma_bf16_k32(as_v8bf(ld16(xa + 32 * i)), as_v8bf(e4m3x8_to_bf16(c[i])), d);
+        return make_float2(sw, d[0]);
+    } else {
+        const uint8_t *qa = qx + t * H + kb * GROUP + 32 * kq;
+        const v4f d = mfma_fp8_k128(as_v8i(ld16(qa), ld16(qa + 16)), as_v8i(w0, w1));
+        return make_float2(sx[t * (H / GROUP) + kb] * sw, d[0]);
     }
 }
 
 // the MFMAs of one batch: lanes 0-7 fold their first-half blocks into acc,
 // lanes 40-47 keep (scale, product) of the second-half blocks in sp[j][c]
+template <int VAR>
 __device__ __forceinline__ void gateup_mfma(const FusedArgs &a, int t, int j0,
                                             const GateUpRegs &r, const uint8_t *qx,
-                                            const float *sx, float2 *sp, float &acc) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+                                            const float *sx, const uint16_t *xs, float2 *sp,
+                                            float &acc) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15;
     const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2, hb = l16 >> 3;
-    const uint8_t *qa = qx + t * H + 32 * kq;
 #pragma unroll
     for (int u = 0; u < GU_STEP; ++u) {
         const int j = j0 + u;
         if (j < KH) {  // wave-uniform
             const int kb = min(hb * KH + j, KB - 1);  // A row l16 and B column l16 share it
-            const v8i av = as_v8i(ld16(qa + kb * GROUP), ld16(qa + kb * GROUP + 16));
-            const v4f d = mfma_fp8_k128(av, as_v8i(r.w[u][0], r.w[u][1]));
-            const float sc = sx[t * KB + kb] * r.sw[u];
-            if (lane < 8) acc = fmaf(sc, d[0], acc);
-            else if (lane >= 40 && lane < 48 && KH + j < KB) sp[j * 8 + lane - 40] = make_float2(sc, d[0]);
+            const float2 v = gu_block<VAR>(t, kb, H, r.w[u][0], r.w[u][1], r.sw[u], qx, sx, xs);
+            if (lane < 8) acc = fmaf(v.x, v.y, acc);
+            else if (lane >= 40 && lane < 48 && KH + j < KB) sp[j * 8 + lane - 40] = v;
         }
     }
 }
@@ -572,15 +635,16 @@ __device__ __forceinline__ void gateup_mfma(const FusedArgs &a, int t, int j0,
 // fold the first half, lanes 40-47 take over their sums and fold the second
 // half, with no LDS and no wait beyond the item's own loads. Larger H takes
 // further batches and keeps the second half's pairs in LDS (sp).
+template <int VAR>
 __device__ __forceinline__ void gateup_finish(const FusedArgs &a, int p, int n0, int e,
                                               const GateUpRegs &r0, const uint8_t *qx,
-                                              const float *sx, float2 *sp, uint32_t epoch) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
-    const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2, t = p / a.K, hb = l16 >> 3;
+                                              const float *sx, const uint16_t *xs, float2 *sp,
+                                              uint32_t epoch) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15;
+    const int H = a.H, KB = H / GROUP, KH = (KB + 1) / 2, t = p / a.KS, hb = l16 >> 3;
     const int src = (lane >= 40 && lane < 48) ? lane - 40 : lane;
     float g;
     if (KH <= GU_STEP) {
-        const uint8_t *qa = qx + t * H + 32 * kq;
         float sc[GU_STEP], pv[GU_STEP];
 #pragma unroll
         for (int u = 0; u < GU_STEP; ++u) {
@@ -588,10 +652,10 @@ __device__ __forceinline__ void gateup_finish(const FusedArgs &a, int p, int n0,
             pv[u] = 0.0f;
             if (u < KH) {  // wave-uniform
                 const int kb = min(hb * KH + u, KB - 1);  // A row l16 and B column l16 share it
-                const v8i av = as_v8i(ld16(qa + kb * GROUP), ld16(qa + kb * GROUP + 16));
-                const v4f d = mfma_fp8_k128(av, as_v8i(r0.w[u][0], r0.w[u][1]));
-                sc[u] = sx[t * KB + kb] * r0.sw[u];
-                pv[u] = d[0];
+                const float2 v =
+                    gu_block<VAR>(t, kb, H, r0.w[u][0], r0.w[u][1], r0.sw[u], qx, sx, xs);
+                sc[u] = v.x;
+                pv[u] = v.y;
             }
         }
         float acc = 0.0f;  // lanes 0-7: blocks 0..KH-1
@@ -604,11 +668,11 @@ __device__ __forceinline__ void gateup_finish(const FusedArgs &a, int p, int n0,
             if (KH + u < KB) g = fmaf(sc[u], pv[u], g);
     } else {
         float acc = 0.0f;
-        gateup_mfma(a, t, 0, r0, qx, sx, sp, acc);
+        gateup_mfma<VAR>(a, t, 0, r0, qx, sx, xs, sp, acc);
         for (int j0 = GU_STEP; j0 < KH; j0 += GU_STEP) {
             GateUpRegs r;
-            gateup_load(a, e, n0, j0, r);
-            gateup_mfma(a, t, j0, r, qx, sx, sp, acc);
+            gateup_load<VAR>(a, e, n0, j0, r);
+            gateup_mfma<VAR>(a, t, j0, r, qx, sx, xs, sp, acc);
         }
         g = __shfl(acc, src);
         wave_lds_sync();
@@ -623,9 +687,11 @@ __device__ __forceinline__ void gateup_finish(const FusedArgs &a, int p, int n0,
     const float u = __shfl(g, min(lane + 4, 63));
     const float hv = silu(g) * u;
     const float hl = __shfl(hv, F + (lane & 3));
+    // the control hands h over rounded to bf16, as its grouped kernel stages it
+    const uint32_t hbits = VAR == DV_NOQ ? f32_to_bf16(hl) : __float_as_uint(hl);
     if (lane < 4 * REPL)
-        st_dev(a.h + ((int64_t)(lane >> 2) * a.T * a.K + p) * a.I + n0 + (lane & 3),
-               tagged(__float_as_uint(hl), epoch));
+        st_dev(a.h + ((int64_t)(lane >> 2) * a.T * a.KS + p) * a.I + n0 + (lane & 3),
+               tagged(hbits, epoch));
 }
 
 // ------------------------------------------------------------- phase C
@@ -678,28 +744,43 @@ __device__ __forceinline__ void down_stage_shared(const DownRegs<KBR, TPW> &r, u
     for (int i = 0; i < 4; ++i) sdo[(wave * 4 + i) * 64 + lane] = r.s[i];
 }
 
+// Expert e's down rows and block scales (e = E: the block-FP8 shared expert)
+template <int VAR>
+__device__ __forceinline__ void expert_down(const FusedArgs &a, int e, const uint8_t *&w,
+                                            const float *&s) {
+    if (VAR == DV_SFP8 && e == a.E) {
+        w = a.sh8_down;
+        s = a.sh_s_down;
+    } else {
+        w = a.w_down + (int64_t)e * a.H * a.I;
+        s = a.s_down + (int64_t)e * (a.H / GROUP) * (a.I / GROUP);
+    }
+}
+
 // Routed A operands and block scales of unit (t, m0) for this wave's tiles,
-// K blocks [0, KBR). Branch-free: slots past K reload slot K - 1 and K
+// K blocks [0, KBR). Branch-free: slots past KS reload slot KS - 1 and K
 // blocks past the row reload the last one (the MFMA loop skips both), so the
 // loads form one straight run and a later wait on earlier loads does not
 // also wait for these.
-template <int KBR, int TPW>
+template <int KBR, int TPW, int VAR>
 __device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int m0,
                                                  const int32_t *ids, DownRegs<KBR, TPW> &r) {
-    const int H = a.H, I = a.I, K = a.K, IB = I / GROUP;
+    const int I = a.I, KS = a.KS, IB = I / GROUP;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int tau = wave + 4 * u;
-        const int e = ids[t * K + min(2 * tau + (l16 >> 3), K - 1)];
-        const uint8_t *row = a.w_down + ((int64_t)e * H + m0 + (l16 & 7)) * I + 32 * kq;
-        const int es = ids[t * K + min(2 * tau + (kq >> 1), K - 1)];
-        const float *sd = a.s_down + ((int64_t)es * (H / GROUP) + m0 / GROUP) * IB;
+        const uint8_t *wb;
+        const float *sb, *sbs;
+        const uint8_t *dummy;
+        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (l16 >> 3), KS - 1)], wb, sb);
+        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (kq >> 1), KS - 1)], dummy, sbs);
+        const uint8_t *row = wb + (int64_t)(m0 + (l16 & 7)) * I;
+        const float *sd = sbs + (int64_t)(m0 / GROUP) * IB;
 #pragma unroll
         for (int b = 0; b < KBR; ++b) {
             const int bc = min(b, IB - 1);
-            r.w[u][b][0] = ld16(row + bc * GROUP);
-            r.w[u][b][1] = ld16(row + bc * GROUP + 16);
+            load_block<VAR>(row, bc, r.w[u][b][0], r.w[u][b][1]);
             r.sd[u][b] = sd[bc];
         }
     }
@@ -731,51 +812,81 @@ __device__ __forceinline__ float shared_down_chain(const FusedArgs &a, int t, in
 
 // The unit's output: every routed slot's e_j (MFMA), the gated shared row
 // and the combine y = bf16(sum_j w_j e_j + gamma s), slots in order. ej and
-// ss are LDS scratch ([K][MB] and [MB] fp32); hs and gamma were staged in
-// LDS; with chain false the shared rows' s is already in ss. Every thread of
+// ss are LDS scratch ([KS][MB] and [MB] fp32); hs and gamma were staged in
+// LDS; with chain false the shared rows' s is already in ss. With the
+// block-FP8 shared expert, s is its slot's e (slot K). qh holds h as 1x128
+// e4m3 codes with scales shs, or (DV_NOQ) as bf16 values. Every thread of
 // the workgroup calls this (it has barriers).
-template <int KBR, int TPW>
+template <int KBR, int TPW, int VAR>
 __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
                                           const DownRegs<KBR, TPW> &r, const uint8_t *qh,
                                           const float *shs, const int32_t *ids,
                                           const float *wts, const uint16_t *hs_l,
                                           const float *gam_l, float *ej, float *ss,
                                           uint4 *sdo, bool chain) {
-    const int H = a.H, I = a.I, K = a.K, IB = I / GROUP, Is = a.Is;
+    const int H = a.H, I = a.I, K = a.K, KS = a.KS, IB = I / GROUP, Is = a.Is;
+    const int Isb = VAR == DV_SFP8 ? 0 : Is;  // width of the bf16 shared expert
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kq = lane >> 4;
 
     // routed slots: tile tau = wave + 4u holds slots 2 tau, 2 tau + 1
-    const int ntiles = (K + 1) / 2;
-    const int jb = min(l16, K - 1);  // this lane's B column: slot l16
-    const uint8_t *qb = qh + (int64_t)(t * K + jb) * I + 32 * kq;
+    const int ntiles = (KS + 1) / 2;
+    const int jb = min(l16, KS - 1);  // this lane's B column: slot l16
+    const uint8_t *qb = qh + (int64_t)(t * KS + jb) * I + 32 * kq;
+    const uint16_t *hb = reinterpret_cast<const uint16_t *>(qh) + (int64_t)(t * KS + jb) * I + 8 * kq;
     const uint8_t *wrow[TPW];
     float acc[TPW][4] = {};
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int tau = wave + 4 * u;
-        const int e = ids[t * K + min(2 * tau + (l16 >> 3), K - 1)];
-        wrow[u] = a.w_down + ((int64_t)e * H + m0 + (l16 & 7)) * I + 32 * kq;
+        const float *sb;
+        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (l16 >> 3), KS - 1)], wrow[u], sb);
+        wrow[u] += (int64_t)(m0 + (l16 & 7)) * I;
     }
     const int js_lane = 2 * wave + (kq >> 1);  // slot of this lane's D rows (tile u adds 8u)
     for (int b = 0; b < IB; ++b) {
-        const v8i bq = as_v8i(*reinterpret_cast<const uint4 *>(qb + b * GROUP),
-                              *reinterpret_cast<const uint4 *>(qb + b * GROUP + 16));
+        v8i bq;
+        v8bf bh[4];
+        if constexpr (VAR == DV_NOQ) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bh[i] = as_v8bf(*reinterpret_cast<const uint4 *>(hb + b * GROUP + 32 * i));
+        } else {
+            bq = as_v8i(*reinterpret_cast<const uint4 *>(qb + b * GROUP),
+                        *reinterpret_cast<const uint4 *>(qb + b * GROUP + 16));
+        }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             if (wave + 4 * u >= ntiles) continue;
-            v8i aw;
+            const int js = min(js_lane + 8 * u, KS - 1);
+            uint4 w0, w1;
             float sdv;
             if (b < KBR) {
-                aw = as_v8i(r.w[u][b][0], r.w[u][b][1]);
+                w0 = r.w[u][b][0];
+                w1 = r.w[u][b][1];
                 sdv = r.sd[u][b];
             } else {  // K blocks past the register copy
-                aw = as_v8i(ld16(wrow[u] + b * GROUP), ld16(wrow[u] + b * GROUP + 16));
-                const int es = ids[t * K + min(js_lane + 8 * u, K - 1)];
-                sdv = a.s_down[((int64_t)es * (H / GROUP) + m0 / GROUP) * IB + b];
+                load_block<VAR>(wrow[u], b, w0, w1);
+                const uint8_t *dummy;
+                const float *sb;
+                expert_down<VAR>(a, ids[t * KS + js], dummy, sb);
+                sdv = sb[(int64_t)(m0 / GROUP) * IB + b];
             }
-            const v4f d = mfma_fp8_k128(aw, bq);
-            const int js = min(js_lane + 8 * u, K - 1);
-            const float sc = shs[(t * K + js) * IB + b] * sdv;
+            v4f d;
+            float sc;
+            if constexpr (VAR == DV_NOQ) {
+                // the control: four chained bf16 MFMAs from zero on the
+                // decoded codes and bf16 h, folded with the weight scale
+                const uint2 c[4] = {make_uint2(w0.x, w0.y), make_uint2(w0.z, w0.w),
+                                    make_uint2(w1.x, w1.y), make_uint2(w1.z, w1.w)};
+                d = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    d = mfma_bf16_k32(as_v8bf(e4m3x8_to_bf16(c[i])), bh[i], d);
+                sc = sdv;
+            } else {
+                d = mfma_fp8_k128(as_v8i(w0, w1), bq);
+                sc = shs[(t * KS + js) * IB + b] * sdv;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(sc, d[i], acc[u][i]);
         }
@@ -785,11 +896,11 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
         const int js = js_lane + 8 * u;
         // D rows 4 kq + i are slot 2 tau + (kq >> 1), rows m0 + 4 (kq & 1) + i;
         // the lane whose column is that slot holds the product wanted
-        if (js < K && l16 == js)
+        if (js < KS && l16 == js)
 #pragma unroll
             for (int i = 0; i < 4; ++i) ej[js * MB + 4 * (kq & 1) + i] = bf16_round(acc[u][i]);
     }
-    if (Is > 0 && chain) {  // else computed before the h handoff
+    if (Isb > 0 && chain) {  // else computed before the h handoff
         down_stage_shared<KBR, TPW>(r, sdo);
         __syncthreads();
         if (wave == CHAIN_WAVE) {
@@ -802,8 +913,8 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
     // combine: slots in order, then the shared term
     if (tid < MB) {
         float yacc = 0.0f;
-        for (int j = 0; j < K; ++j) yacc = fmaf(wts[t * K + j], ej[j * MB + tid], yacc);
-        if (Is > 0) yacc = fmaf(gam_l[t], ss[tid], yacc);
+        for (int j = 0; j < K; ++j) yacc = fmaf(wts[t * KS + j], ej[j * MB + tid], yacc);
+        if (Is > 0) yacc = fmaf(gam_l[t], VAR == DV_SFP8 ? ej[K * MB + tid] : ss[tid], yacc);
         const uint16_t yb = (uint16_t)f32_to_bf16(yacc);
         a.y[(int64_t)t * H + m0 + tid] = yb;
         if (a.y2) a.y2[(int64_t)t * H + m0 + tid] = yb;
@@ -818,18 +929,31 @@ struct LdsPlan {
     int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
-__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is) {
+// slots per row of variant var: the block-FP8 shared expert is one more
+// slot with the routed experts' shape (Is = I) and at most 16 slots fit the
+// phase-C tiles; -1 when the kernel cannot run the variant
+int decode_slots(int var, int K, int I, int Is) {
+    if (var != DV_SFP8) return K;
+    if (Is != I || K + 1 > 16) return -1;
+    return K + 1;
+}
+
+__host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is, int var) {
     LdsPlan L;
+    if (var == DV_SFP8) {
+        K += 1;  // slots
+        Is = 0;  // no bf16 shared expert
+    }
     const int P = T * K, KB = H / GROUP, KH = (KB + 1) / 2;
     L.qx = 0;
     L.sx = L.qx + al16i(T * H);
     L.qh = L.sx + al16i(T * KB * 4);
-    L.shs = L.qh + al16i(P * I);
+    L.shs = L.qh + al16i(P * I * (var == DV_NOQ ? 2 : 1));  // codes, or bf16 h
     L.ids = L.shs + al16i(P * (I / GROUP) * 4);
     L.wts = L.ids + al16i(P * 4);
     L.hs = L.wts + al16i(P * 4);
     L.gam = L.hs + al16i(T * Is * 2);
-    L.ej = L.gam + al16i(T * 4);          // phase-C unit: e_j of its rows
+    L.ej = L.gam + al16i(T * 4);          // phase-C unit: e_j of its rows, every slot
     L.ss = L.ej + al16i(K * MB * 4);      // phase-C unit: shared down of its rows
     L.rl = L.ss + al16i(MB * 4);          // router: 2 x 4 fp64 wave partials
     L.xs = L.rl + 64;                     // x rows, bf16
@@ -841,8 +965,9 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is) 
     return L;
 }
 
-bool decode_fits(int T, int H, int K, int I, int Is) {
-    return T >= 1 && T <= DECODE_MAX_ROWS && lds_plan(T, H, K, I, Is).total <= 150 * 1024;
+bool decode_fits(int T, int H, int K, int I, int Is, int var) {
+    return T >= 1 && T <= DECODE_MAX_ROWS && decode_slots(var, K, I, Is) > 0 &&
+           lds_plan(T, H, K, I, Is, var).total <= 150 * 1024;
 }
 
 // h groups each 16-lane team stages per round of loads
@@ -905,20 +1030,35 @@ __device__ __forceinline__ void stage_h_quant(int base, int nk, const uint32_t (
         }
 }
 
+// the control's h: bf16 values (the words' low half) into LDS, no scales
+__device__ __forceinline__ void stage_h_bf16(int base, int nk, const uint32_t (&bits)[8 * STAGE_HG],
+                                             uint8_t *qh) {
+    const int teams = blockDim.x >> 4, team = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    uint16_t *hb = reinterpret_cast<uint16_t *>(qh);
+#pragma unroll
+    for (int k = 0; k < STAGE_HG; ++k)
+        if (k < nk) {
+            uint16_t *row = hb + (base + team + teams * k) * GROUP + sub;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) row[16 * i] = (uint16_t)bits[8 * k + i];
+        }
+}
+
+// Isb: width of the bf16 shared expert (hs); gam: whether gamma exists
 __device__ __forceinline__ void stage_c_issue(const uint64_t *h, const uint64_t *hs,
-                                              const uint64_t *gamma, int T, int P, int I, int Is,
-                                              uint32_t epoch, StageC &c) {
+                                              const uint64_t *gamma, int T, int P, int I, int Isb,
+                                              bool gam, uint32_t epoch, StageC &c) {
     const int rp = blockIdx.x % REPL, tid = threadIdx.x, nth = blockDim.x;
-    const int n_hs = T * Is;
+    const int n_hs = T * Isb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) c.sidx[i] = tid + nth * i;
     c.n_s0 = min(8, max(0, (n_hs - tid + nth - 1) / nth));
     c.gidx[0] = rp * T + tid;
-    c.n_g = Is > 0 && tid < T ? 1 : 0;
+    c.n_g = gam && tid < T ? 1 : 0;
     c.nk0 = stage_h_round(0, P * (I / GROUP), c.hidx);
     // hs and gamma first: they were written in phase A, and waiting for
     // them must not also wait for the h words behind them
-    poll_issue<8>(hs + (int64_t)rp * T * Is, c.sidx, c.n_s0, epoch, c.sw);
+    poll_issue<8>(hs + (int64_t)rp * T * Isb, c.sidx, c.n_s0, epoch, c.sw);
     poll_issue<1>(gamma, c.gidx, c.n_g, epoch, c.gw);
     poll_issue<8 * STAGE_HG>(h + (int64_t)rp * P * I, c.hidx, 8 * c.nk0, epoch, c.hw);
 }
@@ -955,6 +1095,7 @@ __device__ __forceinline__ void stage_c_finish_shared(const uint64_t *hs, const 
     }
 }
 
+template <int VAR>
 __device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P, int I,
                                                  uint32_t epoch, uint32_t *err, StageC &c,
                                                  uint8_t *qh, float *shs) {
@@ -965,14 +1106,16 @@ __device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P
         uint32_t bits[8 * STAGE_HG];
         poll_complete<8 * STAGE_HG, 2>(err, handoff_region(hsrc, P * I), c.hidx, 8 * c.nk0, epoch,
                                        c.hw, bits);
-        stage_h_quant(0, c.nk0, bits, qh, shs);
+        if constexpr (VAR == DV_NOQ) stage_h_bf16(0, c.nk0, bits, qh);
+        else stage_h_quant(0, c.nk0, bits, qh, shs);
     }
     for (int base = STAGE_HG * teams; base < n_groups; base += STAGE_HG * teams) {
         int idx[8 * STAGE_HG];
         const int nk = stage_h_round(base, n_groups, idx);
         uint32_t bits[8 * STAGE_HG];
         poll_words<8 * STAGE_HG>(err, hsrc, idx, 8 * nk, epoch, bits);
-        stage_h_quant(base, nk, bits, qh, shs);
+        if constexpr (VAR == DV_NOQ) stage_h_bf16(base, nk, bits, qh);
+        else stage_h_quant(base, nk, bits, qh, shs);
     }
 }
 
@@ -1000,21 +1143,22 @@ __device__ __forceinline__ void renorm_rows_to_lds(const uint16_t *y, int T, int
 }
 
 // RN: the renormalising variant (x from y_prev in the prologue)
-template <int NQ, int KBR, int TPW, bool RN>
+template <int NQ, int KBR, int TPW, bool RN, int VAR>
 __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int T = a.T, H = a.H, K = a.K, I = a.I, E = a.E, P = T * K, Is = a.Is;
+    const int T = a.T, H = a.H, K = a.K, KS = a.KS, I = a.I, E = a.E, P = T * KS, Is = a.Is;
+    const int Isb = VAR == DV_SFP8 ? 0 : Is;  // width of the bf16 shared expert
     const int KB = H / GROUP, KH = (KB + 1) / 2;
-    const LdsPlan L = lds_plan(T, H, K, I, Is);
+    const LdsPlan L = lds_plan(T, H, K, I, Is, VAR);
     uint8_t *qx = lds + L.qx;                                 // [T][H]
     float *sx = reinterpret_cast<float *>(lds + L.sx);        // [T][H/128]
-    uint8_t *qh = lds + L.qh;                                 // [P][I]
+    uint8_t *qh = lds + L.qh;                                 // [P][I] (bf16 with DV_NOQ)
     float *shs = reinterpret_cast<float *>(lds + L.shs);      // [P][I/128]
     int32_t *ids = reinterpret_cast<int32_t *>(lds + L.ids);  // [P]
     float *wts = reinterpret_cast<float *>(lds + L.wts);      // [P]
-    uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Is]
+    uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Isb]
     float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
-    float *ej = reinterpret_cast<float *>(lds + L.ej);          // [K][MB]
+    float *ej = reinterpret_cast<float *>(lds + L.ej);          // [KS][MB]
     float *ss = reinterpret_cast<float *>(lds + L.ss);          // [MB]
     double *rl = reinterpret_cast<double *>(lds + L.rl);        // [2][4]
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds + L.xs);    // [T][H]
@@ -1067,12 +1211,28 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
 
     // A2: the shared expert's gate/up columns and the shared gate, on waves
     // 1-3 (wave 0 runs the top-K next, and a wave with loads in flight would
-    // wait for them before its first poll)
+    // wait for them before its first poll). The block-FP8 shared expert is
+    // slot K of every row: its gate/up items are the routed items' (expert
+    // E), with h handed over among the routed pairs' h.
     if (wave > 0 && Is > 0) {
-        const int n_s = Is / 2, n_items = n_s + T;
-        for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
-            if (it < n_s) s_item(a, it, xs, sq, epoch);
-            else g_item(a, it - n_s, xs, epoch);
+        if constexpr (VAR == DV_SFP8) {
+            const int per_row = Is / 4, n_s = T * per_row, n_items = n_s + T;
+            for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
+                if (it < n_s) {
+                    const int t = it / per_row, n0 = (it % per_row) * 4;
+                    GateUpRegs gr;
+                    gateup_load<VAR>(a, E, n0, 0, gr);
+                    gateup_finish<VAR>(a, t * KS + K, n0, E, gr, qx, sx, xs, sp, epoch);
+                } else {
+                    g_item(a, it - n_s, xs, epoch);
+                }
+            }
+        } else {
+            const int n_s = Is / 2, n_items = n_s + T;
+            for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
+                if (it < n_s) s_item(a, it, xs, sq, epoch);
+                else g_item(a, it - n_s, xs, epoch);
+            }
         }
     }
 
@@ -1080,8 +1240,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     // routed gate/up items
     for (int t = wave; t < T; t += 4)
         topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
-                    threadIdx.x & 63, ids + t * K, wts + t * K,
+                    threadIdx.x & 63, ids + t * KS, wts + t * KS,
                     !a.bias && !(a.flags & K_LOGITS_FP32));
+    if (VAR == DV_SFP8 && (int)threadIdx.x < T) {  // slot K: the shared expert
+        ids[threadIdx.x * KS + K] = E;
+        wts[threadIdx.x * KS + K] = 0.0f;
+    }
     __syncthreads();
     // The first unit's routed and shared down rows are issued once this
     // wave's first gate/up rows are in and their h has gone out: they stream
@@ -1089,50 +1253,55 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     // (issued alongside them, they held the gate/up phase back by about
     // 0.8 us and the layer by about 0.4 us). Scheduling barriers keep the
     // three steps in this order.
-    const int per_pair = I / 4, n_items = P * per_pair;
+    // routed item it: pair (t, j) of the T * K routed pairs, columns n0..n0+3
+    const int per_pair = I / 4, n_items = T * K * per_pair;
+    auto pair_of = [&](int it) {
+        const int rp = it / per_pair;
+        return VAR == DV_SFP8 ? (rp / K) * KS + rp % K : rp;
+    };
     DownRegs<KBR, TPW> dr;
     {
         const int it = min(gw, n_items - 1);  // waves past the last item load it (unused)
-        const int p = it / per_pair, n0 = (it % per_pair) * 4;
+        const int p = pair_of(it), n0 = (it % per_pair) * 4;
         GateUpRegs gr;
-        gateup_load(a, ids[p], n0, 0, gr);
+        gateup_load<VAR>(a, ids[p], n0, 0, gr);
         __builtin_amdgcn_sched_barrier(0);
-        if (gw < n_items) gateup_finish(a, p, n0, ids[p], gr, qx, sx, sp, epoch);
+        if (gw < n_items) gateup_finish<VAR>(a, p, n0, ids[p], gr, qx, sx, xs, sp, epoch);
         __builtin_amdgcn_sched_barrier(0);
-        down_load_routed<KBR, TPW>(a, t_first, m_first, ids, dr);
-        if (Is > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
+        down_load_routed<KBR, TPW, VAR>(a, t_first, m_first, ids, dr);
+        if (Isb > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int it = gw + nw; it < n_items; it += nw) {
-        const int p = it / per_pair, n0 = (it % per_pair) * 4;
+        const int p = pair_of(it), n0 = (it % per_pair) * 4;
         GateUpRegs gr;
-        gateup_load(a, ids[p], n0, 0, gr);
-        gateup_finish(a, p, n0, ids[p], gr, qx, sx, sp, epoch);
+        gateup_load<VAR>(a, ids[p], n0, 0, gr);
+        gateup_finish<VAR>(a, p, n0, ids[p], gr, qx, sx, xs, sp, epoch);
     }
 
     // C: hs and gamma (ready since phase A) into LDS, the first unit's
     // shared down rows while h is still on its way, then h (re-quantised)
     // into LDS once it exists, and whole output rows with the combine.
     StageC sc;
-    stage_c_issue(a.h, a.hs, a.gamma, T, P, I, Is, epoch, sc);
+    stage_c_issue(a.h, a.hs, a.gamma, T, P, I, Isb, Is > 0, epoch, sc);
     __builtin_amdgcn_sched_barrier(0);
-    stage_c_finish_shared(a.hs, a.gamma, T, Is, epoch, err, sc, hs_l, gam_l);
-    if (Is > 0) down_stage_shared<KBR, TPW>(dr, sdo);
+    stage_c_finish_shared(a.hs, a.gamma, T, Isb, epoch, err, sc, hs_l, gam_l);
+    if (Isb > 0) down_stage_shared<KBR, TPW>(dr, sdo);
     __syncthreads();
-    if (Is > 0 && wave == CHAIN_WAVE && (int)blockIdx.x < units) {
+    if (Isb > 0 && wave == CHAIN_WAVE && (int)blockIdx.x < units) {
         const float s = shared_down_chain(a, t_first, m_first, sdo, hs_l);
         if ((threadIdx.x & 63) < MB) ss[threadIdx.x & 63] = s;
     }
-    stage_c_finish_h(a.h, T, P, I, epoch, err, sc, qh, shs);
+    stage_c_finish_h<VAR>(a.h, T, P, I, epoch, err, sc, qh, shs);
     __syncthreads();
     for (int u = blockIdx.x; u < units; u += a.nwg) {
         const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
         const bool first = u == (int)blockIdx.x;
         if (!first) {
-            down_load_routed<KBR, TPW>(a, t, m0, ids, dr);
-            if (Is > 0) down_load_shared<KBR, TPW>(a, m0, dr);
+            down_load_routed<KBR, TPW, VAR>(a, t, m0, ids, dr);
+            if (Isb > 0) down_load_shared<KBR, TPW>(a, m0, dr);
         }
-        down_unit<KBR, TPW>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, ss, sdo, !first);
+        down_unit<KBR, TPW, VAR>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, ss, sdo, !first);
     }
     // every wave has read the counter: advance it for the next call
     if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 1u);
@@ -1140,55 +1309,66 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
 
 // NQ: router chunks per lane (H / 2048, rounded up to 1 or 4); KBR: K blocks
 // of a down row held in registers (I / 128 up to 4; more are loaded in the
-// loop); TPW: MFMA tiles (slot pairs) per wave (K up to 8: one, up to 16:
-// two)
+// loop); TPW: MFMA tiles (slot pairs) per wave (KS up to 8: one, up to 16:
+// two); VAR: the layer or one of its switches (the renormalising prologue
+// only with the plain layer)
 // Every workgroup waits for values other workgroups produce, so all of the
 // grid (one workgroup per CU) must be resident at once: the launch is
 // refused unless one workgroup with the largest LDS plan the decode path
 // takes fits on a CU (checked once per kernel variant).
-template <int NQ, int KBR, int TPW, bool RN>
+template <int NQ, int KBR, int TPW, bool RN, int VAR>
 static hipError_t launch_v(const FusedArgs &a, size_t lds, hipStream_t st) {
     static const hipError_t fits = [] {
         int n = 0;
         const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN>), 256,
+            &n, reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN, VAR>), 256,
             150 * 1024);
         return e != hipSuccess ? e : n >= 1 ? hipSuccess : hipErrorInvalidConfiguration;
     }();
     if (fits != hipSuccess) return fits;
-    hipLaunchKernelGGL((decode_fused_kernel<NQ, KBR, TPW, RN>), dim3(a.nwg), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((decode_fused_kernel<NQ, KBR, TPW, RN, VAR>), dim3(a.nwg), dim3(256), lds,
+                       st, a);
     return hipGetLastError();
 }
 
-template <int NQ, int TPW, bool RN>
+template <int NQ, int TPW, bool RN, int VAR>
 static hipError_t launch_t(const FusedArgs &a, size_t lds, hipStream_t st) {
     const int ib = a.I / GROUP;
-    if (ib <= 1) return launch_v<NQ, 1, TPW, RN>(a, lds, st);
-    if (ib <= 2) return launch_v<NQ, 2, TPW, RN>(a, lds, st);
-    return launch_v<NQ, 4, TPW, RN>(a, lds, st);
+    if (ib <= 1) return launch_v<NQ, 1, TPW, RN, VAR>(a, lds, st);
+    if (ib <= 2) return launch_v<NQ, 2, TPW, RN, VAR>(a, lds, st);
+    return launch_v<NQ, 4, TPW, RN, VAR>(a, lds, st);
 }
 
-template <int NQ, bool RN>
+template <int NQ, bool RN, int VAR>
 static hipError_t launch_nq(const FusedArgs &a, size_t lds, hipStream_t st) {
-    if (a.K <= 8) return launch_t<NQ, 1, RN>(a, lds, st);
-    return launch_t<NQ, 2, RN>(a, lds, st);
+    if (a.KS <= 8) return launch_t<NQ, 1, RN, VAR>(a, lds, st);
+    return launch_t<NQ, 2, RN, VAR>(a, lds, st);
 }
 
-template <int NQ, int KBR, int TPW, bool RN>
+template <int NQ, int KBR, int TPW, bool RN, int VAR>
 static void set_lds_limit() {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN>),
+        reinterpret_cast<const void *>(&decode_fused_kernel<NQ, KBR, TPW, RN, VAR>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
-template <int NQ, bool RN>
+template <int NQ, bool RN, int VAR>
 static void set_lds_limits() {
-    set_lds_limit<NQ, 1, 1, RN>();
-    set_lds_limit<NQ, 2, 1, RN>();
-    set_lds_limit<NQ, 4, 1, RN>();
-    set_lds_limit<NQ, 1, 2, RN>();
-    set_lds_limit<NQ, 2, 2, RN>();
-    set_lds_limit<NQ, 4, 2, RN>();
+    set_lds_limit<NQ, 1, 1, RN, VAR>();
+    set_lds_limit<NQ, 2, 1, RN, VAR>();
+    set_lds_limit<NQ, 4, 1, RN, VAR>();
+    set_lds_limit<NQ, 1, 2, RN, VAR>();
+    set_lds_limit<NQ, 2, 2, RN, VAR>();
+    set_lds_limit<NQ, 4, 2, RN, VAR>();
+}
+
+template <int NQ>
+static hipError_t launch_var(const FusedArgs &a, size_t lds, hipStream_t st) {
+    if (a.y_prev) return a.var == DV_PLAIN ? launch_nq<NQ, true, DV_PLAIN>(a, lds, st)
+                                           : hipErrorInvalidValue;
+    if (a.var == DV_SFP8) return launch_nq<NQ, false, DV_SFP8>(a, lds, st);
+    if (a.var == DV_NOQ) return launch_nq<NQ, false, DV_NOQ>(a, lds, st);
+    return launch_nq<NQ, false, DV_PLAIN>(a, lds, st);
 }
 
 // copies the spin-out word to *out and, with clear, zeroes it (one thread)
@@ -1203,20 +1383,25 @@ hipError_t launch_decode_status(uint32_t *sync, uint32_t *out, int clear, hipStr
 }
 
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I, a.Is).total;
+    if (a.var < DV_PLAIN || a.var > DV_NOQ || a.KS != decode_slots(a.var, a.K, a.I, a.Is))
+        return hipErrorInvalidValue;
+    const size_t lds = (size_t)lds_plan(a.T, a.H, a.K, a.I, a.Is, a.var).total;
     if (lds > 64 * 1024) {
         static const bool once = [] {
-            set_lds_limits<1, false>();
-            set_lds_limits<4, false>();
-            set_lds_limits<1, true>();
-            set_lds_limits<4, true>();
+            set_lds_limits<1, false, DV_PLAIN>();
+            set_lds_limits<4, false, DV_PLAIN>();
+            set_lds_limits<1, true, DV_PLAIN>();
+            set_lds_limits<4, true, DV_PLAIN>();
+            set_lds_limits<1, false, DV_SFP8>();
+            set_lds_limits<4, false, DV_SFP8>();
+            set_lds_limits<1, false, DV_NOQ>();
+            set_lds_limits<4, false, DV_NOQ>();
             return true;
         }();
         (void)once;
     }
-    const bool rn = a.y_prev != nullptr;
-    if (a.H <= 2048) return rn ? launch_nq<1, true>(a, lds, st) : launch_nq<1, false>(a, lds, st);
-    return rn ? launch_nq<4, true>(a, lds, st) : launch_nq<4, false>(a, lds, st);
+    if (a.H <= 2048) return launch_var<1>(a, lds, st);
+    return launch_var<4>(a, lds, st);
 }
 
 }  // namespace moe

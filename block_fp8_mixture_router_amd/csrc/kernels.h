@@ -49,21 +49,30 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *
                              hipStream_t st);
 
 // ---- decode.hip (row-at-a-time path: one persistent kernel per layer)
+// what the one-row kernel computes: the layer as the pages define it, or one
+// of its two switches (the block-FP8 shared expert, run as one more slot of
+// every row; the control without activation quantisation)
+constexpr int DV_PLAIN = 0, DV_SFP8 = 1, DV_NOQ = 2;
 struct FusedArgs {
     int T, H, E, K, I, Is;
+    int KS;   // slots per row: K, or K + 1 when the block-FP8 shared expert is slot K
+    int var;  // DV_*
     uint32_t flags;
     const uint16_t *x, *router_w;
     const float *bias;
     const uint8_t *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     const uint16_t *sh_gate, *sh_up, *sh_down, *sh_gate_w;
+    // DV_SFP8: the shared expert's e4m3 rows and 128x128 block scales
+    const uint8_t *sh8_gate, *sh8_up, *sh8_down;
+    const float *sh_s_gate, *sh_s_up, *sh_s_down;
     // values that cross workgroups are 64-bit words (32-bit value, call
     // epoch) kept in DECODE_REPLICAS copies, so each copy is read by
     // 1/DECODE_REPLICAS of the workgroups
     uint64_t *logits;  // [R][T, E] fp32 logits
     uint64_t *gamma;   // [R][T] fp32
     uint64_t *hs;      // [R][T, Is] bf16 shared-expert SwiGLU output
-    uint64_t *h;       // [R][T*K, I] fp32 routed SwiGLU output
+    uint64_t *h;       // [R][T*KS, I] fp32 routed SwiGLU output (bf16 bits with DV_NOQ)
     uint32_t *sync;    // [ERR_WORD] spin-out flag, [SYNC_FLAGS + b] workgroup b's call counter
     uint16_t *y;       // [T, H]
     uint16_t *y2;      // [T, H] a second copy of y, or null
@@ -79,7 +88,9 @@ constexpr int DECODE_REPLICAS = 8;
 constexpr int SYNC_FLAGS = 64;
 constexpr int SYNC_WORDS = SYNC_FLAGS + 1024;  // up to 1024 workgroups
 constexpr int SYNC_ERR_WORD = 32;              // the spin-out word
-bool decode_fits(int T, int H, int K, int I, int Is);
+// slots per row of the one-row kernel for variant var (-1: it cannot run it)
+int decode_slots(int var, int K, int I, int Is);
+bool decode_fits(int T, int H, int K, int I, int Is, int var);
 hipError_t launch_decode_fused(const FusedArgs &a, hipStream_t st);
 // the decode path's spin-out word (workspace sync word SYNC_ERR_WORD) -> out
 hipError_t launch_decode_status(uint32_t *sync, uint32_t *out, int clear, hipStream_t st);

@@ -23,17 +23,6 @@ constexpr int NQ_PAD = 16;         // LDS row padding (bytes)
 
 __device__ __forceinline__ v8bf nq_as_v8bf(uint4 v) { return __builtin_bit_cast(v8bf, v); }
 
-// Eight e4m3 codes (a uint2) -> eight bf16 values (exact).
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
-    float f[8];
-    e4m3x4_to_f32(c.x, f[0], f[1], f[2], f[3]);
-    e4m3x4_to_f32(c.y, f[4], f[5], f[6], f[7]);
-    uint32_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(f[2 * k]) | (f32_to_bf16(f[2 * k + 1]) << 16);
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 // One K block (128 columns) of a weight row for lane (l16, kq): the codes of
 // columns 32i + 8kq .. +8 for i = 0..3, as bf16 B operands.
 __device__ __forceinline__ void nq_load_w(const uint8_t *row, int kb, int kq, uint2 (&c)[4]) {

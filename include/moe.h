@@ -61,14 +61,15 @@ typedef enum {
 #define MOE_SHARED_FP8    (1u << 0) /* variant: the shared expert stored block-FP8 (codes and
                                        128x128 block scales sh_s_*), run exactly as a routed
                                        expert on the quantised rows, gamma in place of w;
-                                       moe_forward only, grouped path at any T */
+                                       moe_forward only */
 #define MOE_LOGITS_FP32   (1u << 1) /* decide on fp32 router logits (no bf16 rounding) */
 #define MOE_NO_ACT_QUANT  (1u << 2) /* fidelity control: the routed experts take bf16 x and
                                        bf16 h times the decoded e4m3 weights (no activation
-                                       quantisation); moe_forward only, grouped path at any T */
+                                       quantisation); moe_forward only */
 #define MOE_FORCE_GEMV    (1u << 8) /* run the one-row decode kernel (T <= 4; refused with
                                        MOE_E_UNSUPPORTED beyond, where its LDS plan does not
-                                       fit, or with a variant flag) */
+                                       fit, and with MOE_SHARED_FP8 unless Is = I and
+                                       top_k <= 15) */
 #define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
 
 typedef struct {
@@ -173,14 +174,17 @@ moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  *   gamma     = sigmoid(sh_gate_w . x);
  *   y[t]      = bf16(sum_j w_j e_j + gamma s), the sum in slot order.
  * With MOE_SHARED_FP8, s is instead the output of the block-FP8 shared
- * matrices computed as e_j is (quantised x, requantised h); it runs on the
- * expert-grouped kernels at any T and is refused with MOE_FORCE_GEMV or
- * together with MOE_NO_ACT_QUANT.
+ * matrices computed as e_j is (quantised x, requantised h, s rounded to
+ * bf16); it is refused together with MOE_NO_ACT_QUANT. The one-row kernel
+ * runs it as one more slot of every row when Is = I and top_k <= 15 (else
+ * the expert-grouped kernels run it, and MOE_FORCE_GEMV is refused).
  * With MOE_NO_ACT_QUANT (a fidelity control, not a fast path): g_j and u_j
  * take bf16 x unquantised, h_j is rounded to bf16 instead of re-quantised,
  * and e_j takes that h; every product is with the decoded e4m3 weights times
- * their block scales. It runs on the expert-grouped kernels at any T and is
- * refused (MOE_E_UNSUPPORTED) together with MOE_FORCE_GEMV.
+ * their block scales.
+ * Both switches take the one-row kernel at T <= 4 and the expert-grouped
+ * kernels beyond, as the layer does, and a row's output bytes are the same
+ * on either.
  * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
  * workspace: >= moe_workspace_bytes(cfg, T) bytes, zero-filled once before
  * the first moe_forward call that uses it (any single repeated byte value

@@ -224,11 +224,11 @@ def test_no_act_quant_flag():
         return (T * s.top_k * s.inter * 2 + 255) // 256 * 256
 
     # growth with rows is the plain layout's plus the bf16 h region; the
-    # control never takes the one-row path, so it has no handoff regions
+    # control takes the one-row path with the plain layer's handoff regions
     grow_n = moe.workspace_bytes(n, 1024) - moe.workspace_bytes(n, 1)
     grow_c = moe.workspace_bytes(c, 1024) - moe.workspace_bytes(c, 1)
     assert grow_n == grow_c + extra(1024) - extra(1)
-    assert moe.workspace_bytes(n, 1) < moe.workspace_bytes(c, 1)
+    assert moe.workspace_bytes(n, 1) == moe.workspace_bytes(c, 1) + extra(1)
     L = moe.lib()
     TB = _fake_layers(40)
     X, Y, WS = 0x20000000, 0x30000000, 0x40000000
@@ -237,20 +237,37 @@ def test_no_act_quant_flag():
     assert L.moe_forward_stack(ctypes.byref(n), TB, 40, X, 1, eps, Y, None, WS, nb, None) == -5
     w = _fake_weights()
     gemv = _cfg(flags=moe.NO_ACT_QUANT | moe.FORCE_GEMV)
-    assert _fwd(gemv, w, X, 1, Y, WS, moe.workspace_bytes(gemv, 1)) == -5
+    assert _fwd(gemv, w, X, 1, Y, WS, moe.workspace_bytes(gemv, 1)) == -5  # no gfx950 here
+
+
+def _a256(b):
+    return (b + 255) // 256 * 256
 
 
 def test_shared_fp8_flag():
     """The block-FP8 shared flag is known, adds its own workspace regions,
-    needs the three shared scale arrays, and is refused with the control, in
-    a stack and with the decode path forced."""
+    needs the three shared scale arrays, and is refused with the control and
+    in a stack."""
     c, f = _cfg(), _cfg(flags=moe.SHARED_FP8)
-    # per-row regions of its own (pair list, h codes and scales) on top of the
-    # plain layout's; the flag never takes the one-row path, so it has no
-    # handoff regions and its fixed part is smaller
+    s = inputs.DECODE
+    # per-row regions of its own (pair list, tile list and count, h codes and
+    # scales) on top of the plain layout's
     grow_f = moe.workspace_bytes(f, 1024) - moe.workspace_bytes(f, 1)
     grow_c = moe.workspace_bytes(c, 1024) - moe.workspace_bytes(c, 1)
     assert grow_f > grow_c
+    # the one-row path's handoff regions, for its 4 rows in 8 copies of
+    # 8-byte words: no bf16 hs, and h of K + 1 slots (the shared expert is
+    # slot K) instead of K
+    R, td, K, I, Is = 8, 4, s.top_k, s.inter, s.shared_inter
+    own = _a256(4) + _a256(16) + _a256(4) + _a256(Is) + _a256(Is // 128 * 4)
+    handoff = (_a256(R * td * (K + 1) * I * 8) - _a256(R * td * K * I * 8)
+               - _a256(R * td * Is * 8))
+    assert moe.workspace_bytes(f, 1) == moe.workspace_bytes(c, 1) + own + handoff
+    # Is != I: the one-row kernel cannot take the block-FP8 shared expert as a
+    # slot, so that config has no handoff regions at all
+    odd = _cfg(shared_inter=2 * s.inter, flags=moe.SHARED_FP8)
+    odd_plain = _cfg(shared_inter=2 * s.inter)
+    assert moe.workspace_bytes(odd, 1) < moe.workspace_bytes(odd_plain, 1)
     assert moe.workspace_bytes(_cfg(flags=moe.SHARED_FP8 | moe.NO_ACT_QUANT), 1) == 0
     L = moe.lib()
     TB = _fake_layers(40)

@@ -1,11 +1,14 @@
 """The no-activation-quantisation control (MOE_NO_ACT_QUANT) on the GPU
 against the oracle's matching mode, which multiplies unquantised x and h
 by the decoded e4m3 weights; the control's h goes to the down product in
-bf16, inside the output tolerance."""
+bf16, inside the output tolerance. The one-row kernel gives the bits of the
+expert-grouped kernels."""
 import numpy as np
 import pytest
+import torch
 
 import block_fp8_mixture_router_amd as moe
+from block_fp8_mixture_router_amd import inputs
 import oracle
 from tests.gpu_common import OUT_TOL, bits, layer, need_gpu, rel_rows, run_forward, say, x_rows
 
@@ -63,5 +66,44 @@ def test_control_is_deterministic_and_poison_proof():
     shape, dev, _ = layer("DECODE", 0)
     x, _ = x_rows(shape, 64, seed=9)
     a = run_forward(shape, dev, x, moe.NO_ACT_QUANT)
+    b = run_forward(shape, dev, x, moe.NO_ACT_QUANT, poison=True)
+    assert np.array_equal(bits(a.cpu()), bits(b.cpu()))
+
+
+ONE_ROW_SHAPES = {
+    "TINY": inputs.TINY,
+    "DECODE": inputs.DECODE,
+    "ODD": inputs.LayerShape(hidden=384, n_experts=12, top_k=3, inter=384, shared_inter=384),
+    "K12": inputs.LayerShape(hidden=256, n_experts=32, top_k=12, inter=128, shared_inter=128),
+    "H4096": inputs.LayerShape(hidden=4096, n_experts=16, top_k=2, inter=256, shared_inter=256),
+}
+
+
+@pytest.mark.parametrize("name,T,shared", [
+    ("TINY", 1, True), ("TINY", 4, True), ("TINY", 2, False), ("DECODE", 1, True),
+    ("DECODE", 3, True), ("DECODE", 1, False), ("ODD", 2, True), ("K12", 1, True),
+    ("H4096", 2, True),
+])
+def test_control_one_row_kernel(name, T, shared):
+    """The control on the one-row kernel: within its oracle mode's tolerance,
+    and bit for bit the expert-grouped control kernels' output."""
+    say(f"no-act-quant one-row kernel {name} T={T} shared={shared}")
+    shape = ONE_ROW_SHAPES[name]
+    dev = inputs.make_layer(shape, seed=5, device="cuda")
+    torch.cuda.synchronize()
+    host = dev.to("cpu")
+    x, xh = x_rows(shape, T, seed=700 + T)
+    yd = run_forward(shape, dev, x, moe.NO_ACT_QUANT | moe.FORCE_GEMV, shared=shared)
+    yg = run_forward(shape, dev, x, moe.NO_ACT_QUANT | moe.FORCE_GROUPED, shared=shared)
+    rel, worst = _rel(shape, host, xh, yd, oracle.NO_ACT_QUANT, shared=shared)
+    say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
+    assert rel <= OUT_TOL, (rel, worst)
+    assert np.array_equal(bits(yd.cpu()), bits(yg.cpu()))
+
+
+def test_control_one_row_default_and_poison_proof():
+    shape, dev, _ = layer("DECODE", 0)
+    x, _ = x_rows(shape, 2, seed=19)
+    a = run_forward(shape, dev, x, moe.NO_ACT_QUANT | moe.FORCE_GEMV)
     b = run_forward(shape, dev, x, moe.NO_ACT_QUANT, poison=True)
     assert np.array_equal(bits(a.cpu()), bits(b.cpu()))
