@@ -475,7 +475,7 @@ __device__ __forceinline__ void g_item(const FusedArgs &a, int t, const uint16_t
 
 // top-K of row t from this workgroup's copy of the tagged logits
 template <int NL>
-__device__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
+__device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
                               int lane, int32_t *ids, float *wts, bool packed) {
     int idx[NL];
 #pragma unroll
@@ -502,13 +502,23 @@ __device__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, 
     }
 }
 
-__device__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
-                            int lane, int32_t *ids, float *wts, bool packed) {
-    if (E <= 64) topk_tagged_n<1>(lr, E, K, epoch, err, lane, ids, wts, packed);
-    else if (E <= 128) topk_tagged_n<2>(lr, E, K, epoch, err, lane, ids, wts, packed);
-    else if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed);
-    else if (E <= 512) topk_tagged_n<8>(lr, E, K, epoch, err, lane, ids, wts, packed);
-    else topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed);
+// more than 256 experts: 16 per lane, in a function of its own
+__device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, uint32_t epoch,
+                                              uint32_t *err, int lane, int32_t *ids, float *wts,
+                                              bool packed) {
+    topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed);
+}
+
+// Up to 256 experts (4 per lane) the top-K is inlined into the kernel, not
+// called: a call saves a callee-saved register to scratch memory on entry
+// and loads it back on return, one more memory round trip (queued behind
+// the wave's other memory operations) on the path every later step waits
+// for.
+__device__ __forceinline__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch,
+                                            uint32_t *err, int lane, int32_t *ids, float *wts,
+                                            bool packed) {
+    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed);
+    else topk_tagged_wide(lr, E, K, epoch, err, lane, ids, wts, packed);
 }
 
 // Routed gate/up. One item: columns n0..n0+3 of the gate and up matrices of

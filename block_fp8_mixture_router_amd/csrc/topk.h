@@ -16,8 +16,8 @@ namespace moe {
 // Selection on values already in registers: lane l holds experts l, l + 64,
 // ... (v = -inf, ix = INT_MAX beyond E). Results (slot order) to ids/wts.
 template <int NL>
-__device__ inline void topk_select_n(float (&v)[NL], int (&ix)[NL], int K, int lane,
-                                     int32_t *ids, float *wts) {
+__device__ __forceinline__ void topk_select_n(float (&v)[NL], int (&ix)[NL], int K, int lane,
+                                              int32_t *ids, float *wts) {
     // odd-even transposition sort of the lane's NL entries
 #pragma unroll
     for (int r = 0; r < NL; ++r)
@@ -104,8 +104,8 @@ __device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
 
 // Selection on packed keys already in registers (0 beyond E).
 template <int NL>
-__device__ inline void topk_select_packed(uint32_t (&k)[NL], int K, int lane, int32_t *ids,
-                                          float *wts) {
+__device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int lane,
+                                                   int32_t *ids, float *wts) {
 #pragma unroll
     for (int r = 0; r < NL; ++r)
 #pragma unroll
