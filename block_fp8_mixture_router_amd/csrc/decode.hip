@@ -473,10 +473,11 @@ __device__ __forceinline__ void g_item(const FusedArgs &a, int t, const uint16_t
 
 // ------------------------------------------------------------- phase B
 
-// top-K of row t from this workgroup's copy of the tagged logits
+// top-K of row t from this workgroup's copy of the tagged logits; each
+// slot's expert is published in LDS (ids, then *ready) as its round ends
 template <int NL>
 __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
-                              int lane, int32_t *ids, float *wts, bool packed) {
+                              int lane, int32_t *ids, float *wts, bool packed, int *ready) {
     int idx[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) idx[i] = lane + WAVE * i;
@@ -489,7 +490,7 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
         uint32_t k[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) k[i] = i < n ? bf16_order_key(__uint_as_float(bits[i]), idx[i]) : 0u;
-        topk_select_packed<NL>(k, K, lane, ids, wts);
+        topk_select_packed<NL, true>(k, K, lane, ids, wts, ready);
     } else {
         float v[NL];
         int ix[NL];
@@ -498,15 +499,15 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
             v[i] = i < n ? __uint_as_float(bits[i]) : -INFINITY;
             ix[i] = i < n ? idx[i] : 0x7FFFFFFF;
         }
-        topk_select_n<NL>(v, ix, K, lane, ids, wts);
+        topk_select_n<NL, true>(v, ix, K, lane, ids, wts, ready);
     }
 }
 
 // more than 256 experts: 16 per lane, in a function of its own
 __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, uint32_t epoch,
                                               uint32_t *err, int lane, int32_t *ids, float *wts,
-                                              bool packed) {
-    topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed);
+                                              bool packed, int *ready) {
+    topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
 }
 
 // Up to 256 experts (4 per lane) the top-K is inlined into the kernel, not
@@ -516,9 +517,27 @@ __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, 
 // for.
 __device__ __forceinline__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch,
                                             uint32_t *err, int lane, int32_t *ids, float *wts,
-                                            bool packed) {
-    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed);
-    else topk_tagged_wide(lr, E, K, epoch, err, lane, ids, wts, packed);
+                                            bool packed, int *ready) {
+    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
+    else topk_tagged_wide(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
+}
+
+// Slot j of a row once the wave selecting the row has published it (*ready
+// > j): its expert, read after the count (in order, see publish_slot).
+// Bounded like the handoff waits, though the publishing wave depends on
+// nothing that can stall for good.
+__device__ __forceinline__ int wait_slot(const int *ready, const int32_t *ids, int j,
+                                         uint32_t *err) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <= j) {
+        if (++spins > SPIN_LIMIT) {
+            if ((threadIdx.x & 63) == 0) st_dev(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return __hip_atomic_load(ids + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Routed gate/up. One item: columns n0..n0+3 of the gate and up matrices of
@@ -936,7 +955,7 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, rdy, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
 // slots per row of variant var: the block-FP8 shared expert is one more
@@ -971,7 +990,8 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is, 
     L.sq = L.red + 32;                    // shared gate/up partials, per wave [KB][16]
     L.sp = L.sq + 4 * al16i(KB * 16 * 4); // routed gate/up second halves, per wave [KH][8]
     L.sdo = L.sp + 4 * al16i(KH * 8 * 8); // shared down operands [SDB][4][64] uint4
-    L.total = L.sdo + (Is > 0 ? SDB * 4 * 64 * 16 : 0);
+    L.rdy = L.sdo + (Is > 0 ? SDB * 4 * 64 * 16 : 0);  // per row: slots published
+    L.total = L.rdy + 16;
     return L;
 }
 
@@ -1173,6 +1193,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     double *rl = reinterpret_cast<double *>(lds + L.rl);        // [2][4]
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds + L.xs);    // [T][H]
     uint4 *sdo = reinterpret_cast<uint4 *>(lds + L.sdo);        // [SDB][4][64]
+    int *ready = reinterpret_cast<int *>(lds + L.rdy);          // [T] slots published
 
     const int wave = threadIdx.x >> 6;
     const int nw = a.nwg * 4;
@@ -1185,6 +1206,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     uint32_t *counter = a.sync + SYNC_FLAGS + blockIdx.x;
     const uint32_t cnt = ld_dev(counter);
     uint32_t *err = a.sync + ERR_WORD;
+    if ((int)threadIdx.x < T) ready[threadIdx.x] = 0;  // before the barrier below
 
     // phase-C units (t, MB-row block), workgroup-major; a workgroup past the
     // last unit loads the last unit's rows (unused), so its loads need no
@@ -1219,15 +1241,17 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     }
     __syncthreads();  // xs, qx, sx ready
 
-    // A2: the shared expert's gate/up columns and the shared gate, on waves
-    // 1-3 (wave 0 runs the top-K next, and a wave with loads in flight would
-    // wait for them before its first poll). The block-FP8 shared expert is
-    // slot K of every row: its gate/up items are the routed items' (expert
-    // E), with h handed over among the routed pairs' h.
-    if (wave > 0 && Is > 0) {
+    // A2: the shared expert's gate/up columns and the shared gate, on wave 3
+    // (wave 0 runs the top-K next, and a wave with loads in flight would wait
+    // for them before its first poll; waves 1 and 2 start their routed
+    // gate/up items as soon as the top-K has published their slots). The
+    // block-FP8 shared expert is slot K of every row: its gate/up items are
+    // the routed items' (expert E), with h handed over among the routed
+    // pairs' h.
+    if (wave == 3 && Is > 0) {
         if constexpr (VAR == DV_SFP8) {
             const int per_row = Is / 4, n_s = T * per_row, n_items = n_s + T;
-            for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
+            for (int it = blockIdx.x; it < n_items; it += a.nwg) {
                 if (it < n_s) {
                     const int t = it / per_row, n0 = (it % per_row) * 4;
                     GateUpRegs gr;
@@ -1239,54 +1263,60 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
             }
         } else {
             const int n_s = Is / 2, n_items = n_s + T;
-            for (int it = (wave - 1) * a.nwg + blockIdx.x; it < n_items; it += 3 * a.nwg) {
+            for (int it = blockIdx.x; it < n_items; it += a.nwg) {
                 if (it < n_s) s_item(a, it, xs, sq, epoch);
                 else g_item(a, it - n_s, xs, epoch);
             }
         }
     }
 
-    // B: top-K per row (one wave per row) once its logits exist, then the
-    // routed gate/up items
-    for (int t = wave; t < T; t += 4)
+    // B: top-K per row (one wave per row) once its logits exist, each slot
+    // published in LDS as its round ends; then the routed gate/up items, each
+    // wave waiting only for the slot of its own item (no barrier: a wave
+    // whose slot comes out in an early round starts its loads while the
+    // later rounds run)
+    for (int t = wave; t < T; t += 4) {
+        if (VAR == DV_SFP8 && (threadIdx.x & 63) == 0) {  // slot K: the shared expert
+            ids[t * KS + K] = E;  // published with slot 0
+            wts[t * KS + K] = 0.0f;
+        }
         topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
                     threadIdx.x & 63, ids + t * KS, wts + t * KS,
-                    !a.bias && !(a.flags & K_LOGITS_FP32));
-    if (VAR == DV_SFP8 && (int)threadIdx.x < T) {  // slot K: the shared expert
-        ids[threadIdx.x * KS + K] = E;
-        wts[threadIdx.x * KS + K] = 0.0f;
+                    !a.bias && !(a.flags & K_LOGITS_FP32), ready + t);
     }
-    __syncthreads();
-    // The first unit's routed and shared down rows are issued once this
-    // wave's first gate/up rows are in and their h has gone out: they stream
-    // in while the h handoff runs, without competing with the gate/up rows
-    // (issued alongside them, they held the gate/up phase back by about
-    // 0.8 us and the layer by about 0.4 us). Scheduling barriers keep the
-    // three steps in this order.
-    // routed item it: pair (t, j) of the T * K routed pairs, columns n0..n0+3
+    // Routed item it: pair (t, j) of the T * K routed pairs (pair index
+    // t * KS + j), columns n0..n0+3. The first unit's routed and shared down
+    // rows are issued once this wave's first gate/up rows are in and their h
+    // has gone out: they stream in while the h handoff runs, without
+    // competing with the gate/up rows (issued alongside them, they held the
+    // gate/up phase back by about 0.8 us and the layer by about 0.4 us).
+    // Scheduling barriers keep the three steps in this order.
     const int per_pair = I / 4, n_items = T * K * per_pair;
-    auto pair_of = [&](int it) {
-        const int rp = it / per_pair;
-        return VAR == DV_SFP8 ? (rp / K) * KS + rp % K : rp;
-    };
     DownRegs<KBR, TPW> dr;
     {
         const int it = min(gw, n_items - 1);  // waves past the last item load it (unused)
-        const int p = pair_of(it), n0 = (it % per_pair) * 4;
+        const int rp = it / per_pair, t = rp / K, j = rp - t * K, p = t * KS + j;
+        const int n0 = (it - rp * per_pair) * 4;
+        const int e = wait_slot(ready + t, ids + t * KS, j, err);
         GateUpRegs gr;
-        gateup_load<VAR>(a, ids[p], n0, 0, gr);
+        gateup_load<VAR>(a, e, n0, 0, gr);
         __builtin_amdgcn_sched_barrier(0);
-        if (gw < n_items) gateup_finish<VAR>(a, p, n0, ids[p], gr, qx, sx, xs, sp, epoch);
+        if (gw < n_items) gateup_finish<VAR>(a, p, n0, e, gr, qx, sx, xs, sp, epoch);
         __builtin_amdgcn_sched_barrier(0);
+        // every slot of the unit's row (the shared slot K, if any, is
+        // published with slot 0)
+        wait_slot(ready + t_first, ids + t_first * KS, K - 1, err);
         down_load_routed<KBR, TPW, VAR>(a, t_first, m_first, ids, dr);
         if (Isb > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int it = gw + nw; it < n_items; it += nw) {
-        const int p = pair_of(it), n0 = (it % per_pair) * 4;
+        const int rp = it / per_pair, t = rp / K, j = rp - t * K, p = t * KS + j;
+        const int n0 = (it - rp * per_pair) * 4;
+        const int e = wait_slot(ready + t, ids + t * KS, j, err);
         GateUpRegs gr;
-        gateup_load<VAR>(a, ids[p], n0, 0, gr);
-        gateup_finish<VAR>(a, p, n0, ids[p], gr, qx, sx, xs, sp, epoch);
+        gateup_load<VAR>(a, e, n0, 0, gr);
+        gateup_finish<VAR>(a, p, n0, e, gr, qx, sx, xs, sp, epoch);
     }
 
     // C: hs and gamma (ready since phase A) into LDS, the first unit's

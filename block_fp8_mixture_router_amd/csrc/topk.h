@@ -5,6 +5,17 @@
 
 namespace moe {
 
+// Slot j's expert for the other waves of the workgroup: ids[j], then the
+// count of published slots. A wave's LDS operations complete in the order
+// it issues them, so a wave that reads the count j + 1 and then ids[j] gets
+// the expert; the fence only keeps the compiler from swapping the stores
+// (no wait is needed between them).
+__device__ __forceinline__ void publish_slot(int32_t *ids, int *ready, int j, int e) {
+    __hip_atomic_store(ids + j, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __hip_atomic_store(ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Top-K of one router row by one full wave, then the softmax over the K in
 // slot order (results to LDS). Lane l holds experts l, l + 64, ...; it sorts
 // its NL values once (logit descending, expert ascending), so each of the K
@@ -15,9 +26,12 @@ namespace moe {
 // and are read with device-coherent (sc1) loads.
 // Selection on values already in registers: lane l holds experts l, l + 64,
 // ... (v = -inf, ix = INT_MAX beyond E). Results (slot order) to ids/wts.
-template <int NL>
+// With PUB (ids and *ready in LDS), slot j's expert is published as soon
+// as its round ends: ids[j], then *ready = j + 1, so other waves of the
+// workgroup can start on slot j while the later rounds run.
+template <int NL, bool PUB = false>
 __device__ __forceinline__ void topk_select_n(float (&v)[NL], int (&ix)[NL], int K, int lane,
-                                              int32_t *ids, float *wts) {
+                                              int32_t *ids, float *wts, int *ready = nullptr) {
     // odd-even transposition sort of the lane's NL entries
 #pragma unroll
     for (int r = 0; r < NL; ++r)
@@ -50,12 +64,13 @@ __device__ __forceinline__ void topk_select_n(float (&v)[NL], int (&ix)[NL], int
             my_id = win;
             my_v = vmax;
         }
+        if (PUB && lane == 0) publish_slot(ids, ready, j, win);
     }
     const float ex = lane < K ? expf(my_v - v0) : 0.0f;
     float sum = 0.0f;
     for (int j = 0; j < K; ++j) sum += readlane_f(ex, j);
     if (lane < K) {
-        ids[lane] = my_id;
+        if (!PUB) ids[lane] = my_id;
         wts[lane] = ex / sum;
     }
 }
@@ -102,10 +117,12 @@ __device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
                    (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
-// Selection on packed keys already in registers (0 beyond E).
-template <int NL>
+// Selection on packed keys already in registers (0 beyond E); PUB as for
+// topk_select_n.
+template <int NL, bool PUB = false>
 __device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int lane,
-                                                   int32_t *ids, float *wts) {
+                                                   int32_t *ids, float *wts,
+                                                   int *ready = nullptr) {
 #pragma unroll
     for (int r = 0; r < NL; ++r)
 #pragma unroll
@@ -125,6 +142,7 @@ __device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int
         }
         if (j == 0) k0 = best;
         if (lane == j) my_k = best;
+        if (PUB && lane == 0) publish_slot(ids, ready, j, (int)(0xFFFF - (best & 0xFFFFu)));
     }
     // back to the logit values: undo the order map of the top 16 bits
     auto val = [](uint32_t key) {
@@ -136,7 +154,7 @@ __device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int
     float sum = 0.0f;
     for (int j = 0; j < K; ++j) sum += readlane_f(ex, j);
     if (lane < K) {
-        ids[lane] = (int)(0xFFFF - (my_k & 0xFFFFu));
+        if (!PUB) ids[lane] = (int)(0xFFFF - (my_k & 0xFFFFu));
         wts[lane] = ex / sum;
     }
 }
