@@ -188,8 +188,10 @@ moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  * x: bf16 [T, H]; y: bf16 [T, H] (must not alias x);
  * workspace: >= moe_workspace_bytes(cfg, T) bytes, zero-filled once before
  * the first moe_forward call that uses it (any single repeated byte value
- * also works); from then on the library keeps it valid, so later calls need
- * no clearing. The decode path (T <= 4 by default) keeps per-workgroup call
+ * also works); from then on the library keeps it valid for that config, so
+ * later calls need no clearing. The layout depends on the config (flags
+ * included): before a call with another config, zero-fill it again
+ * (moe_forward_noalloc does so itself). The decode path (T <= 4 by default) keeps per-workgroup call
  * counters and epoch-tagged handoff words in it between calls, so two calls
  * that overlap in time must not share a workspace; calls ordered on one
  * stream may. The decode kernel runs one workgroup per CU and every
