@@ -474,10 +474,12 @@ __device__ __forceinline__ void g_item(const FusedArgs &a, int t, const uint16_t
 // ------------------------------------------------------------- phase B
 
 // top-K of row t from this workgroup's copy of the tagged logits; each
-// slot's expert is published in LDS (ids, then *ready) as its round ends
+// slot's expert is published in LDS (one 64-bit word per slot, see
+// publish_slot) as its round ends
 template <int NL>
-__device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch, uint32_t *err,
-                              int lane, int32_t *ids, float *wts, bool packed, int *ready) {
+__device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch,
+                                              uint32_t *err, int lane, uint64_t *slots,
+                                              float *wts, bool packed) {
     int idx[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) idx[i] = lane + WAVE * i;
@@ -490,7 +492,7 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
         uint32_t k[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) k[i] = i < n ? bf16_order_key(__uint_as_float(bits[i]), idx[i]) : 0u;
-        topk_select_packed<NL, true>(k, K, lane, ids, wts, ready);
+        topk_select_packed<NL, true>(k, K, lane, nullptr, wts, slots);
     } else {
         float v[NL];
         int ix[NL];
@@ -499,15 +501,15 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
             v[i] = i < n ? __uint_as_float(bits[i]) : -INFINITY;
             ix[i] = i < n ? idx[i] : 0x7FFFFFFF;
         }
-        topk_select_n<NL, true>(v, ix, K, lane, ids, wts, ready);
+        topk_select_n<NL, true>(v, ix, K, lane, nullptr, wts, slots);
     }
 }
 
 // more than 256 experts: 16 per lane, in a function of its own
 __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, uint32_t epoch,
-                                              uint32_t *err, int lane, int32_t *ids, float *wts,
-                                              bool packed, int *ready) {
-    topk_tagged_n<16>(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
+                                              uint32_t *err, int lane, uint64_t *slots,
+                                              float *wts, bool packed) {
+    topk_tagged_n<16>(lr, E, K, epoch, err, lane, slots, wts, packed);
 }
 
 // Up to 256 experts (4 per lane) the top-K is inlined into the kernel, not
@@ -516,28 +518,46 @@ __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, 
 // the wave's other memory operations) on the path every later step waits
 // for.
 __device__ __forceinline__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch,
-                                            uint32_t *err, int lane, int32_t *ids, float *wts,
-                                            bool packed, int *ready) {
-    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
-    else topk_tagged_wide(lr, E, K, epoch, err, lane, ids, wts, packed, ready);
+                                            uint32_t *err, int lane, uint64_t *slots, float *wts,
+                                            bool packed) {
+    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, slots, wts, packed);
+    else topk_tagged_wide(lr, E, K, epoch, err, lane, slots, wts, packed);
 }
 
-// Slot j of a row once the wave selecting the row has published it (*ready
-// > j): its expert, read after the count (in order, see publish_slot).
+// a slot word's expert (the low half)
+__device__ __forceinline__ int slot_expert(uint64_t w) { return (int)(uint32_t)w; }
+__device__ __forceinline__ uint64_t ld_slot(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// A slot's expert once the wave selecting its row has published it.
 // Bounded like the handoff waits, though the publishing wave depends on
-// nothing that can stall for good.
-__device__ __forceinline__ int wait_slot(const int *ready, const int32_t *ids, int j,
-                                         uint32_t *err) {
+// nothing that can stall for good (on giving up: expert 0).
+__device__ __forceinline__ int wait_slot(const uint64_t *slot, uint32_t *err) {
     uint32_t spins = 0;
-    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <= j) {
+    uint64_t w;
+    while (((w = ld_slot(slot)) >> 32) == 0) {
         if (++spins > SPIN_LIMIT) {
             if ((threadIdx.x & 63) == 0) st_dev(err, 1u);
-            break;
+            return 0;
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return __hip_atomic_load(ids + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return slot_expert(w);
+}
+
+// Waits until every slot [0, n) of a row is published (lane l < n polls
+// slot l; every word is checked, since different words are not ordered).
+__device__ __forceinline__ void wait_row(const uint64_t *slots, int n, uint32_t *err) {
+    const int lane = threadIdx.x & 63;
+    uint32_t spins = 0;
+    while (__builtin_amdgcn_ballot_w64(lane < n && (ld_slot(slots + min(lane, n - 1)) >> 32) == 0)) {
+        if (++spins > SPIN_LIMIT) {
+            if (lane == 0) st_dev(err, 1u);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
 }
 
 // Routed gate/up. One item: columns n0..n0+3 of the gate and up matrices of
@@ -559,9 +579,15 @@ struct GateUpRegs {
 // Expert e's gate or up rows and their block scales; with the block-FP8
 // shared expert, e = E is that expert (its matrices have the routed ones'
 // shape, Is = I).
+// Expert indices come from LDS words the top-K publishes; they are clamped
+// to the valid range here (a no-op on published words), so no weight address
+// can leave the expert arrays whatever such a word holds.
+__device__ __forceinline__ int clamp_expert(int e, int hi) { return min(max(e, 0), hi); }
+
 template <int VAR>
 __device__ __forceinline__ void expert_gu(const FusedArgs &a, int e, bool up, const uint8_t *&w,
                                           const float *&s) {
+    e = clamp_expert(e, VAR == DV_SFP8 ? a.E : a.E - 1);
     if (VAR == DV_SFP8 && e == a.E) {
         w = up ? a.sh8_up : a.sh8_gate;
         s = up ? a.sh_s_up : a.sh_s_gate;
@@ -777,6 +803,7 @@ __device__ __forceinline__ void down_stage_shared(const DownRegs<KBR, TPW> &r, u
 template <int VAR>
 __device__ __forceinline__ void expert_down(const FusedArgs &a, int e, const uint8_t *&w,
                                             const float *&s) {
+    e = clamp_expert(e, VAR == DV_SFP8 ? a.E : a.E - 1);
     if (VAR == DV_SFP8 && e == a.E) {
         w = a.sh8_down;
         s = a.sh_s_down;
@@ -793,7 +820,7 @@ __device__ __forceinline__ void expert_down(const FusedArgs &a, int e, const uin
 // also wait for these.
 template <int KBR, int TPW, int VAR>
 __device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int m0,
-                                                 const int32_t *ids, DownRegs<KBR, TPW> &r) {
+                                                 const uint64_t *slots, DownRegs<KBR, TPW> &r) {
     const int I = a.I, KS = a.KS, IB = I / GROUP;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -802,8 +829,9 @@ __device__ __forceinline__ void down_load_routed(const FusedArgs &a, int t, int 
         const uint8_t *wb;
         const float *sb, *sbs;
         const uint8_t *dummy;
-        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (l16 >> 3), KS - 1)], wb, sb);
-        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (kq >> 1), KS - 1)], dummy, sbs);
+        expert_down<VAR>(a, slot_expert(slots[t * KS + min(2 * tau + (l16 >> 3), KS - 1)]), wb, sb);
+        expert_down<VAR>(a, slot_expert(slots[t * KS + min(2 * tau + (kq >> 1), KS - 1)]), dummy,
+                         sbs);
         const uint8_t *row = wb + (int64_t)(m0 + (l16 & 7)) * I;
         const float *sd = sbs + (int64_t)(m0 / GROUP) * IB;
 #pragma unroll
@@ -849,7 +877,7 @@ __device__ __forceinline__ float shared_down_chain(const FusedArgs &a, int t, in
 template <int KBR, int TPW, int VAR>
 __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
                                           const DownRegs<KBR, TPW> &r, const uint8_t *qh,
-                                          const float *shs, const int32_t *ids,
+                                          const float *shs, const uint64_t *slots,
                                           const float *wts, const uint16_t *hs_l,
                                           const float *gam_l, float *ej, float *ss,
                                           uint4 *sdo, bool chain) {
@@ -868,7 +896,8 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
     for (int u = 0; u < TPW; ++u) {
         const int tau = wave + 4 * u;
         const float *sb;
-        expert_down<VAR>(a, ids[t * KS + min(2 * tau + (l16 >> 3), KS - 1)], wrow[u], sb);
+        expert_down<VAR>(a, slot_expert(slots[t * KS + min(2 * tau + (l16 >> 3), KS - 1)]), wrow[u],
+                         sb);
         wrow[u] += (int64_t)(m0 + (l16 & 7)) * I;
     }
     const int js_lane = 2 * wave + (kq >> 1);  // slot of this lane's D rows (tile u adds 8u)
@@ -897,7 +926,7 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
                 load_block<VAR>(wrow[u], b, w0, w1);
                 const uint8_t *dummy;
                 const float *sb;
-                expert_down<VAR>(a, ids[t * KS + js], dummy, sb);
+                expert_down<VAR>(a, slot_expert(slots[t * KS + js]), dummy, sb);
                 sdv = sb[(int64_t)(m0 / GROUP) * IB + b];
             }
             v4f d;
@@ -955,7 +984,7 @@ __device__ __forceinline__ void down_unit(const FusedArgs &a, int t, int m0,
 
 // LDS carve-up of the fused kernel, every piece 16-byte aligned
 struct LdsPlan {
-    int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, rdy, total;
+    int qx, sx, qh, shs, ids, wts, hs, gam, ej, ss, rl, xs, red, sq, sp, sdo, total;
 };
 __host__ __device__ inline int al16i(int b) { return (b + 15) & ~15; }
 // slots per row of variant var: the block-FP8 shared expert is one more
@@ -979,7 +1008,7 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is, 
     L.qh = L.sx + al16i(T * KB * 4);
     L.shs = L.qh + al16i(P * I * (var == DV_NOQ ? 2 : 1));  // codes, or bf16 h
     L.ids = L.shs + al16i(P * (I / GROUP) * 4);
-    L.wts = L.ids + al16i(P * 4);
+    L.wts = L.ids + al16i(P * 8);  // ids: one 64-bit slot word per pair
     L.hs = L.wts + al16i(P * 4);
     L.gam = L.hs + al16i(T * Is * 2);
     L.ej = L.gam + al16i(T * 4);          // phase-C unit: e_j of its rows, every slot
@@ -990,8 +1019,7 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int H, int K, int I, int Is, 
     L.sq = L.red + 32;                    // shared gate/up partials, per wave [KB][16]
     L.sp = L.sq + 4 * al16i(KB * 16 * 4); // routed gate/up second halves, per wave [KH][8]
     L.sdo = L.sp + 4 * al16i(KH * 8 * 8); // shared down operands [SDB][4][64] uint4
-    L.rdy = L.sdo + (Is > 0 ? SDB * 4 * 64 * 16 : 0);  // per row: slots published
-    L.total = L.rdy + 16;
+    L.total = L.sdo + (Is > 0 ? SDB * 4 * 64 * 16 : 0);
     return L;
 }
 
@@ -1184,7 +1212,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     float *sx = reinterpret_cast<float *>(lds + L.sx);        // [T][H/128]
     uint8_t *qh = lds + L.qh;                                 // [P][I] (bf16 with DV_NOQ)
     float *shs = reinterpret_cast<float *>(lds + L.shs);      // [P][I/128]
-    int32_t *ids = reinterpret_cast<int32_t *>(lds + L.ids);  // [P]
+    uint64_t *slots = reinterpret_cast<uint64_t *>(lds + L.ids);  // [P] published experts
     float *wts = reinterpret_cast<float *>(lds + L.wts);      // [P]
     uint16_t *hs_l = reinterpret_cast<uint16_t *>(lds + L.hs);  // [T][Isb]
     float *gam_l = reinterpret_cast<float *>(lds + L.gam);      // [T]
@@ -1193,7 +1221,6 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     double *rl = reinterpret_cast<double *>(lds + L.rl);        // [2][4]
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds + L.xs);    // [T][H]
     uint4 *sdo = reinterpret_cast<uint4 *>(lds + L.sdo);        // [SDB][4][64]
-    int *ready = reinterpret_cast<int *>(lds + L.rdy);          // [T] slots published
 
     const int wave = threadIdx.x >> 6;
     const int nw = a.nwg * 4;
@@ -1206,7 +1233,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     uint32_t *counter = a.sync + SYNC_FLAGS + blockIdx.x;
     const uint32_t cnt = ld_dev(counter);
     uint32_t *err = a.sync + ERR_WORD;
-    if ((int)threadIdx.x < T) ready[threadIdx.x] = 0;  // before the barrier below
+    if ((int)threadIdx.x < P) slots[threadIdx.x] = 0;  // unpublished, before the barrier below
 
     // phase-C units (t, MB-row block), workgroup-major; a workgroup past the
     // last unit loads the last unit's rows (unused), so its loads need no
@@ -1277,12 +1304,12 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
     // later rounds run)
     for (int t = wave; t < T; t += 4) {
         if (VAR == DV_SFP8 && (threadIdx.x & 63) == 0) {  // slot K: the shared expert
-            ids[t * KS + K] = E;  // published with slot 0
+            publish_slot(slots + t * KS + K, E);
             wts[t * KS + K] = 0.0f;
         }
         topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
-                    threadIdx.x & 63, ids + t * KS, wts + t * KS,
-                    !a.bias && !(a.flags & K_LOGITS_FP32), ready + t);
+                    threadIdx.x & 63, slots + t * KS, wts + t * KS,
+                    !a.bias && !(a.flags & K_LOGITS_FP32));
     }
     // Routed item it: pair (t, j) of the T * K routed pairs (pair index
     // t * KS + j), columns n0..n0+3. The first unit's routed and shared down
@@ -1297,23 +1324,21 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
         const int it = min(gw, n_items - 1);  // waves past the last item load it (unused)
         const int rp = it / per_pair, t = rp / K, j = rp - t * K, p = t * KS + j;
         const int n0 = (it - rp * per_pair) * 4;
-        const int e = wait_slot(ready + t, ids + t * KS, j, err);
+        const int e = wait_slot(slots + p, err);
         GateUpRegs gr;
         gateup_load<VAR>(a, e, n0, 0, gr);
         __builtin_amdgcn_sched_barrier(0);
         if (gw < n_items) gateup_finish<VAR>(a, p, n0, e, gr, qx, sx, xs, sp, epoch);
         __builtin_amdgcn_sched_barrier(0);
-        // every slot of the unit's row (the shared slot K, if any, is
-        // published with slot 0)
-        wait_slot(ready + t_first, ids + t_first * KS, K - 1, err);
-        down_load_routed<KBR, TPW, VAR>(a, t_first, m_first, ids, dr);
+        wait_row(slots + t_first * KS, KS, err);  // every slot of the unit's row
+        down_load_routed<KBR, TPW, VAR>(a, t_first, m_first, slots, dr);
         if (Isb > 0) down_load_shared<KBR, TPW>(a, m_first, dr);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int it = gw + nw; it < n_items; it += nw) {
         const int rp = it / per_pair, t = rp / K, j = rp - t * K, p = t * KS + j;
         const int n0 = (it - rp * per_pair) * 4;
-        const int e = wait_slot(ready + t, ids + t * KS, j, err);
+        const int e = wait_slot(slots + p, err);
         GateUpRegs gr;
         gateup_load<VAR>(a, e, n0, 0, gr);
         gateup_finish<VAR>(a, p, n0, e, gr, qx, sx, xs, sp, epoch);
@@ -1338,10 +1363,11 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
         const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
         const bool first = u == (int)blockIdx.x;
         if (!first) {
-            down_load_routed<KBR, TPW, VAR>(a, t, m0, ids, dr);
+            down_load_routed<KBR, TPW, VAR>(a, t, m0, slots, dr);
             if (Isb > 0) down_load_shared<KBR, TPW>(a, m0, dr);
         }
-        down_unit<KBR, TPW, VAR>(a, t, m0, dr, qh, shs, ids, wts, hs_l, gam_l, ej, ss, sdo, !first);
+        down_unit<KBR, TPW, VAR>(a, t, m0, dr, qh, shs, slots, wts, hs_l, gam_l, ej, ss, sdo,
+                                 !first);
     }
     // every wave has read the counter: advance it for the next call
     if (threadIdx.x == 0) st_dev(counter, call_epoch(cnt) + 1u);

@@ -5,15 +5,14 @@
 
 namespace moe {
 
-// Slot j's expert for the other waves of the workgroup: ids[j], then the
-// count of published slots. A wave's LDS operations complete in the order
-// it issues them, so a wave that reads the count j + 1 and then ids[j] gets
-// the expert; the fence only keeps the compiler from swapping the stores
-// (no wait is needed between them).
-__device__ __forceinline__ void publish_slot(int32_t *ids, int *ready, int j, int e) {
-    __hip_atomic_store(ids + j, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __hip_atomic_store(ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// A slot's expert for the other waves of the workgroup: one 64-bit LDS word
+// holding a published mark (1) above the expert index, stored at once (an
+// aligned 64-bit LDS access is single-copy atomic), so a reader sees either
+// the word it was reset to (0, before the workgroup's first barrier) or the
+// expert. Nothing is ordered between two different words.
+__device__ __forceinline__ void publish_slot(uint64_t *slot, int e) {
+    __hip_atomic_store(slot, (1ull << 32) | (uint32_t)e, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Top-K of one router row by one full wave, then the softmax over the K in
@@ -26,12 +25,14 @@ __device__ __forceinline__ void publish_slot(int32_t *ids, int *ready, int j, in
 // and are read with device-coherent (sc1) loads.
 // Selection on values already in registers: lane l holds experts l, l + 64,
 // ... (v = -inf, ix = INT_MAX beyond E). Results (slot order) to ids/wts.
-// With PUB (ids and *ready in LDS), slot j's expert is published as soon
-// as its round ends: ids[j], then *ready = j + 1, so other waves of the
-// workgroup can start on slot j while the later rounds run.
+// With PUB, slot j's expert is published as soon as its round ends, in
+// one 64-bit LDS word slots[j] (see publish_slot; ids is then not written),
+// so other waves of the workgroup can start on slot j while the later
+// rounds run.
 template <int NL, bool PUB = false>
 __device__ __forceinline__ void topk_select_n(float (&v)[NL], int (&ix)[NL], int K, int lane,
-                                              int32_t *ids, float *wts, int *ready = nullptr) {
+                                              int32_t *ids, float *wts,
+                                              uint64_t *slots = nullptr) {
     // odd-even transposition sort of the lane's NL entries
 #pragma unroll
     for (int r = 0; r < NL; ++r)
@@ -64,7 +65,7 @@ __device__ __forceinline__ void topk_select_n(float (&v)[NL], int (&ix)[NL], int
             my_id = win;
             my_v = vmax;
         }
-        if (PUB && lane == 0) publish_slot(ids, ready, j, win);
+        if (PUB && lane == 0) publish_slot(slots + j, win);
     }
     const float ex = lane < K ? expf(my_v - v0) : 0.0f;
     float sum = 0.0f;
@@ -122,7 +123,7 @@ __device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
 template <int NL, bool PUB = false>
 __device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int lane,
                                                    int32_t *ids, float *wts,
-                                                   int *ready = nullptr) {
+                                                   uint64_t *slots = nullptr) {
 #pragma unroll
     for (int r = 0; r < NL; ++r)
 #pragma unroll
@@ -142,7 +143,7 @@ __device__ __forceinline__ void topk_select_packed(uint32_t (&k)[NL], int K, int
         }
         if (j == 0) k0 = best;
         if (lane == j) my_k = best;
-        if (PUB && lane == 0) publish_slot(ids, ready, j, (int)(0xFFFF - (best & 0xFFFFu)));
+        if (PUB && lane == 0) publish_slot(slots + j, (int)(0xFFFF - (best & 0xFFFFu)));
     }
     // back to the logit values: undo the order map of the top 16 bits
     auto val = [](uint32_t key) {

@@ -56,6 +56,29 @@ def test_quant_act_every_bf16_value():
         assert bad.size == 0, [(float(x[0, i]), int(q[0, i]), int(qo[0, i])) for i in bad[:8]]
 
 
+@pytest.mark.parametrize("amax_bits", [0x3F80, 0x4049, 0x3BE0, 0x447A, 0x37C9, 0x5082, 0x3F7F])
+def test_quant_act_every_bf16_value_inexact_scales(amax_bits):
+    """Every finite bf16 value a with |a| <= amax, in groups whose amax is not
+    448 times a power of two: the quotients a / s are inexact, so the
+    kernel's correctly rounded division and the e4m3 rounding of its result
+    are checked against the oracle for every bf16 numerator at each scale."""
+    vals = exact.bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    vals = vals[np.isfinite(vals)]
+    anchor = exact.bits_to_f32(np.array([amax_bits], np.uint16))[0]
+    v = vals[np.abs(vals) <= anchor]
+    pad = (-len(v)) % 127
+    v = np.concatenate([v, np.zeros(pad, np.float32)]).reshape(-1, 127)
+    rows = np.concatenate([np.full((v.shape[0], 1), anchor, np.float32), v], axis=1)
+    x = torch.from_numpy(rows.reshape(1, -1)).to(torch.bfloat16)
+    say(f"quant sweep amax={anchor} groups={rows.shape[0]}")
+    q, s = moe.quant_act(x.cuda())
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_act(x)
+    assert np.array_equal(s.cpu().numpy(), so)
+    bad = np.nonzero(q.cpu().numpy() != qo)[1]
+    assert bad.size == 0, [(float(x[0, i]), int(q[0, i]), int(qo[0, i])) for i in bad[:8]]
+
+
 def test_quant_act_special_groups():
     x = torch.zeros(1, 512)
     x[0, 128:256] = -0.0
