@@ -24,6 +24,7 @@ def _check_rows(shape, host, xh, y, rows):
     rel, worst = rel_rows(bits(y.cpu())[rows], acc)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e} over {len(rows)} rows")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
 
 
 def test_max_rows():
@@ -83,3 +84,4 @@ def test_variants_at_odd_shape(T):
         rel, worst = rel_rows(bits(y.cpu()), acc)
         say(f"  flags {flags}: relL2 {rel:.2e} worst row {worst:.2e}")
         assert rel <= OUT_TOL, (flags, rel, worst)
+        assert worst <= OUT_TOL, (flags, rel, worst)  # each row on its own

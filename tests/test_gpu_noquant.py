@@ -44,6 +44,7 @@ def test_control_matches_oracle_mode(shape_name, T, shared):
     say(f"  control vs its oracle {rel_n:.2e} (worst row {worst_n:.2e}); "
         f"quantised layer vs the same oracle {rel_q:.2e}")
     assert rel_n <= OUT_TOL, (rel_n, worst_n)
+    assert worst_n <= OUT_TOL, (rel_n, worst_n)  # each row on its own
     # the switch takes effect: the quantised layer sits further from this mode
     assert rel_n < 0.5 * rel_q, (rel_n, rel_q)
 
@@ -60,6 +61,7 @@ def test_control_full_chunk_sampled_rows(skewed):
     rel, worst = _rel(shape, host, xh, y, oracle.NO_ACT_QUANT, rows=rows)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
 
 
 def test_control_is_deterministic_and_poison_proof():
@@ -98,6 +100,7 @@ def test_control_one_row_kernel(name, T, shared):
     rel, worst = _rel(shape, host, xh, yd, oracle.NO_ACT_QUANT, shared=shared)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
     assert np.array_equal(bits(yd.cpu()), bits(yg.cpu()))
 
 

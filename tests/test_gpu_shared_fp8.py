@@ -46,6 +46,7 @@ def test_shared_fp8_matches_oracle_mode(shape_name, T):
     rel, worst = _rel(shape, host, xh, y)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
 
 
 @pytest.mark.parametrize("skewed", [False, True])
@@ -60,6 +61,7 @@ def test_shared_fp8_full_chunk_sampled_rows(skewed):
     rel, worst = _rel(shape, host, xh, y, rows=rows)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
 
 
 def test_shared_fp8_deterministic_and_poison_proof():
@@ -116,6 +118,7 @@ def test_shared_fp8_one_row_kernel(name, T):
     rel, worst = _rel(shape, host, xh, yd)
     say(f"  relL2 {rel:.2e} worst row {worst:.2e}")
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
     assert np.array_equal(bits(yd.cpu()), bits(yg.cpu()))
 
 
@@ -145,3 +148,4 @@ def test_shared_fp8_shared_width_unlike_routed():
     y = run_forward(shape, dev, x, moe.SHARED_FP8)
     rel, worst = _rel(shape, host, xh, y)
     assert rel <= OUT_TOL, (rel, worst)
+    assert worst <= OUT_TOL, (rel, worst)  # each row on its own
