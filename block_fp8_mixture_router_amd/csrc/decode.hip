@@ -49,9 +49,11 @@
 // workspace started out filled with one repeated byte. Epochs are odd, below
 // 2^30 and differ from the counter they come from, so neither such a fill nor
 // words left by an earlier call can satisfy a wait. Waits are bounded: after
-// SPIN_LIMIT = 2^17 unsuccessful poll rounds (about 0.1-0.3 s: a round is
-// one device-coherent load round trip; workgroups not all resident) the
-// spin-out word is set and the kernel still finishes.
+// SPIN_LIMIT = 2^17 unsuccessful poll rounds the spin-out word is set and the
+// kernel still finishes. A round of a wait on other workgroups is one
+// device-coherent load round trip, so such a wait gives up after about
+// 0.1-0.3 s (workgroups not all resident); a wave's wait for a top-K slot of
+// its own workgroup polls LDS and gives up after about 10 ms.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -59,7 +61,7 @@
 namespace moe {
 
 constexpr int REPL = DECODE_REPLICAS;   // copies of every cross-workgroup value
-constexpr uint32_t SPIN_LIMIT = 1u << 17;  // poll rounds before giving up (about 0.1-0.3 s)
+constexpr uint32_t SPIN_LIMIT = 1u << 17;  // poll rounds before a wait gives up
 constexpr int ERR_WORD = SYNC_ERR_WORD;
 constexpr int MB = 8;  // output rows per phase-C unit
 

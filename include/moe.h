@@ -199,10 +199,13 @@ moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  * resident at once: the launch is refused (MOE_E_LAUNCH) on a device where
  * one of its workgroups does not fit on a CU, and concurrent work that holds
  * CUs (another decode call included) can keep some from starting. Its waits
- * are bounded: after 2^17 poll rounds (about 0.1-0.3 s) a waiting
- * workgroup gives up, the output is undefined, and the workspace's spin-out
- * word is set; moe_decode_status reads (and clears) it. moe_forward still
- * returns MOE_OK, since the outcome is known only on the device.
+ * are bounded: after 2^17 poll rounds a waiting workgroup gives up (a wait
+ * on other workgroups after about 0.1-0.3 s, a round being one
+ * device-coherent load round trip; a wait inside a workgroup, for its own
+ * top-K, after about 10 ms), the output is undefined, and the workspace's
+ * spin-out word is set; moe_decode_status reads (and clears) it.
+ * moe_forward still returns MOE_OK, since the outcome is known only on the
+ * device.
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                        int32_t T, void *y, void *workspace, size_t workspace_bytes,
