@@ -191,10 +191,10 @@ moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  * also works); from then on the library keeps it valid for that config, so
  * later calls need no clearing. The layout depends on the config (flags
  * included): before a call with another config, zero-fill it again
- * (moe_forward_noalloc does so itself). The decode path (T <= 4 by default) keeps per-workgroup call
- * counters and epoch-tagged handoff words in it between calls, so two calls
- * that overlap in time must not share a workspace; calls ordered on one
- * stream may. The decode kernel runs one workgroup per CU and every
+ * (moe_forward_noalloc does so itself). The decode path (T <= 4 by
+ * default) keeps per-workgroup call counters and epoch-tagged handoff words
+ * in it between calls, so two calls that overlap in time must not share a
+ * workspace; calls ordered on one stream may. The decode kernel runs one workgroup per CU and every
  * workgroup waits for values the others produce, so all of them must be
  * resident at once: the launch is refused (MOE_E_LAUNCH) on a device where
  * one of its workgroups does not fit on a CU, and concurrent work that holds
