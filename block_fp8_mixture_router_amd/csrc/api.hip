@@ -100,6 +100,12 @@ int decode_var(const moe_config *c) {
 // the workspace moves with T (a grouped call's plain data can never sit
 // where a later decode call polls for tagged words).
 int decode_rows_max(const moe_config *c) {
+    // The plain layer's one-row kernel with four router chunks per lane
+    // (hidden above 2048) made an illegal memory access the first time it
+    // ran (hidden 8192, 64 experts, top-8, intermediate 1024, one row), and
+    // no cause has been shown; such configs take the expert-grouped kernels
+    // until one is.
+    if (decode_var(c) == DV_PLAIN && c->hidden > 2048) return 0;
     for (int t = DECODE_MAX_ROWS; t >= 1; --t)
         if (decode_fits(t, c->hidden, c->top_k, c->inter, c->shared_inter, decode_var(c)))
             return t;

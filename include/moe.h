@@ -68,8 +68,11 @@ typedef enum {
                                        quantisation); moe_forward only */
 #define MOE_FORCE_GEMV    (1u << 8) /* run the one-row decode kernel (T <= 4; refused with
                                        MOE_E_UNSUPPORTED beyond, where its LDS plan does not
-                                       fit, and with MOE_SHARED_FP8 unless Is = I and
-                                       top_k <= 15) */
+                                       fit, with MOE_SHARED_FP8 unless Is = I and
+                                       top_k <= 15, and for the plain layer (neither
+                                       MOE_SHARED_FP8 nor MOE_NO_ACT_QUANT) above
+                                       H = 2048, which takes the expert-grouped
+                                       kernels at every T) */
 #define MOE_FORCE_GROUPED (1u << 9) /* run the expert-grouped path at any T */
 
 typedef struct {
@@ -192,7 +195,8 @@ moe_status moe_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  * later calls need no clearing. The layout depends on the config (flags
  * included): before a call with another config, zero-fill it again
  * (moe_forward_noalloc does so itself). The decode path (T <= 4 by
- * default) keeps per-workgroup call counters and epoch-tagged handoff words
+ * default; the plain layer only up to H = 2048) keeps per-workgroup call
+ * counters and epoch-tagged handoff words
  * in it between calls, so two calls that overlap in time must not share a
  * workspace; calls ordered on one stream may. The decode kernel runs one workgroup per CU and every
  * workgroup waits for values the others produce, so all of them must be
@@ -268,7 +272,9 @@ moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, cons
  * x); ys: bf16 [n_layers][T, H] every layer's output, or NULL (then the
  * layers' outputs alternate between two rows of the workspace);
  * T rows of the decode path only (MOE_E_UNSUPPORTED where it does not take
- * them, beyond 4 rows on the decode-layer shape); cfg->flags may not force a
+ * them: beyond 4 rows on the decode-layer shape, and at any T above
+ * H = 2048, where the plain layer takes the expert-grouped kernels);
+ * cfg->flags may not force a
  * path or set MOE_NO_ACT_QUANT or MOE_SHARED_FP8;
  * 0 <= n_layers <= 4096; 0 <= eps <= 1; workspace as for moe_forward.
  */

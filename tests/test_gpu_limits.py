@@ -2,6 +2,8 @@
 (65,536 rows, 524,288 pairs through the multi-pass sort) and the largest
 shapes (hidden 8192, 1024 experts, top-16, intermediate 4096), each
 against the oracle on sampled rows (rows are independent)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -66,6 +68,28 @@ def test_large_shapes(shape, T):
     rows = np.arange(T) if T <= 8 else np.unique(
         np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, 6, replace=False)]))
     _check_rows(shape, host, xh, y, rows)
+
+
+def test_plain_one_row_kernel_off_above_2048():
+    """Above H = 2048 the plain layer has no one-row path: forcing it is
+    refused on the host (nothing is enqueued) and the stack refuses the
+    config."""
+    shape = inputs.LayerShape(hidden=4096, n_experts=64, top_k=8, inter=512, shared_inter=512)
+    dev = inputs.make_layer(shape, seed=2, device="cuda")
+    x, _ = x_rows(shape, 1, seed=5)
+    cfg = moe.config(shape, moe.FORCE_GEMV)
+    ws = moe.alloc_workspace(cfg, 1)
+    y = torch.empty_like(x)
+    w = moe.weights_struct(dev)
+    rc = moe.lib().moe_forward(ctypes.byref(cfg), ctypes.byref(w), x.data_ptr(), 1,
+                               y.data_ptr(), ws.data_ptr(), ws.numel(), None)
+    assert rc == -5  # MOE_E_UNSUPPORTED
+    cplain = moe.config(shape)
+    rc = moe.lib().moe_forward_stack(ctypes.byref(cplain), moe.weights_array([dev]), 1,
+                                     x.data_ptr(), 1, ctypes.c_float(1e-6), y.data_ptr(), None,
+                                     ws.data_ptr(), ws.numel(), None)
+    assert rc == -5  # MOE_E_UNSUPPORTED
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("T", [1, 37])
