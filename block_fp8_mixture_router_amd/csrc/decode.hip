@@ -201,9 +201,12 @@ __device__ __forceinline__ uint64_t region_word(__amdgpu_buffer_rsrc_t r, int by
 // latency plus part of a round gap, not a full round trip per retry.
 // Bounded: past SPIN_LIMIT passes the error word is set and the stale
 // values are returned.
-constexpr int POLL_GAP = 6;  // s_sleep units (64 clocks) between re-poll rounds
+// s_sleep units (64 clocks) between re-poll rounds: the lone layer polls at
+// the shorter gap, the renormalising (stacked) layer at the longer one (each
+// measured the faster for its kernel)
+constexpr int POLL_GAP = 3, POLL_GAP_RN = 6;
 
-template <int N, int DEPTH>
+template <int N, int DEPTH, int GAP = POLL_GAP>
 __device__ __forceinline__ void poll_complete(uint32_t *err, __amdgpu_buffer_rsrc_t r,
                                               const int (&idx)[N], int n, uint32_t epoch,
                                               uint64_t (&w)[N], uint32_t (&v)[N]) {
@@ -218,7 +221,7 @@ __device__ __forceinline__ void poll_complete(uint32_t *err, __amdgpu_buffer_rsr
 #pragma unroll
             for (int i = 0; i < N; ++i)
                 q[d][i] = region_word(r, has_epoch(w[i], epoch) ? POLL_OOB : 8 * idx[i]);
-            if (d + 1 < DEPTH) __builtin_amdgcn_s_sleep(POLL_GAP);
+            if (d + 1 < DEPTH) __builtin_amdgcn_s_sleep(GAP);
         }
         for (uint32_t spin = 0;; ++spin) {
             bool fin = false;  // wave-uniform
@@ -478,7 +481,7 @@ __device__ __forceinline__ void g_item(const FusedArgs &a, int t, const uint16_t
 // top-K of row t from this workgroup's copy of the tagged logits; each
 // slot's expert is published in LDS (one 64-bit word per slot, see
 // publish_slot) as its round ends
-template <int NL>
+template <int NL, int GAP>
 __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, uint32_t epoch,
                                               uint32_t *err, int lane, uint64_t *slots,
                                               float *wts, bool packed) {
@@ -489,7 +492,8 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
     uint32_t bits[NL];
     uint64_t w[NL];
     poll_issue<NL>(lr, idx, n, epoch, w);
-    poll_complete<NL, (NL <= 4 ? 3 : 1)>(err, handoff_region(lr, E), idx, n, epoch, w, bits);
+    poll_complete<NL, (NL <= 4 ? 3 : 1), GAP>(err, handoff_region(lr, E), idx, n, epoch, w,
+                                               bits);
     if (packed) {
         uint32_t k[NL];
 #pragma unroll
@@ -508,10 +512,11 @@ __device__ __forceinline__ void topk_tagged_n(const uint64_t *lr, int E, int K, 
 }
 
 // more than 256 experts: 16 per lane, in a function of its own
+template <int GAP>
 __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, uint32_t epoch,
                                               uint32_t *err, int lane, uint64_t *slots,
                                               float *wts, bool packed) {
-    topk_tagged_n<16>(lr, E, K, epoch, err, lane, slots, wts, packed);
+    topk_tagged_n<16, GAP>(lr, E, K, epoch, err, lane, slots, wts, packed);
 }
 
 // Up to 256 experts (4 per lane) the top-K is inlined into the kernel, not
@@ -519,11 +524,12 @@ __device__ __noinline__ void topk_tagged_wide(const uint64_t *lr, int E, int K, 
 // and loads it back on return, one more memory round trip (queued behind
 // the wave's other memory operations) on the path every later step waits
 // for.
+template <int GAP>
 __device__ __forceinline__ void topk_tagged(const uint64_t *lr, int E, int K, uint32_t epoch,
                                             uint32_t *err, int lane, uint64_t *slots, float *wts,
                                             bool packed) {
-    if (E <= 256) topk_tagged_n<4>(lr, E, K, epoch, err, lane, slots, wts, packed);
-    else topk_tagged_wide(lr, E, K, epoch, err, lane, slots, wts, packed);
+    if (E <= 256) topk_tagged_n<4, GAP>(lr, E, K, epoch, err, lane, slots, wts, packed);
+    else topk_tagged_wide<GAP>(lr, E, K, epoch, err, lane, slots, wts, packed);
 }
 
 // a slot word's expert (the low half)
@@ -1155,7 +1161,7 @@ __device__ __forceinline__ void stage_c_finish_shared(const uint64_t *hs, const 
     }
 }
 
-template <int VAR>
+template <int VAR, bool RN>
 __device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P, int I,
                                                  uint32_t epoch, uint32_t *err, StageC &c,
                                                  uint8_t *qh, float *shs) {
@@ -1164,8 +1170,9 @@ __device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P
     const int n_groups = P * (I / GROUP);
     {
         uint32_t bits[8 * STAGE_HG];
-        poll_complete<8 * STAGE_HG, 2>(err, handoff_region(hsrc, P * I), c.hidx, 8 * c.nk0, epoch,
-                                       c.hw, bits);
+        // the lone layer: three re-poll rounds; the renormalising one: two
+        poll_complete<8 * STAGE_HG, RN ? 2 : 3, RN ? POLL_GAP_RN : POLL_GAP>(
+            err, handoff_region(hsrc, P * I), c.hidx, 8 * c.nk0, epoch, c.hw, bits);
         if constexpr (VAR == DV_NOQ) stage_h_bf16(0, c.nk0, bits, qh);
         else stage_h_quant(0, c.nk0, bits, qh, shs);
     }
@@ -1309,9 +1316,9 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
             publish_slot(slots + t * KS + K, E);
             wts[t * KS + K] = 0.0f;
         }
-        topk_tagged(a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
-                    threadIdx.x & 63, slots + t * KS, wts + t * KS,
-                    !a.bias && !(a.flags & K_LOGITS_FP32));
+        topk_tagged<RN ? POLL_GAP_RN : POLL_GAP>(
+            a.logits + (int64_t)((blockIdx.x % REPL) * T + t) * E, E, K, epoch, err,
+            threadIdx.x & 63, slots + t * KS, wts + t * KS, !a.bias && !(a.flags & K_LOGITS_FP32));
     }
     // Routed item it: pair (t, j) of the T * K routed pairs (pair index
     // t * KS + j), columns n0..n0+3. The first unit's routed and shared down
@@ -1359,7 +1366,7 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
         const float s = shared_down_chain(a, t_first, m_first, sdo, hs_l);
         if ((threadIdx.x & 63) < MB) ss[threadIdx.x & 63] = s;
     }
-    stage_c_finish_h<VAR>(a.h, T, P, I, epoch, err, sc, qh, shs);
+    stage_c_finish_h<VAR, RN>(a.h, T, P, I, epoch, err, sc, qh, shs);
     __syncthreads();
     for (int u = blockIdx.x; u < units; u += a.nwg) {
         const int t = u / (H / MB), m0 = (u % (H / MB)) * MB;
