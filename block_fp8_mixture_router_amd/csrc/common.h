@@ -236,19 +236,27 @@ __device__ __forceinline__ double sumsq8(const float (&v)[8], double acc) {
     for (int k = 0; k < 8; ++k) acc = fma((double)v[k], (double)v[k], acc);
     return acc;
 }
+// sum / H correctly rounded: for a power-of-two H the exact scaling by
+// 2^-log2(H) (one instruction, rounded only if the result is subnormal, as
+// the division would be), else the division
 __device__ __forceinline__ float rms_scale(double sum, int H, float eps) {
-    const float ms = (float)(sum / (double)H);
+    const double q = (H & (H - 1)) == 0 ? ldexp(sum, -__builtin_ctz((unsigned)H)) : sum / (double)H;
+    const float ms = (float)q;
     return 1.0f / sqrtf(ms + eps);
 }
 
 // The row's scale from this thread's chunks (zero past H). part: 4 doubles
 // of LDS; every thread of the workgroup calls this (it has a barrier), and
 // part may be written again only after a later barrier.
-__device__ __forceinline__ float renorm_row_scale(const uint4 (&v)[RENORM_CHUNKS], int H,
-                                                  float eps, double *part) {
+// CH: the thread's chunks (a caller whose rows fit in fewer than
+// RENORM_CHUNKS passes fewer: the chunks past H hold zeros, whose squares
+// leave the sum unchanged).
+template <int CH>
+__device__ __forceinline__ float renorm_row_scale(const uint4 (&v)[CH], int H, float eps,
+                                                  double *part) {
     double acc = 0.0;
 #pragma unroll
-    for (int i = 0; i < RENORM_CHUNKS; ++i) {
+    for (int i = 0; i < CH; ++i) {
         const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
                             bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
         acc = sumsq8(f, acc);

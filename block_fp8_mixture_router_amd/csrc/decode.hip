@@ -1189,19 +1189,21 @@ __device__ __forceinline__ void stage_c_finish_h(const uint64_t *h, int T, int P
 // Renormalising prologue: x_t = bf16(y_prev_t * rms scale) into LDS, every
 // workgroup for every row, with the stand-alone renormalisation's arithmetic
 // (renorm_row_scale, renorm_chunk). y_prev was written by an earlier launch.
+// CH chunks of 8 values per thread cover H (one up to 2048)
+template <int CH>
 __device__ __forceinline__ void renorm_rows_to_lds(const uint16_t *y, int T, int H, float eps,
                                                    uint16_t *xs, double *red) {
     const int tid = threadIdx.x, nc = H / 8;
     for (int t = 0; t < T; ++t) {
-        uint4 v[RENORM_CHUNKS];
+        uint4 v[CH];
 #pragma unroll
-        for (int i = 0; i < RENORM_CHUNKS; ++i) {
+        for (int i = 0; i < CH; ++i) {
             const int c = tid + 256 * i;
             v[i] = c < nc ? ld16(y + (int64_t)t * H + c * 8) : make_uint4(0, 0, 0, 0);
         }
-        const float r = renorm_row_scale(v, H, eps, red);
+        const float r = renorm_row_scale<CH>(v, H, eps, red);
 #pragma unroll
-        for (int i = 0; i < RENORM_CHUNKS; ++i) {
+        for (int i = 0; i < CH; ++i) {
             const int c = tid + 256 * i;
             if (c < nc) st16(xs + t * H + c * 8, renorm_chunk(v[i], r));
         }
@@ -1261,7 +1263,8 @@ __global__ __launch_bounds__(256, 1) void decode_fused_kernel(FusedArgs a) {
         RouterRegs<NQ> rr;
         if constexpr (RN) {
             if ((int)blockIdx.x < n_logits) router_load_w<NQ>(a, blockIdx.x, rr);
-            renorm_rows_to_lds(a.y_prev, T, H, a.eps, xs, reinterpret_cast<double *>(lds + L.red));
+            renorm_rows_to_lds<NQ>(a.y_prev, T, H, a.eps, xs,
+                                   reinterpret_cast<double *>(lds + L.red));
             if ((int)blockIdx.x < n_logits) router_load_x<NQ, RN>(a, blockIdx.x, xs, rr);
         } else {
             if ((int)blockIdx.x < n_logits) router_load<NQ, RN>(a, blockIdx.x, xs, rr);

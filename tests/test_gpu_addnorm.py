@@ -33,7 +33,8 @@ def _inputs(T, H, seed):
     return h, r, w
 
 
-@pytest.mark.parametrize("T,H", [(1, 2048), (5, 256), (64, 2048), (3, 8192), (1024, 2048)])
+@pytest.mark.parametrize("T,H", [(1, 2048), (5, 256), (64, 2048), (3, 8192), (1024, 2048),
+                                 (2, 384), (3, 6144)])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_add_rmsnorm_quant_bit_exact(T, H, in_place):
     say(f"add_rmsnorm_quant T={T} H={H} in_place={in_place}")

@@ -32,7 +32,8 @@ def _special_rows(H):
     return torch.from_numpy(rows).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,H", [(1, 2048), (5, 256), (64, 2048), (3, 8192), (1024, 2048)])
+@pytest.mark.parametrize("T,H", [(1, 2048), (5, 256), (64, 2048), (3, 8192), (1024, 2048),
+                                 (2, 384), (3, 6144)])
 def test_renorm_bit_exact(T, H):
     say(f"renorm T={T} H={H}")
     g = torch.Generator().manual_seed(T * H)
