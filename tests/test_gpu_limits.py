@@ -70,6 +70,20 @@ def test_large_shapes(shape, T):
     _check_rows(shape, host, xh, y, rows)
 
 
+def test_one_row_at_hidden_8192_takes_the_grouped_kernels():
+    """One row at hidden 8192 with the plain layer: the default path is now
+    the expert-grouped kernels (the one-row kernel is off above H = 2048),
+    checked against the oracle like the other large shapes."""
+    shape = inputs.LayerShape(hidden=8192, n_experts=64, top_k=8, inter=1024, shared_inter=1024)
+    say(f"forward {shape} T=1 (grouped kernels)")
+    dev = inputs.make_layer(shape, seed=1, device="cuda")
+    torch.cuda.synchronize()
+    host = dev.to("cpu")
+    x, xh = x_rows(shape, 1, seed=11)
+    y = run_forward(shape, dev, x)
+    _check_rows(shape, host, xh, y, np.arange(1))
+
+
 def test_plain_one_row_kernel_off_above_2048():
     """Above H = 2048 the plain layer has no one-row path: forcing it is
     refused on the host (nothing is enqueued) and the stack refuses the
